@@ -1,0 +1,311 @@
+/*
+ * CPU oracle for the batch-1 quantized GQA decode step (plain definitions, fp64).
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load this library.  It shares no code, header or table with the GPU
+ * library; it reads the packed weight and KV layouts from their written description.
+ *
+ * Sources (page title, then section):
+ *  [RT]  "How To Construct Your Personal LLM Runtime From Scratch" (newsaiworld post on the
+ *        annotated H100 runtime): section 3 (dims, GQA 28:4, 16-token KV pages),
+ *        section 6 (region order qkv_gemv -> append_tail_kv -> paged_attention -> o_proj ->
+ *        gate_up_gemv -> swiglu_down), section 7 (per-weight INT4 decode contract).
+ *  [H100] "Bare-Metal LLM Inference on NVIDIA H100 ..." (whatvis): "Architectural Blueprint"
+ *        (group-wise INT4 with one fp16 scale per group per output row; GQA 7:1).
+ *  [FQ]  FlashQwen README: "Local benchmark" (INT8 per-row weights, fp32 activations, bf16 KV),
+ *        "Optimization study" stages 5 (greedy argmax), 7 (split-K decode attention),
+ *        8 (INT8 per-output-row dequant in the GEMV).
+ *  [PA]  "Chapter 2 Systems Foundations for LLMs": "PagedAttention - Virtual Memory for KV
+ *        Caches" (page table from logical token block to physical block).
+ *  [NQ]  "Naive CUDA Kernel Qwen engine, part 1" (eduardoqian): sections RMSNorm, Rope,
+ *        SwiGLU, Sampler; the GGUF tensor list of a Qwen2 block.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - INT4 codes: byte j of a row holds k = 2j in bits 0-3 and k = 2j+1 in bits 4-7; the code
+ *    is unsigned with zero point 8, so the integer level is nibble - 8 in [-8, 7].
+ *  - RoPE: theta_i = base^(-2i/D), pairs (i, i + D/2) ("rotate half"), angles in fp64.
+ *  - Attention scale 1/sqrt(D), causal over every cached token plus the current one.
+ *  - SwiGLU: SiLU (beta = 1) on the gate projection, the up projection linear.
+ *  - Residual wiring: pre-norm, h += o_proj(attn(...)), h += down(swiglu(...)).
+ *  - Greedy tie-break: smallest index.
+ */
+#include "qdec_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- number formats */
+
+/* IEEE binary16 -> binary32 by fields; every binary16 value is exact in binary32. */
+float orc_f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1Fu;
+  uint32_t m = h & 0x3FFu;
+  uint32_t bits;
+  float f;
+  if (e == 0) {
+    /* zero or subnormal: m * 2^-24 */
+    f = (float)m * 5.9604644775390625e-08f;
+    return sign ? -f : f;
+  }
+  if (e == 31)
+    bits = sign | 0x7F800000u | (m << 13); /* inf / nan */
+  else
+    bits = sign | ((e + 112u) << 23) | (m << 13); /* rebias 15 -> 127 */
+  memcpy(&f, &bits, 4);
+  return f;
+}
+
+/* binary32 -> bf16 (upper 16 bits) rounded to nearest, ties to even. */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) return (uint16_t)((b >> 16) | 0x40u);
+  uint32_t lsb = (b >> 16) & 1u;
+  b += 0x7FFFu + lsb;
+  return (uint16_t)(b >> 16);
+}
+
+float orc_bf16_to_f32(uint16_t v) {
+  uint32_t b = (uint32_t)v << 16;
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+
+/* ---------------------------------------------------------------- dequantisation */
+
+/*
+ * INT8 per output row [FQ stage 8]: w = fp32(q) * s[row], one fp32 multiply.
+ * INT4 [RT section 7; H100 "Architectural Blueprint"]: level = nibble - 8 (zero point 8),
+ * times the fp16 scale of its group of `group` consecutive k in the row.  The product of a
+ * 4-bit level and an 11-bit fp16 significand is exact in fp32.
+ */
+void orc_dequant_row(int fmt, const void *W, const void *S, int group, int64_t row, int K, float *w) {
+  if (fmt == ORC_W_Q8) {
+    const int8_t *q = (const int8_t *)W + row * (int64_t)K;
+    float s = ((const float *)S)[row];
+    for (int k = 0; k < K; ++k) w[k] = (float)q[k] * s;
+  } else {
+    const uint8_t *b = (const uint8_t *)W + row * (int64_t)(K / 2);
+    const uint16_t *s = (const uint16_t *)S + row * (int64_t)(K / group);
+    for (int k = 0; k < K; ++k) {
+      uint8_t byte = b[k / 2];
+      int nib = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+      w[k] = (float)(nib - 8) * orc_f16_to_f32(s[k / group]);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------- GEMV */
+
+/* y = W x (+ bias) (+ residual), fp64 sum rounded once to fp32 [RT section 7: FP32 accumulate] */
+void orc_gemv(int fmt, const void *W, const void *S, int group, const float *x, const float *bias,
+              const float *residual, float *y, int N, int K, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel num_threads(nthreads)
+  {
+    float *w = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < N; ++n) {
+      orc_dequant_row(fmt, W, S, group, n, K, w);
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += (double)w[k] * (double)x[k];
+      if (bias) acc += (double)bias[n];
+      if (residual) acc += (double)residual[n];
+      y[n] = (float)acc;
+    }
+    free(w);
+  }
+}
+
+/* ---------------------------------------------------------------- RMSNorm [NQ RMSNorm] */
+
+void orc_rmsnorm(const float *x, const float *gamma, float *y, int rows, int dim, double eps) {
+  for (int r = 0; r < rows; ++r) {
+    const float *xr = x + (int64_t)r * dim;
+    double ss = 0.0;
+    for (int i = 0; i < dim; ++i) ss += (double)xr[i] * (double)xr[i];
+    double inv = 1.0 / sqrt(ss / dim + eps);
+    for (int i = 0; i < dim; ++i) {
+      double g = gamma ? (double)gamma[i] : 1.0;
+      y[(int64_t)r * dim + i] = (float)(g * (double)xr[i] * inv);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------- RoPE [NQ Rope] */
+
+/* Position as a 2-D rotation of coordinate pairs; angle of pair i is pos * base^(-2i/dim). */
+void orc_rope(float *x, int rows, int dim, int pos, double base) {
+  int half = dim / 2;
+  for (int i = 0; i < half; ++i) {
+    double theta = pow(base, -2.0 * (double)i / (double)dim);
+    double phi = (double)pos * theta;
+    double c = cos(phi), s = sin(phi);
+    for (int r = 0; r < rows; ++r) {
+      float *xr = x + (int64_t)r * dim;
+      double a = xr[i], b = xr[i + half];
+      xr[i] = (float)(a * c - b * s);
+      xr[i + half] = (float)(b * c + a * s);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------- SwiGLU [NQ SwiGLU] */
+
+void orc_swiglu(const float *g, const float *u, float *m, int n) {
+  for (int i = 0; i < n; ++i) {
+    double z = g[i];
+    double silu = z / (1.0 + exp(-z));
+    m[i] = (float)(silu * (double)u[i]);
+  }
+}
+
+/* ---------------------------------------------------------------- paged KV [PA; RT section 3] */
+
+static inline int64_t kv_index(const int32_t *page_table, int page_size, int n_kv_heads, int head_dim,
+                               int t, int j, int d) {
+  int64_t page = page_table[t / page_size];
+  return ((page * n_kv_heads + j) * page_size + (t % page_size)) * (int64_t)head_dim + d;
+}
+
+void orc_kv_store(void *pool, int kv_fmt, const int32_t *page_table, int page_size, int n_kv_heads,
+                  int head_dim, int t, const float *kv) {
+  for (int j = 0; j < n_kv_heads; ++j)
+    for (int d = 0; d < head_dim; ++d) {
+      int64_t i = kv_index(page_table, page_size, n_kv_heads, head_dim, t, j, d);
+      float v = kv[j * head_dim + d];
+      if (kv_fmt == ORC_KV_F32)
+        ((float *)pool)[i] = v;
+      else
+        ((uint16_t *)pool)[i] = orc_f32_to_bf16(v);
+    }
+}
+
+float orc_kv_load(const void *pool, int kv_fmt, const int32_t *page_table, int page_size,
+                  int n_kv_heads, int head_dim, int t, int j, int d) {
+  int64_t i = kv_index(page_table, page_size, n_kv_heads, head_dim, t, j, d);
+  return kv_fmt == ORC_KV_F32 ? ((const float *)pool)[i] : orc_bf16_to_f32(((const uint16_t *)pool)[i]);
+}
+
+/* ---------------------------------------------------------------- GQA decode attention */
+
+/*
+ * Query head h reads KV head h / (Hq / Hkv) [RT section 3: 28 query heads share 4 KV heads].
+ * Plain two-pass softmax in fp64 (max, exp, sum, divide), no split: the split-K form of the
+ * FlashQwen stage-7 kernel is an exact reformulation of this.
+ */
+void orc_attention(const float *q, const void *k_pool, const void *v_pool, int kv_fmt,
+                   const int32_t *page_table, int page_size, int T, int Hq, int Hkv, int D,
+                   double scale, float *out, float *probs) {
+  int G = Hq / Hkv;
+#pragma omp parallel for schedule(static)
+  for (int h = 0; h < Hq; ++h) {
+    int j = h / G;
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    double mx = -INFINITY;
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += (double)q[h * D + d] *
+               (double)orc_kv_load(k_pool, kv_fmt, page_table, page_size, Hkv, D, t, j, d);
+      s[t] = acc * scale;
+      if (s[t] > mx) mx = s[t];
+    }
+    double z = 0.0;
+    for (int t = 0; t < T; ++t) {
+      s[t] = exp(s[t] - mx);
+      z += s[t];
+    }
+    for (int t = 0; t < T; ++t) {
+      s[t] /= z;
+      if (probs) probs[(int64_t)h * T + t] = (float)s[t];
+    }
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int t = 0; t < T; ++t)
+        acc += s[t] * (double)orc_kv_load(v_pool, kv_fmt, page_table, page_size, Hkv, D, t, j, d);
+      out[h * D + d] = (float)acc;
+    }
+    free(s);
+  }
+}
+
+/* ---------------------------------------------------------------- greedy [FQ stage 5; NQ Sampler] */
+
+int orc_argmax(const float *v, int n) {
+  int best = -1;
+  for (int i = 0; i < n; ++i)
+    if (v[i] == v[i] && (best < 0 || v[i] > v[best])) best = i;
+  return best;
+}
+
+/* ---------------------------------------------------------------- one decode step */
+
+int orc_decode_step(const orc_config *c, const orc_layer *layers, const orc_head *head,
+                    const int32_t *page_table, int pos, int token, float *h, float *trace,
+                    float *logits, int nthreads) {
+  const int H = c->hidden, Hq = c->n_heads, Hkv = c->n_kv_heads, D = c->head_dim, I = c->inter;
+  const int qd = Hq * D, kvd = Hkv * D, T = pos + 1;
+  const double scale = 1.0 / sqrt((double)D);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+  float *a = (float *)malloc(sizeof(float) * (size_t)(H > qd ? H : qd));
+  float *q = (float *)malloc(sizeof(float) * (size_t)qd);
+  float *k = (float *)malloc(sizeof(float) * (size_t)kvd);
+  float *v = (float *)malloc(sizeof(float) * (size_t)kvd);
+  float *att = (float *)malloc(sizeof(float) * (size_t)qd);
+  float *g = (float *)malloc(sizeof(float) * (size_t)I);
+  float *u = (float *)malloc(sizeof(float) * (size_t)I);
+  float *m = (float *)malloc(sizeof(float) * (size_t)I);
+
+  /* embedding: the bf16 row of the token, widened exactly to fp32 */
+  if (c->has_embedding)
+    for (int i = 0; i < H; ++i) h[i] = orc_bf16_to_f32(head->embed[(int64_t)token * H + i]);
+  if (trace) memcpy(trace, h, sizeof(float) * (size_t)H);
+
+  for (int l = 0; l < c->n_layers; ++l) {
+    const orc_layer *L = &layers[l];
+    /* attention block: pre-norm, q/k/v projections with bias (Qwen2) */
+    orc_rmsnorm(h, L->g_attn, a, 1, H, c->eps);
+    orc_gemv(c->wfmt, L->wq, L->sq, c->group, a, c->has_bias ? L->bq : NULL, NULL, q, qd, H, nthreads);
+    orc_gemv(c->wfmt, L->wk, L->sk, c->group, a, c->has_bias ? L->bk : NULL, NULL, k, kvd, H, nthreads);
+    orc_gemv(c->wfmt, L->wv, L->sv, c->group, a, c->has_bias ? L->bv : NULL, NULL, v, kvd, H, nthreads);
+    if (c->has_qk_norm) { /* per-head RMSNorm of q and k (Qwen3), before RoPE */
+      orc_rmsnorm(q, L->g_q, q, Hq, D, c->eps);
+      orc_rmsnorm(k, L->g_k, k, Hkv, D, c->eps);
+    }
+    orc_rope(q, Hq, D, pos, c->rope_base);
+    orc_rope(k, Hkv, D, pos, c->rope_base);
+    /* append the new token, then attend over keys 0..pos read back from the cache */
+    orc_kv_store(L->k_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, k);
+    orc_kv_store(L->v_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, v);
+    orc_attention(q, L->k_pool, L->v_pool, c->kv_fmt, page_table, c->page_size, T, Hq, Hkv, D, scale,
+                  att, NULL);
+    orc_gemv(c->wfmt, L->wo, L->so, c->group, att, NULL, h, h, H, qd, nthreads);
+    /* MLP block: pre-norm, SwiGLU, down projection */
+    orc_rmsnorm(h, L->g_ffn, a, 1, H, c->eps);
+    orc_gemv(c->wfmt, L->wg, L->sg, c->group, a, NULL, NULL, g, I, H, nthreads);
+    orc_gemv(c->wfmt, L->wu, L->su, c->group, a, NULL, NULL, u, I, H, nthreads);
+    orc_swiglu(g, u, m, I);
+    orc_gemv(c->wfmt, L->wd, L->sd, c->group, m, NULL, h, h, H, I, nthreads);
+    if (trace) memcpy(trace + (int64_t)(l + 1) * H, h, sizeof(float) * (size_t)H);
+  }
+
+  int next = -1;
+  if (c->has_lm_head) {
+    orc_rmsnorm(h, head->g_out, a, 1, H, c->eps);
+    float *lg = logits ? logits : (float *)malloc(sizeof(float) * (size_t)c->vocab);
+    orc_gemv(c->wfmt, head->w_lm, head->s_lm, c->group, a, NULL, NULL, lg, c->vocab, H, nthreads);
+    next = orc_argmax(lg, c->vocab);
+    if (!logits) free(lg);
+  }
+  free(a); free(q); free(k); free(v); free(att); free(g); free(u); free(m);
+  return next;
+}

@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with a closed form,
+an invariant, a library routine, a page-printed figure, a hand-derived case, or the independent
+numpy decoder.  ``tests/test_oracle_pins.py`` runs them against the oracle, and
+``tests/test_oracle_mutants.py`` runs them against deliberately broken copies of the oracle to
+show that each plausible mistake is caught by at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+from dataclasses import replace
+from fractions import Fraction
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle as O
+import synth as S
+
+from np_decoder import NumpyDecoder, logical_kv
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                out[k] = int(v)
+    return out
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _f16_bits(vals):
+    return np.asarray(vals, np.float16).view(np.uint16)
+
+
+# ----------------------------------------------------------------------------- number formats
+def check_f16_decode_exhaustive():
+    """All 65536 binary16 patterns against numpy's binary16 -> binary32 conversion, bit for bit."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = O.f16_to_f32(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def check_bf16_round_nearest_even():
+    """Tie cases by hand, then random values against torch's bf16 rounding."""
+    ties = {0x3F808000: 0x3F80, 0x3F818000: 0x3F82, 0x3F80C000: 0x3F81, 0x3F807FFF: 0x3F80,
+            0x7F800000: 0x7F80, 0xFF800000: 0xFF80, 0x7F7FFFFF: 0x7F80, 0x00000000: 0x0000,
+            0x80000000: 0x8000}
+    for fbits, want in ties.items():
+        f = np.array([fbits], np.uint32).view(np.float32)
+        assert int(O.f32_to_bf16(f)[0]) == want, hex(fbits)
+    r = _rng(1)
+    x = (r.standard_normal(4000) * np.exp(r.uniform(-30, 30, 4000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16(x), ref)
+
+
+# ----------------------------------------------------------------------------- dequant + GEMV
+def check_int4_codes_by_hand():
+    """Per-weight INT4 contract: mask 4 bits, subtract the zero point 8, times the group's fp16
+    scale.  Byte j of a row holds k = 2j (bits 0-3) and k = 2j+1 (bits 4-7)."""
+    K = 128
+    W = np.full((1, K // 2), 0x88, np.uint8)          # every code 8 -> level 0
+    W[0, 0] = 0x1F                                      # k=0: 15 -> +7 ; k=1: 1 -> -7
+    W[0, 32] = 0x0F                                     # k=64: 15 -> +7 ; k=65: 0 -> -8
+    S_ = _f16_bits([1.0, 2.0]).reshape(1, 2)
+    w = O.dequant_row("q4", W, S_, 0, K, 64)
+    want = np.zeros(K, np.float32)
+    want[0], want[1], want[64], want[65] = 7.0, -7.0, 14.0, -16.0
+    assert np.array_equal(w, want)
+    # a scale that is not a power of two: the product stays exact in fp32
+    s3 = np.float16(0.0133)
+    S3 = np.array([[s3.view(np.uint16), s3.view(np.uint16)]], np.uint16)
+    w3 = O.dequant_row("q4", W, S3, 0, K, 64)
+    assert w3[0] == np.float32(7) * np.float32(s3) and w3[65] == np.float32(-8) * np.float32(s3)
+
+
+def check_int8_onehot():
+    """x = e_k gives column k of the dequantised matrix: fl32(q * s), bit for bit."""
+    r = _rng(2)
+    N, K = 37, 48
+    q = r.integers(-127, 128, (N, K)).astype(np.int8)
+    s = ((0.02 / 127) * r.uniform(0.5, 1.5, N)).astype(np.float32)
+    for k in (0, 1, 17, K - 1):
+        x = np.zeros(K, np.float32); x[k] = 1.0
+        y = O.gemv("q8", q, s, x)
+        assert np.array_equal(y, q[:, k].astype(np.float32) * s)
+
+
+def check_gemv_ones_closed_form():
+    """x = 1: y_n = sum_g s_g * sum_{k in g} (nib - 8), exact rational arithmetic."""
+    r = _rng(3)
+    N, K, grp = 9, 192, 64
+    W = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    sv = r.uniform(0.005, 0.02, (N, K // grp)).astype(np.float16)
+    y = O.gemv("q4", W, sv.view(np.uint16), np.ones(K, np.float32), group=grp)
+    for n in range(N):
+        tot = Fraction(0)
+        for g in range(K // grp):
+            lev = 0
+            for k in range(g * grp, (g + 1) * grp):
+                byte = int(W[n, k // 2])
+                lev += ((byte >> 4) if k % 2 else (byte & 15)) - 8
+            tot += Fraction(float(sv[n, g])) * lev
+        assert y[n] == np.float32(float(tot)), n
+    # int8: sum of fp32 products; the closed form s * sum(q) holds to fp32 rounding of each term
+    q = r.integers(-127, 128, (N, K)).astype(np.int8)
+    s = np.full(N, np.float32(0.02 / 127))
+    y8 = O.gemv("q8", q, s, np.ones(K, np.float32))
+    exact = s.astype(np.float64) * q.astype(np.int64).sum(1)
+    bound = np.abs(q).astype(np.float64).sum(1) * float(s[0]) * 2.0 ** -24 + np.abs(exact) * 2.0 ** -24
+    assert np.all(np.abs(y8 - exact) <= bound + 1e-30)
+
+
+def check_gemv_bruteforce():
+    """Both formats, with bias and residual, against an independent numpy dequant + fp64 matmul."""
+    from np_decoder import dequant
+    r = _rng(4)
+    for wfmt, grp in (("q8", 64), ("q4", 64), ("q4", 32)):
+        N, K = 45, 192
+        if wfmt == "q8":
+            W = r.integers(-127, 128, (N, K)).astype(np.int8)
+            Sc = ((0.02 / 127) * r.uniform(0.5, 1.5, N)).astype(np.float32)
+        else:
+            W = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
+            Sc = r.uniform(0.005, 0.02, (N, K // grp)).astype(np.float16).view(np.uint16)
+        x = r.standard_normal(K).astype(np.float32)
+        b = (0.02 * r.standard_normal(N)).astype(np.float32)
+        res = r.standard_normal(N).astype(np.float32)
+        y = O.gemv(wfmt, W, Sc, x, bias=b, residual=res, group=grp)
+        ref = dequant(wfmt, W, Sc, grp) @ x.astype(np.float64) + b + res
+        assert np.allclose(y, ref, rtol=1e-6, atol=1e-6), wfmt
+        y0 = O.gemv(wfmt, W, Sc, x, group=grp)
+        assert np.allclose(y0, dequant(wfmt, W, Sc, grp) @ x.astype(np.float64), rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+def check_rmsnorm_closed_forms():
+    r = _rng(5)
+    dim, eps = 64, 1e-6
+    g = (1 + 0.1 * r.standard_normal(dim)).astype(np.float32)
+    for c in (0.7, 1e-3, 25.0):
+        y = O.rmsnorm(np.full(dim, c, np.float32), g, eps)
+        want = g.astype(np.float64) * np.float32(c) / math.sqrt(float(np.float32(c)) ** 2 + eps)
+        assert np.allclose(y, want, rtol=2e-7, atol=0), c
+    x = r.standard_normal((3, dim)).astype(np.float32)
+    y = O.rmsnorm(x, g, eps).astype(np.float64)
+    ms = np.mean(x.astype(np.float64) ** 2, axis=1)
+    assert np.allclose(np.mean((y / g) ** 2, axis=1), ms / (ms + eps), rtol=1e-6)
+    y2 = O.rmsnorm(1000.0 * x, g, eps)
+    assert np.allclose(y2, y, rtol=2e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- RoPE
+def check_rope_invariants():
+    r = _rng(6)
+    D, base = 128, 1e6
+    x = r.standard_normal((5, D)).astype(np.float32)
+    assert np.array_equal(O.rope(x, 0, base), x)                      # R(0) = I
+    y = O.rope(x, 32768, base)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-6)
+    q, k = x[0], x[1]
+    for m, n in ((1000, 400), (4096, 4095), (17, 0), (32768, 3)):
+        lhs = float(O.rope(q, m, base).astype(np.float64) @ O.rope(k, n, base).astype(np.float64))
+        rhs = float(O.rope(q, m - n, base).astype(np.float64) @ k.astype(np.float64))
+        assert abs(lhs - rhs) <= 1e-5 * np.linalg.norm(q) * np.linalg.norm(k), (m, n)
+
+
+def check_rope_textbook_cases():
+    # D = 2: the textbook 2x2 rotation by angle pos (theta_0 = base^0 = 1)
+    for pos in (1, 3, 1000):
+        v = np.array([0.6, -1.3], np.float32)
+        R = np.array([[math.cos(pos), -math.sin(pos)], [math.sin(pos), math.cos(pos)]])
+        assert np.allclose(O.rope(v, pos, 1e6), R @ v.astype(np.float64), rtol=1e-6, atol=1e-7)
+    # D = 8, pairs (i, i + 4), theta_i = base^(-2i/8)
+    base = 100.0
+    for i in range(4):
+        e = np.zeros(8, np.float32); e[i] = 1.0
+        pos = 20
+        phi = pos * base ** (-2.0 * i / 8)
+        want = np.zeros(8); want[i] = math.cos(phi); want[i + 4] = math.sin(phi)
+        assert np.allclose(O.rope(e, pos, base), want, atol=1e-7), i
+        e2 = np.zeros(8, np.float32); e2[i + 4] = 1.0
+        want2 = np.zeros(8); want2[i] = -math.sin(phi); want2[i + 4] = math.cos(phi)
+        assert np.allclose(O.rope(e2, pos, base), want2, atol=1e-7), i
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+def check_swiglu_identities():
+    r = _rng(7)
+    g = (3 * r.standard_normal(1000)).astype(np.float32)
+    u = r.standard_normal(1000).astype(np.float32)
+    m = O.swiglu(g, u)
+    ref = g.astype(np.float64) * scipy.special.expit(g.astype(np.float64)) * u
+    assert np.allclose(m, ref, rtol=1e-6, atol=1e-12)
+    assert np.all(O.swiglu(np.zeros(4, np.float32), np.full(4, 5.0, np.float32)) == 0)
+    one = np.ones_like(g)
+    assert np.allclose(O.swiglu(-g, one).astype(np.float64), O.swiglu(g, one).astype(np.float64) - g,
+                       rtol=0, atol=2e-6 * (1 + np.abs(g)))
+    big = np.full(3, 40.0, np.float32)
+    assert np.allclose(O.swiglu(big, np.full(3, 2.0, np.float32)), 80.0, rtol=1e-7)
+
+
+# ----------------------------------------------------------------------------- paged KV + attention
+def _pool(r, P, Hkv, D, fmt, ps=16):
+    a = r.standard_normal((P, Hkv, ps, D)).astype(np.float32)
+    if fmt == "bf16":
+        return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return a
+
+
+def _logical(pool, pt, T, fmt, ps=16):
+    t = np.arange(T)
+    a = pool[pt[t // ps], :, t % ps, :]
+    if fmt == "bf16":
+        a = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    return a.astype(np.float64)            # [T][Hkv][D]
+
+
+def check_attention_bruteforce():
+    r = _rng(8)
+    Hq, Hkv, D = 4, 2, 8
+    for fmt in ("f32", "bf16"):
+        for T in (1, 2, 5, 17, 49):
+            P = -(-T // 16) + 1
+            pt = r.permutation(P).astype(np.int32)
+            kp, vp = _pool(r, P, Hkv, D, fmt), _pool(r, P, Hkv, D, fmt)
+            q = (2 * r.standard_normal((Hq, D))).astype(np.float32)
+            out, probs = O.attention(q, kp, vp, fmt, pt, T, probs=True)
+            Kl, Vl = _logical(kp, pt, T, fmt), _logical(vp, pt, T, fmt)
+            for h in range(Hq):
+                j = h // (Hq // Hkv)
+                p = scipy.special.softmax(Kl[:, j, :] @ q[h].astype(np.float64) / math.sqrt(D))
+                assert np.allclose(out[h], p @ Vl[:, j, :], rtol=1e-6, atol=1e-7), (fmt, T, h)
+                assert np.allclose(probs[h], p, rtol=1e-6, atol=1e-9)
+            assert np.allclose(probs.astype(np.float64).sum(1), 1.0, atol=1e-6)
+
+
+def check_attention_special_cases():
+    r = _rng(9)
+    Hq, Hkv, D, fmt = 6, 2, 8, "f32"
+    P = 4
+    pt = np.array([2, 0, 3, 1], np.int32)
+    kp, vp = _pool(r, P, Hkv, D, fmt), _pool(r, P, Hkv, D, fmt)
+    q = r.standard_normal((Hq, D)).astype(np.float32)
+    # T = 1: the only probability is exactly 1, so out is v of token 0 bit for bit
+    out = O.attention(q, kp, vp, fmt, pt, 1)
+    for h in range(Hq):
+        assert np.array_equal(out[h], vp[pt[0], h // 3, 0, :])
+    # equal scores (q = 0): the mean of V
+    T = 37
+    out = O.attention(np.zeros((Hq, D), np.float32), kp, vp, fmt, pt, T)
+    Vl = _logical(vp, pt, T, fmt)
+    for h in range(Hq):
+        assert np.allclose(out[h], Vl[:, h // 3, :].mean(0), rtol=1e-6, atol=1e-7)
+    # GQA map: V of KV head j constant c_j -> every query head of group j returns c_j
+    vc = np.zeros_like(vp)
+    vc[:, 0], vc[:, 1] = 1.5, -4.0
+    out = O.attention(q, kp, vc, fmt, pt, T)
+    assert np.allclose(out[:3], 1.5, rtol=1e-6) and np.allclose(out[3:], -4.0, rtol=1e-6)
+    # the same logical context behind two different page tables gives the same output
+    pt2 = np.array([1, 3, 0, 2], np.int32)
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[pt2], vp2[pt2] = kp[pt], vp[pt]
+    assert np.array_equal(O.attention(q, kp, vp, fmt, pt, T), O.attention(q, kp2, vp2, fmt, pt2, T))
+
+
+def check_kv_layout_against_page_figures():
+    """16 KiB pages, 4 KiB per KV-head slice, 1 KB of K per token per layer (Qwen2.5-7B shape)."""
+    dims = read_golden("qwen25_7b_dims.txt")
+    Hkv, D, ps = dims["n_kv_heads"], dims["head_dim"], dims["page_tokens"]
+    P = 3
+    pool = np.zeros((P, Hkv, ps, D), np.uint16)
+    pt = np.array([2, 0, 1], np.int32)
+    t = 16 + 5                                       # logical page 1 -> physical page 0, slot 5
+    kv = np.ones((Hkv, D), np.float32)
+    O.kv_store(pool, "bf16", pt, ps, t, kv)
+    nz = np.flatnonzero(pool.view(np.uint8).reshape(-1))
+    assert nz.size == dims["kv_bytes_per_token_per_layer"]          # 4 * 128 * 2 bytes
+    page_bytes = pool[0].nbytes
+    assert page_bytes == dims["kv_page_bytes"] and page_bytes % dims["page_alignment_bytes"] == 0
+    assert pool[0, 0].nbytes == dims["kv_head_slice_bytes"]
+    assert nz.min() == 0 * page_bytes + 5 * D * 2                    # physical page 0, head 0, slot 5
+    for j in range(Hkv):
+        off = j * dims["kv_head_slice_bytes"] + 5 * D * 2
+        assert np.all(pool.view(np.uint8).reshape(-1)[off:off + 2 * D] != 0)
+    assert O.kv_store is not None and float(O.lib().orc_kv_load(
+        O._p(pool), 2, O._p(pt), ps, Hkv, D, t, 3, 127)) == 1.0
+
+
+def check_workload_shapes_against_pages():
+    d7 = read_golden("qwen25_7b_dims.txt")
+    for name in ("qwen2.5-7b-q4", "qwen2.5-7b-q4-32k"):
+        wl = S.WORKLOADS[name]
+        assert (wl.n_layers, wl.hidden, wl.inter, wl.vocab) == (
+            d7["n_layers"], d7["hidden"], d7["inter"], d7["vocab"])
+        assert (wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.page_size) == (
+            d7["n_heads"], d7["n_kv_heads"], d7["head_dim"], d7["page_tokens"])
+    d15 = read_golden("qwen25_15b_meta.txt")
+    wl = S.WORKLOADS["qwen2.5-1.5b-q8"]
+    assert (wl.n_layers, wl.n_heads, wl.n_kv_heads) == (d15["n_layers"], d15["n_heads"], d15["n_kv_heads"])
+    assert S.WORKLOADS["qwen2.5-7b-q4-32k"].ctx <= d15["context_length"]
+
+
+# ----------------------------------------------------------------------------- argmax
+def check_argmax_ties():
+    assert O.argmax(np.array([1, 3, 3, 2], np.float32)) == 1
+    assert O.argmax(np.array([5, 5], np.float32)) == 0
+    assert O.argmax(np.array([np.nan, 1, 2], np.float32)) == 2
+    assert O.argmax(np.array([-1, -1, -1], np.float32)) == 0
+    v = np.zeros(152064, np.float32); v[[9, 70000, 152063]] = 4.0
+    assert O.argmax(v) == 9
+
+
+# ----------------------------------------------------------------------------- decode step
+def _zero_scales(model):
+    for P in model["layers"]:
+        for s in ("sq", "sk", "sv", "so", "sg", "su", "sd"):
+            P[s] = np.zeros_like(P[s])
+    if "s_lm" in model:
+        model["s_lm"] = np.zeros_like(model["s_lm"])
+    return model
+
+
+def check_decode_zero_weights_identity():
+    """With every weight scale 0 each layer is the identity on h, bit for bit; logits are 0 and
+    the greedy token is 0 (smallest index among equal maxima)."""
+    for wfmt in ("q8", "q4"):
+        wl = S.tiny(wfmt)
+        m = _zero_scales(S.make_model(wl))
+        kv = S.make_kv(wl, 16)
+        r = O.OracleDecoder(m, kv).step(wl.ctx, m["token"], trace=True)
+        e = m["embed"][m["token"]].astype(np.uint32) << 16
+        for row in r["trace"]:
+            assert np.array_equal(row.view(np.uint32), e)
+        assert np.all(r["logits"] == 0) and r["token"] == 0
+
+
+def check_decode_against_numpy(steps: int = 3):
+    """The C oracle against the independent numpy decoder on tiny models, several steps."""
+    variants = [S.tiny("q8"), S.tiny("q4"), S.tiny("q8", qk_norm=True, qkv_bias=False),
+                S.tiny("q4", kv_fmt="f32", shuffled_pages=True)]
+    for wl in variants:
+        m = S.make_model(wl)
+        kv = S.make_kv(wl, 32)
+        od = O.OracleDecoder(m, kv)
+        kl, vl = logical_kv(kv, wl, wl.n_layers)
+        nd = NumpyDecoder(m, kl, vl)
+        tok = m["token"]
+        for s in range(steps):
+            pos = wl.ctx + s
+            a = od.step(pos, tok, trace=True)
+            b = nd.step(pos, tok)
+            scale = np.abs(b["trace"]).max(axis=1, keepdims=True)
+            assert np.all(np.abs(a["trace"] - b["trace"]) <= 1e-5 * scale), (wl.name, s)
+            assert np.allclose(a["logits"], b["logits"], rtol=0, atol=1e-5 * np.abs(b["logits"]).max())
+            srt = np.sort(b["logits"].astype(np.float64))
+            if srt[-1] - srt[-2] > 1e-5 * abs(srt[-1]):
+                assert a["token"] == b["token"], (wl.name, s)
+            tok = b["token"]
+
+
+ALL_CHECKS = [
+    check_f16_decode_exhaustive, check_bf16_round_nearest_even, check_int4_codes_by_hand,
+    check_int8_onehot, check_gemv_ones_closed_form, check_gemv_bruteforce,
+    check_rmsnorm_closed_forms, check_rope_invariants, check_rope_textbook_cases,
+    check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
+    check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,
+    check_decode_zero_weights_identity, check_decode_against_numpy,
+]

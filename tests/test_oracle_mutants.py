@@ -1,0 +1,84 @@
+"""Mutation check of the oracle pins (CPU only).
+
+Each mutant is a copy of the oracle source with one plausible mistake planted in it (a dropped
+term, a wrong sign, a wrong index, a swapped operand), compiled to a temporary library.  The
+pins of tests/oracle_pins.py must reject every mutant; a mutant that passes them all means a
+class of mistakes the pins cannot see.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle as O
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(O.__file__), "qdec_oracle.c")
+
+# (name, [(old, new), ...]): every `old` must occur exactly once in the oracle source
+MUTANTS = [
+    ("f16_rebias", [("(e + 112u)", "(e + 111u)")]),
+    ("bf16_truncate", [("b += 0x7FFFu + lsb;", "b += 0u * lsb;")]),
+    ("int4_zero_point", [("(float)(nib - 8)", "(float)(nib - 7)")]),
+    ("int4_nibble_order", [("(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
+                            "(k % 2 == 0) ? (byte >> 4) : (byte & 0x0F)")]),
+    ("int4_group_index", [("s[k / group]", "s[(k / group) / 2]")]),
+    ("int8_row_scale", [("float s = ((const float *)S)[row];", "float s = ((const float *)S)[0];")]),
+    ("gemv_drop_bias", [("if (bias) acc += (double)bias[n];", "")]),
+    ("rms_drop_eps", [("sqrt(ss / dim + eps)", "sqrt(ss / dim)")]),
+    ("rms_sum_not_mean", [("sqrt(ss / dim + eps)", "sqrt(ss + eps)")]),
+    ("rms_drop_gain", [("double g = gamma ? (double)gamma[i] : 1.0;", "double g = 1.0;")]),
+    ("rope_sign", [("xr[i] = (float)(a * c - b * s);", "xr[i] = (float)(a * c + b * s);")]),
+    ("rope_schedule", [("pow(base, -2.0 * (double)i / (double)dim)",
+                        "pow(base, -1.0 * (double)i / (double)dim)")]),
+    ("rope_pairing", [("int half = dim / 2;", "int half = dim / 4;")]),
+    ("swiglu_sign", [("z / (1.0 + exp(-z))", "z / (1.0 + exp(z))")]),
+    ("swiglu_swap", [("double z = g[i];", "double z = u[i];"), ("(double)u[i]", "(double)g[i]")]),
+    ("attn_drop_scale", [("s[t] = acc * scale;", "s[t] = acc;")]),
+    ("attn_head_map", [("int j = h / G;", "int j = h % Hkv;")]),
+    ("attn_page_table", [("int64_t page = page_table[t / page_size];",
+                          "int64_t page = t / page_size;")]),
+    ("step_exclude_new_token", [("T = pos + 1;", "T = pos;")]),
+    ("step_v_from_k", [("Hkv, D, pos, v);", "Hkv, D, pos, k);")]),
+    ("step_drop_o_residual", [("att, NULL, h, h, H, qd", "att, NULL, NULL, h, H, qd")]),
+    ("step_drop_down_residual", [("m, NULL, h, h, H, I", "m, NULL, NULL, h, H, I")]),
+    ("step_ffn_uses_attn_gain", [("orc_rmsnorm(h, L->g_ffn, a, 1, H, c->eps);",
+                                  "orc_rmsnorm(h, L->g_attn, a, 1, H, c->eps);")]),
+    ("step_drop_qk_norm", [("orc_rmsnorm(q, L->g_q, q, Hq, D, c->eps);", "")]),
+    ("step_drop_final_norm", [("orc_rmsnorm(h, head->g_out, a, 1, H, c->eps);",
+                               "memcpy(a, h, sizeof(float) * (size_t)H);")]),
+    ("step_embed_row", [("head->embed[(int64_t)token * H + i]",
+                         "head->embed[(int64_t)token * H + (H - 1 - i)]")]),
+    ("argmax_last_tie", [("v[i] > v[best]", "v[i] >= v[best]")]),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(name, edits, source, tmp_path):
+    src = source
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation site for {name} not unique: {old!r}"
+        src = src.replace(old, new)
+    c = tmp_path / "mutant.c"
+    c.write_text(src)
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-I", os.path.dirname(SRC), str(c), "-o", str(so), "-lm"])
+    caught = []
+    try:
+        O.use_library(str(so))
+        for chk in P.ALL_CHECKS:
+            try:
+                chk()
+            except AssertionError:
+                caught.append(chk.__name__)
+                break
+    finally:
+        O.use_library(None)
+    assert caught, f"mutant {name} passed every pin"

@@ -24,11 +24,11 @@ KV_F32, KV_BF16 = 1, 2
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    """Compile the oracle with gcc (-O3, no fast-math, no FMA contraction: IEEE semantics kept)."""
     stale = not os.path.exists(_SO) or any(os.path.getmtime(_SO) < os.path.getmtime(s) for s in _SRCS)
     if force or stale:
         tmp = _SO + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                                "-fno-fast-math", _SRCS[0], "-o", tmp, "-lm"])
         os.replace(tmp, _SO)
     return _SO
@@ -137,7 +137,7 @@ def gemv(wfmt, W, S, x, bias=None, residual=None, group=64, nthreads=0) -> np.nd
     b = None if bias is None else np.ascontiguousarray(bias, np.float32)
     r = None if residual is None else np.ascontiguousarray(residual, np.float32)
     lib().orc_gemv(_fmt(wfmt), _p(W), _p(S), group, _p(x), _p(b), _p(r), _p(y), N, K,
-                   nthreads or os.cpu_count() or 1)
+                   nthreads or int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1)
     return y
 
 
@@ -196,7 +196,7 @@ class OracleDecoder:
     def __init__(self, model: dict, kv: dict, copy_kv: bool = True, nthreads: int = 0):
         wl = model["workload"]
         self.wl = wl
-        self.nthreads = nthreads or os.cpu_count() or 1
+        self.nthreads = nthreads or int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
         layers = model["layers"]
         self._keep = [model]
         self.k = [a.copy() if copy_kv else a for a in kv["k"][: len(layers)]]

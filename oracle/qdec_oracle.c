@@ -92,11 +92,14 @@ void orc_dequant_row(int fmt, const void *W, const void *S, int group, int64_t r
     for (int k = 0; k < K; ++k) w[k] = (float)q[k] * s;
   } else {
     const uint8_t *b = (const uint8_t *)W + row * (int64_t)(K / 2);
-    const uint16_t *s = (const uint16_t *)S + row * (int64_t)(K / group);
-    for (int k = 0; k < K; ++k) {
-      uint8_t byte = b[k / 2];
-      int nib = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
-      w[k] = (float)(nib - 8) * orc_f16_to_f32(s[k / group]);
+    const uint16_t *sc = (const uint16_t *)S + row * (int64_t)(K / group);
+    for (int g = 0; g < K / group; ++g) {
+      float s = orc_f16_to_f32(sc[g]); /* the scale of k in [g*group, (g+1)*group) */
+      for (int k = g * group; k < (g + 1) * group; ++k) {
+        uint8_t byte = b[k / 2];
+        int nib = (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+        w[k] = (float)(nib - 8) * s;
+      }
     }
   }
 }

@@ -22,7 +22,7 @@ MUTANTS = [
     ("int4_zero_point", [("(float)(nib - 8)", "(float)(nib - 7)")]),
     ("int4_nibble_order", [("(k % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
                             "(k % 2 == 0) ? (byte >> 4) : (byte & 0x0F)")]),
-    ("int4_group_index", [("s[k / group]", "s[(k / group) / 2]")]),
+    ("int4_group_index", [("orc_f16_to_f32(sc[g])", "orc_f16_to_f32(sc[g / 2])")]),
     ("int8_row_scale", [("float s = ((const float *)S)[row];", "float s = ((const float *)S)[0];")]),
     ("gemv_drop_bias", [("if (bias) acc += (double)bias[n];", "")]),
     ("rms_drop_eps", [("sqrt(ss / dim + eps)", "sqrt(ss / dim)")]),
@@ -68,7 +68,7 @@ def test_pins_reject_mutant(name, edits, source, tmp_path):
     c = tmp_path / "mutant.c"
     c.write_text(src)
     so = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+    subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                            "-I", os.path.dirname(SRC), str(c), "-o", str(so), "-lm"])
     caught = []
     try:

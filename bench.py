@@ -1,0 +1,181 @@
+"""Decode-step benchmark: Qwen2.5-7B-shaped INT4 (groups of 64) model, paged bf16 KV of 4096
+tokens, batch 1, greedy, one hipGraph replay per token, on one MI355X.
+
+Prints one JSON line.  `value` is decode throughput (tokens/s) over K timed graph replays with
+the inputs resident in HBM; `roofline` relates the algorithmic bytes of the dominant kernel to
+its launch duration measured with HIP events on its own stream; `cpu_baseline` times the CPU
+oracle on a bounded sample (whole decode steps) of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def step_bytes(wl, T: int) -> int:
+    """Algorithmic HBM bytes of one decode step at T = pos + 1 attended keys: every quantized
+    weight and scale once, biases and norm gains, one embedding row, the lm head, the KV read
+    (each KV byte once per KV head) and the new token's K/V write."""
+    H, I, D = wl.hidden, wl.inter, wl.head_dim
+    qd, kvd = wl.n_heads * D, wl.n_kv_heads * D
+    mats = [(qd + 2 * kvd, H), (H, qd), (2 * I, H), (H, I)]
+
+    def wbytes(N, K):
+        if wl.wfmt == "q4":
+            return N * K // 2 + N * (K // wl.group) * 2
+        return N * K + N * 4
+
+    per_layer = sum(wbytes(N, K) for N, K in mats) + 2 * H * 4
+    if wl.qkv_bias:
+        per_layer += (qd + 2 * kvd) * 4
+    if wl.qk_norm:
+        per_layer += 2 * D * 4
+    kvb = 4 if wl.kv_fmt == "f32" else 2
+    per_layer += 2 * kvd * kvb * T + 2 * kvd * kvb
+    total = wl.n_layers * per_layer
+    if wl.has_lm_head:
+        total += wbytes(wl.vocab, H) + H * 4 + H * 2
+    return total
+
+
+def dominant_kernel_bytes(wl) -> int:
+    """Packed gate/up GEMV of one layer (weights + scales): the largest per-layer kernel."""
+    N, K = 2 * wl.inter, wl.hidden
+    if wl.wfmt == "q4":
+        return N * K // 2 + N * (K // wl.group) * 2
+    return N * K + N * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qwen2.5-7b-q4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the decode step on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import quantized_gemv_gqa_amd as q
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    max_ctx = wl.ctx + W + K + 16
+    t0 = time.time()
+    model = synth.make_model(wl)
+    kv = synth.make_kv(wl, max_ctx)
+    gen_s = time.time() - t0
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dm = q.upload_model(model, dev)
+    dk = q.upload_kv(kv, wl.kv_fmt, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    st = q.DecodeStep(dm, dk, pos0=wl.ctx, token0=model.get("token", 0), log_len=W + K, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            st.step(q.STEP_GRAPH)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(K):
+            st.step(q.STEP_GRAPH)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / K
+    pos_end = int(st.pos.item())
+    assert pos_end == wl.ctx + W + K, pos_end
+    tokens = st.token_log.cpu().numpy()
+    T0 = wl.ctx + W + 1
+    bytes_timed = sum(step_bytes(wl, T0 + i) for i in range(K))
+    gbps_step = bytes_timed / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    # dominant kernel: the gate/up GEMV of a layer, one HIP event pair around each launch on the
+    # stream it runs on; the layer rotates so the weights come from HBM, not from cache
+    xin = torch.randn(wl.hidden, device=dev)
+    y_gu = torch.empty(2 * wl.inter, device=dev)
+    gu_ws = q.gemv_workspace(wl.wfmt, 2 * wl.inter, wl.hidden, dev)
+    reps = 56
+    layers = dm["layers"]
+    with torch.cuda.stream(stream):
+        def gu(i):
+            d = layers[i % len(layers)]
+            q.gemv(wl.wfmt, d["w_gu"], d["s_gu"], xin, 2 * wl.inter, y=y_gu, workspace=gu_ws, group=wl.group)
+
+        for i in range(5):
+            gu(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            gu(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+    us_gu = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    gu_bytes = dominant_kernel_bytes(wl)
+    gu_gbps = gu_bytes / (us_gu * 1e-6) / 1e9
+
+    out = {
+        "metric": "decode ms/token + achieved HBM GB/s (% of peak), Qwen2.5-7B-shape INT4, 1 GPU",
+        "value": K / (e0.elapsed_time(e1) * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": [wl.n_heads, wl.n_kv_heads],
+                   "head_dim": wl.head_dim, "inter": wl.inter, "vocab": wl.vocab, "weights": "int4 g%d zp8 fp16 scales" % wl.group,
+                   "kv": "paged bf16, 16-token pages, shuffled", "context": wl.ctx, "batch": 1,
+                   "submission": "hipGraph replay per token", "kernels_per_step": st.kernel_count,
+                   "num_splits": st.cfg.num_splits},
+        "step_bytes": bytes_timed / K,
+        "step_gbps": gbps_step,
+        "step_frac_of_peak": gbps_step / HBM_PEAK_GBPS,
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "kernel": "gate/up GEMV (INT4, %dx%d)" % (2 * wl.inter, wl.hidden),
+                     "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gu_gbps / HBM_PEAK_GBPS,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": us_gu, "traffic": None},
+        "tokens_head": [int(t) for t in tokens[:8]],
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+        od = oracle.OracleDecoder(model, kv, nthreads=nthreads)
+        tok = model.get("token", 0)
+        n, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and n < 64:
+            c0 = time.perf_counter()
+            r = od.step(wl.ctx + n, tok, logits=True)
+            t_cpu += time.perf_counter() - c0
+            tok = r["token"]
+            n += 1
+        out["cpu_baseline"] = {"value": n / t_cpu, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+                               "sample": "%d whole decode steps of the same model from position %d (greedy)" % (n, wl.ctx)}
+    out["gen_s"] = gen_s
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

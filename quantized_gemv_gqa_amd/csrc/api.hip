@@ -1,0 +1,237 @@
+// C-ABI entry points of libqdec: host-side argument checks, then kernel launches.
+// Every check happens before the first HIP call, so a rejected call leaves the device untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "qdec_internal.h"
+
+namespace qdec {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+qdec_status check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  return QDEC_OK;
+}
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace qdec
+
+using namespace qdec;
+
+extern "C" {
+
+const char *qdec_last_error(void) { return g_err; }
+const char *qdec_version(void) { return "qdec 0.1 (gfx950)"; }
+
+size_t qdec_packed_weight_bytes(int wfmt, int N, int K) {
+  if (N < 1 || K < 1) return 0;
+  const size_t npad = (size_t)((N + kTile - 1) / kTile) * kTile;
+  if (wfmt == QDEC_W_Q8_ROW) return npad * (size_t)K;
+  if (wfmt == QDEC_W_Q4_G_ZP8) return npad * (size_t)K / 2;
+  return 0;
+}
+
+size_t qdec_packed_scale_bytes(int wfmt, int N, int K, int group) {
+  if (N < 1 || K < 1) return 0;
+  const size_t npad = (size_t)((N + kTile - 1) / kTile) * kTile;
+  if (wfmt == QDEC_W_Q8_ROW) return npad * sizeof(float);
+  if (wfmt == QDEC_W_Q4_G_ZP8 && group > 0 && K % group == 0) return npad * (size_t)(K / group) * 2;
+  return 0;
+}
+
+qdec_status qdec_pack_q8(const int8_t *W, const float *scale, int N, int K, void *Wp, float *Sp,
+                         void *stream) {
+  QDEC_REQUIRE(W && scale && Wp && Sp, QDEC_EINVAL, "qdec_pack_q8: null pointer");
+  QDEC_REQUIRE(N >= 1 && K >= 16 && K % 16 == 0, QDEC_EINVAL,
+               "qdec_pack_q8: need N >= 1 and K a positive multiple of 16 (N=%d K=%d)", N, K);
+  QDEC_REQUIRE(aligned(W, 16) && aligned(Wp, 16) && aligned(Sp, 4) && aligned(scale, 4), QDEC_EINVAL,
+               "qdec_pack_q8: W and Wp must be 16-byte aligned");
+  if (launch_pack_q8(W, scale, N, K, reinterpret_cast<uint8_t *>(Wp), Sp, (hipStream_t)stream) !=
+      hipSuccess)
+    return check_launch("qdec_pack_q8");
+  return QDEC_OK;
+}
+
+qdec_status qdec_pack_q4(const uint8_t *W, const uint16_t *scale, int N, int K, int group, void *Wp,
+                         uint16_t *Sp, void *stream) {
+  QDEC_REQUIRE(W && scale && Wp && Sp, QDEC_EINVAL, "qdec_pack_q4: null pointer");
+  QDEC_REQUIRE(group >= 32 && group <= 4096 && (group & (group - 1)) == 0, QDEC_EUNSUPPORTED,
+               "qdec_pack_q4: group must be 32 times a power of two (got %d)", group);
+  QDEC_REQUIRE(N >= 1 && K >= group && K % group == 0, QDEC_EINVAL,
+               "qdec_pack_q4: need N >= 1 and K a multiple of group (N=%d K=%d group=%d)", N, K, group);
+  QDEC_REQUIRE(aligned(W, 16) && aligned(Wp, 16) && aligned(Sp, 2) && aligned(scale, 2), QDEC_EINVAL,
+               "qdec_pack_q4: W and Wp must be 16-byte aligned");
+  if (launch_pack_q4(W, scale, N, K, group, reinterpret_cast<uint8_t *>(Wp), Sp,
+                     (hipStream_t)stream) != hipSuccess)
+    return check_launch("qdec_pack_q4");
+  return QDEC_OK;
+}
+
+size_t qdec_gemv_workspace_bytes(int wfmt, int N, int K) {
+  if (N < 1 || K < 1 || (wfmt != QDEC_W_Q8_ROW && wfmt != QDEC_W_Q4_G_ZP8)) return 0;
+  return gemv_workspace_bytes(wfmt, N, K);
+}
+
+static qdec_status gemv_common(int wfmt, const void *Wp, const void *Sp, int group, const float *x,
+                               const float *bias, const float *residual, float *y, int N, int K,
+                               void *ws, size_t ws_bytes, void *stream, const char *name) {
+  QDEC_REQUIRE(Wp && Sp && x && y, QDEC_EINVAL, "%s: null pointer", name);
+  QDEC_REQUIRE(N >= 1 && K >= 1, QDEC_EINVAL, "%s: N and K must be >= 1 (N=%d K=%d)", name, N, K);
+  if (wfmt == QDEC_W_Q8_ROW) {
+    QDEC_REQUIRE(K % 16 == 0, QDEC_EINVAL, "%s: K must be a multiple of 16 (K=%d)", name, K);
+  } else {
+    QDEC_REQUIRE(group >= 32 && group <= 4096 && (group & (group - 1)) == 0, QDEC_EUNSUPPORTED,
+                 "%s: group must be 32 times a power of two (got %d)", name, group);
+    QDEC_REQUIRE(K % group == 0, QDEC_EINVAL, "%s: K must be a multiple of group (K=%d group=%d)",
+                 name, K, group);
+  }
+  QDEC_REQUIRE(aligned(Wp, 16) && aligned(x, 16) && aligned(y, 4), QDEC_EINVAL,
+               "%s: packed weights and x must be 16-byte aligned", name);
+  QDEC_REQUIRE(x != y && !(x < y + N && y < x + K), QDEC_EINVAL, "%s: x must not overlap y", name);
+  const bool split = ws != nullptr;
+  if (split) {
+    QDEC_REQUIRE(aligned(ws, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", name);
+    QDEC_REQUIRE(ws_bytes >= gemv_workspace_bytes(wfmt, N, K), QDEC_EINVAL,
+                 "%s: workspace too small (%zu < %zu bytes)", name, ws_bytes,
+                 gemv_workspace_bytes(wfmt, N, K));
+  }
+  GemvPlan p = gemv_plan(wfmt, N, K, split);
+  GemvArgs a{};
+  a.W = reinterpret_cast<const uint8_t *>(Wp);
+  a.S = Sp;
+  a.x = x;
+  a.bias = bias;
+  a.residual = residual;
+  a.y = y;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.epi = EPI_STORE;
+  gemv_bind_workspace(a, p, ws);
+  if (launch_gemv(wfmt, a, p, (hipStream_t)stream) != hipSuccess) return check_launch(name);
+  return QDEC_OK;
+}
+
+qdec_status qdec_gemv_q8(const void *Wp, const float *Sp, const float *x, const float *bias,
+                         const float *residual, float *y, int N, int K, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return gemv_common(QDEC_W_Q8_ROW, Wp, Sp, 0, x, bias, residual, y, N, K, workspace,
+                     workspace_bytes, stream, "qdec_gemv_q8");
+}
+
+qdec_status qdec_gemv_q4(const void *Wp, const uint16_t *Sp, int group, const float *x,
+                         const float *bias, const float *residual, float *y, int N, int K,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  return gemv_common(QDEC_W_Q4_G_ZP8, Wp, Sp, group, x, bias, residual, y, N, K, workspace,
+                     workspace_bytes, stream, "qdec_gemv_q4");
+}
+
+qdec_status qdec_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
+                              float eps, float rope_base, const int32_t *pos, void *stream) {
+  QDEC_REQUIRE(x && y, QDEC_EINVAL, "qdec_rmsnorm_rope: null pointer");
+  QDEC_REQUIRE(rows >= 1 && dim >= 2 && dim <= 256 && dim % 2 == 0, QDEC_EINVAL,
+               "qdec_rmsnorm_rope: need rows >= 1 and even dim in [2, 256] (rows=%d dim=%d)", rows,
+               dim);
+  QDEC_REQUIRE(!(rope_base > 0.f) || pos, QDEC_EINVAL, "qdec_rmsnorm_rope: RoPE needs pos");
+  QDEC_REQUIRE(!gamma || (eps >= 0.f && std::isfinite(eps)), QDEC_EINVAL,
+               "qdec_rmsnorm_rope: eps must be finite and >= 0");
+  if (launch_rmsnorm_rope(x, gamma, y, rows, dim, eps, rope_base, pos, (hipStream_t)stream) !=
+      hipSuccess)
+    return check_launch("qdec_rmsnorm_rope");
+  return QDEC_OK;
+}
+
+qdec_status qdec_swiglu(const float *gate, const float *up, float *out, int n, void *stream) {
+  QDEC_REQUIRE(gate && up && out, QDEC_EINVAL, "qdec_swiglu: null pointer");
+  QDEC_REQUIRE(n >= 1, QDEC_EINVAL, "qdec_swiglu: n must be >= 1 (n=%d)", n);
+  if (launch_swiglu(gate, up, out, n, (hipStream_t)stream) != hipSuccess) return check_launch("qdec_swiglu");
+  return QDEC_OK;
+}
+
+qdec_status qdec_argmax(const float *logits, int n, int32_t *token, void *stream) {
+  QDEC_REQUIRE(logits && token, QDEC_EINVAL, "qdec_argmax: null pointer");
+  QDEC_REQUIRE(n >= 1, QDEC_EINVAL, "qdec_argmax: n must be >= 1 (n=%d)", n);
+  if (launch_argmax_finish(logits, n, token, nullptr, nullptr, nullptr, 0, (hipStream_t)stream) !=
+      hipSuccess)
+    return check_launch("qdec_argmax");
+  return QDEC_OK;
+}
+
+size_t qdec_attn_workspace_bytes(int n_heads, int head_dim, int num_splits) {
+  if (n_heads < 1 || head_dim < 1 || num_splits < 1) return 0;
+  return attn_workspace_bytes(n_heads, head_dim, num_splits);
+}
+
+qdec_status qdec_attn_decode_paged(const float *q, const float *k_new, const float *v_new,
+                                   void *k_pool, void *v_pool, int kv_fmt, const int32_t *page_table,
+                                   int n_pages, int page_size, const int32_t *pos, int n_heads,
+                                   int n_kv_heads, int head_dim, float sm_scale, int num_splits,
+                                   void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  const char *nm = "qdec_attn_decode_paged";
+  QDEC_REQUIRE(q && k_pool && v_pool && page_table && pos && workspace && out, QDEC_EINVAL,
+               "%s: null pointer", nm);
+  QDEC_REQUIRE((k_new == nullptr) == (v_new == nullptr), QDEC_EINVAL,
+               "%s: k_new and v_new must both be given or both be NULL", nm);
+  QDEC_REQUIRE(kv_fmt == QDEC_KV_F32 || kv_fmt == QDEC_KV_BF16, QDEC_EUNSUPPORTED,
+               "%s: unknown kv_fmt %d", nm, kv_fmt);
+  QDEC_REQUIRE(page_size == QDEC_PAGE_SIZE, QDEC_EUNSUPPORTED, "%s: page_size must be 16 (got %d)", nm,
+               page_size);
+  QDEC_REQUIRE(n_heads >= 1 && n_kv_heads >= 1 && n_heads % n_kv_heads == 0, QDEC_EINVAL,
+               "%s: n_heads must be a positive multiple of n_kv_heads (%d, %d)", nm, n_heads, n_kv_heads);
+  QDEC_REQUIRE(n_heads / n_kv_heads <= 8, QDEC_EUNSUPPORTED,
+               "%s: at most 8 query heads per KV head (got %d)", nm, n_heads / n_kv_heads);
+  QDEC_REQUIRE(head_dim == 64 || head_dim == 128, QDEC_EUNSUPPORTED,
+               "%s: head_dim must be 64 or 128 (got %d)", nm, head_dim);
+  QDEC_REQUIRE(num_splits >= 1 && num_splits <= kMaxMergeSplits, QDEC_EINVAL, "%s: num_splits in [1, %d]", nm,
+               kMaxMergeSplits);
+  QDEC_REQUIRE(n_kv_heads <= (int)(kAttnCounterBytes / 4), QDEC_EUNSUPPORTED, "%s: at most %d KV heads", nm,
+               (int)(kAttnCounterBytes / 4));
+  QDEC_REQUIRE(n_pages >= 1, QDEC_EINVAL, "%s: n_pages must be >= 1", nm);
+  QDEC_REQUIRE(std::isfinite(sm_scale), QDEC_EINVAL, "%s: sm_scale must be finite", nm);
+  QDEC_REQUIRE(workspace_bytes >= attn_workspace_bytes(n_heads, head_dim, num_splits), QDEC_EINVAL,
+               "%s: workspace too small", nm);
+  QDEC_REQUIRE(aligned(k_pool, 16) && aligned(v_pool, 16) && aligned(q, 16) && aligned(workspace, 256),
+               QDEC_EINVAL, "%s: q and pools must be 16-byte, workspace 256-byte aligned", nm);
+  hipStream_t st = (hipStream_t)stream;
+  if (k_new) {
+    if (launch_kv_append(k_new, v_new, k_pool, v_pool, kv_fmt, page_table, n_pages, pos, n_kv_heads,
+                         head_dim, st) != hipSuccess)
+      return check_launch(nm);
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_fmt = kv_fmt;
+  a.page_table = page_table;
+  a.n_pages = n_pages;
+  a.pos = pos;
+  a.Hq = n_heads;
+  a.Hkv = n_kv_heads;
+  a.D = head_dim;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.splits = num_splits;
+  a.counters = reinterpret_cast<unsigned *>(workspace);
+  a.ws = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kAttnCounterBytes);
+  a.out = out;
+  if (launch_attention(a, st) != hipSuccess) return check_launch(nm);
+  return QDEC_OK;
+}
+
+}  // extern "C"

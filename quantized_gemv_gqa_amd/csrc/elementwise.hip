@@ -1,0 +1,260 @@
+// Small per-step kernels: q/k RMSNorm + RoPE + KV append, RMSNorm/RoPE rows, SwiGLU, embedding
+// gather, greedy argmax.  Each is a few KB of traffic per step; they are written for latency
+// (one wave per head or row, wave64 shuffles) rather than bandwidth.
+//
+// Definitions (naive-CUDA Qwen engine post, part 1): RMSNorm y = g * x / sqrt(mean(x^2) + eps)
+// (section RMSNorm); RoPE rotates coordinate pairs as 2-D rotations by position-proportional
+// angles (section Rope) with the rotate-half pairing (i, i + D/2) and theta_i = base^(-2i/D);
+// SwiGLU multiplies the Swish of one projection by the other (section SwiGLU), Swish taken with
+// beta = 1 on the gate projection; greedy sampling picks the largest logit (section Sampler),
+// the smallest index on ties, done on the GPU so one int leaves the device (FlashQwen README,
+// "Optimization study", stage 5).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "qdec_internal.h"
+
+namespace qdec {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t b = __builtin_bit_cast(uint32_t, f);
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// One wave normalises (optional) and rotates (optional) one row of `dim` <= 256 values.
+// src and dst may alias.  On return the final row is also in `buf` (LDS, >= dim floats, private
+// to the single-wave workgroup) and visible to every lane.
+__device__ void norm_rope_row(const float *src, float *dst, int dim, const float *gamma, float eps,
+                              float base, int pos, float *buf) {
+  const int lane = threadIdx.x & 63;
+  float v[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < dim) ? src[e] : 0.f;
+    ss += v[i] * v[i];
+  }
+  if (gamma) {
+    const float r = rsqrtf(wave_sum(ss) / (float)dim + eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < dim) v[i] = gamma[e] * (v[i] * r);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < dim) buf[e] = v[i];
+  }
+  __syncthreads();
+  if (base > 0.f) {
+    const int half = dim / 2;
+    double ra[2], rb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = lane + 64 * c;
+      if (i < half) {
+        const double theta = pow((double)base, -2.0 * (double)i / (double)dim);
+        const double phi = (double)pos * theta;
+        double sn, cs;
+        sincos(phi, &sn, &cs);
+        const double a = buf[i], b = buf[i + half];
+        ra[c] = a * cs - b * sn;
+        rb[c] = b * cs + a * sn;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = lane + 64 * c;
+      if (i < half) {
+        buf[i] = (float)ra[c];
+        buf[i + half] = (float)rb[c];
+      }
+    }
+    __syncthreads();
+  }
+  for (int e = lane; e < dim; e += 64) dst[e] = buf[e];
+}
+
+__device__ __forceinline__ void store_kv(void *pool, int kv_fmt, size_t e, float v) {
+  if (kv_fmt == QDEC_KV_BF16)
+    reinterpret_cast<uint16_t *>(pool)[e] = float_to_bf16_rne(v);
+  else
+    reinterpret_cast<float *>(pool)[e] = v;
+}
+
+// grid: Hq + 2 Hkv waves, one per q head, k head, v head (in that order)
+__global__ void __launch_bounds__(64) qkv_post(QkvPostArgs a) {
+  __shared__ float buf[256];
+  const int hh = blockIdx.x;
+  const int D = a.D;
+  const int t = *a.pos;
+  float *x;
+  int kind, j;
+  if (hh < a.Hq) {
+    kind = 0; j = hh; x = a.qkv + (size_t)hh * D;
+  } else if (hh < a.Hq + a.Hkv) {
+    kind = 1; j = hh - a.Hq; x = a.qkv + (size_t)(a.Hq + j) * D;
+  } else {
+    kind = 2; j = hh - a.Hq - a.Hkv; x = a.qkv + (size_t)(a.Hq + a.Hkv + j) * D;
+  }
+  if (kind < 2) {
+    norm_rope_row(x, x, D, kind == 0 ? a.g_q : a.g_k, a.eps, a.rope_base, t, buf);
+  }
+  if (kind == 0 || !a.k_pool) return;
+  const int phys = a.page_table[t >> 4];
+  if (phys < 0 || phys >= a.n_pages) return;
+  void *pool = (kind == 1) ? a.k_pool : a.v_pool;
+  const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (t & 15)) * D;
+  for (int d = threadIdx.x; d < D; d += 64) store_kv(pool, a.kv_fmt, e0 + d, kind == 1 ? buf[d] : x[d]);
+}
+
+__global__ void __launch_bounds__(64) rmsnorm_rope_rows(const float *x, const float *gamma, float *y,
+                                                        int dim, float eps, float base,
+                                                        const int32_t *pos) {
+  __shared__ float buf[256];
+  const int row = blockIdx.x;
+  const int t = pos ? *pos : 0;
+  norm_rope_row(x + (size_t)row * dim, y + (size_t)row * dim, dim, gamma, eps, base, t, buf);
+}
+
+__global__ void swiglu_k(const float *__restrict__ g, const float *__restrict__ u, float *__restrict__ m, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float z = g[i];
+    m[i] = (z / (1.0f + expf(-z))) * u[i];
+  }
+}
+
+// grid: ceil(H/64) waves.  E == null: h is given, only the per-tile sums of squares are written.
+__global__ void __launch_bounds__(64) embed_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ token,
+                                              int H, int V, float *h, float *__restrict__ ssq) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  float v = 0.f;
+  if (E) {
+    int tok = *token;
+    if (tok < 0 || tok >= V) tok = 0;  // documented precondition; never read outside the table
+    if (i < H) {
+      v = __builtin_bit_cast(float, (uint32_t)E[(size_t)tok * H + i] << 16);
+      h[i] = v;
+    }
+  } else if (i < H) {
+    v = h[i];
+  }
+  const float s = wave_sum(v * v);
+  if (threadIdx.x == 0) ssq[blockIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(1024) argmax_finish_k(const float *__restrict__ logits, int n,
+                                                        int32_t *token, int32_t *pos, int32_t *log,
+                                                        int32_t *step, int log_len) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int tid = threadIdx.x;
+  int bi = INT_MAX;
+  float bv = -INFINITY;
+  if (logits) {
+    for (int i = tid; i < n; i += 1024) {
+      const float v = logits[i];
+      if (v == v && (bi == INT_MAX || v > bv)) {  // strict: the first index of a maximum wins
+        bv = v;
+        bi = i;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o, 64);
+      const int i2 = __shfl_xor(bi, o, 64);
+      if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    if ((tid & 63) == 0) {
+      sv[tid >> 6] = bv;
+      si[tid >> 6] = bi;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (logits) {
+      bv = sv[0];
+      bi = si[0];
+      for (int w = 1; w < 16; ++w) {
+        const int i2 = si[w];
+        const float v2 = sv[w];
+        if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+          bv = v2;
+          bi = i2;
+        }
+      }
+      if (bi == INT_MAX) bi = 0;  // all NaN: token 0
+      *token = bi;
+      if (log && step) {
+        const int s = *step;
+        if (s >= 0 && s < log_len) log[s] = bi;
+      }
+    }
+    if (step) *step += 1;
+    if (pos) *pos += 1;
+  }
+}
+
+__global__ void copy_k(const float *__restrict__ s, float *__restrict__ d, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) d[i] = s[i];
+}
+
+}  // namespace
+
+hipError_t launch_qkv_post(const QkvPostArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(qkv_post, dim3(a.Hq + 2 * a.Hkv), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
+                               float eps, float rope_base, const int32_t *pos, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_rope_rows, dim3(rows), dim3(64), 0, st, x, gamma, y, dim, eps, rope_base,
+                     pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStream_t st) {
+  int blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(swiglu_k, dim3(blocks), dim3(256), 0, st, g, u, m, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(embed_k, dim3((H + 63) / 64), dim3(64), 0, st, E, token, H, V, h, ssq);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int32_t *pos,
+                                int32_t *token_log, int32_t *step_count, int log_len,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(argmax_finish_k, dim3(1), dim3(1024), 0, st, logits, n, token, pos, token_log,
+                     step_count, log_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const float *src, float *dst, int n, hipStream_t st) {
+  hipLaunchKernelGGL(copy_k, dim3((n + 255) / 256), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace qdec

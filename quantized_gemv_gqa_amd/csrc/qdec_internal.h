@@ -1,0 +1,122 @@
+// Internal declarations shared by the qdec HIP sources (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qdec.h"
+
+namespace qdec {
+
+constexpr int kWave = 64;
+constexpr int kTile = QDEC_TILE_ROWS;  // rows per packed tile = lanes per wave
+
+// ---------------------------------------------------------------------------------- errors
+void set_error(const char *fmt, ...);
+#define QDEC_REQUIRE(cond, code, ...)        \
+  do {                                       \
+    if (!(cond)) {                           \
+      ::qdec::set_error(__VA_ARGS__);        \
+      return (code);                         \
+    }                                        \
+  } while (0)
+qdec_status check_launch(const char *what);
+
+// ---------------------------------------------------------------------------------- GEMV
+enum GemvEpilogue : int {
+  EPI_STORE = 0,   // y[n] = acc (+bias) (+residual)
+  EPI_SWIGLU = 1,  // packed rows pair gate/up by half tile; y[i] = silu(g_i) * u_i
+  EPI_ARGMAX = 2,  // y[n] = acc, then greedy token over all rows (lm head): *token, log, pos += 1
+};
+
+struct GemvArgs {
+  const uint8_t *W;        // packed weights
+  const void *S;           // packed scales (q8: fp32 [Npad], q4: fp16 [tiles][K/group][64])
+  const float *x;          // activation [K]
+  const float *gamma;      // RMSNorm gain [K] or null: x' = gamma * x, finalizer multiplies by r
+  const float *ssq;        // per-tile partial sums of x^2 (ssq_n of them), used with gamma
+  int ssq_n;
+  float eps;
+  const float *bias;       // [N] or null
+  const float *residual;   // [N] or null (may alias y)
+  float *y;                // output
+  float *ssq_out;          // if non-null: per-tile sum of y^2 over the tile's valid rows
+  float *part;             // split-K partials [tiles][ks][64]
+  unsigned *counters;      // [tiles] arrival counters, zero between launches
+  int N, K, group;
+  int ks, cps;             // k splits, chunks per split
+  int epi;
+  // EPI_ARGMAX: per-tile (value, index) candidates [2 * tiles] and the step scalars
+  float *cand;
+  int32_t *token, *pos, *token_log, *step_count;
+  int log_len;
+};
+
+struct GemvPlan {
+  int tiles, nch, ks, cps, units, blocks;
+};
+GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split);
+size_t gemv_workspace_bytes(int wfmt, int N, int K, bool argmax = false);
+void gemv_bind_workspace(GemvArgs &a, const GemvPlan &p, void *ws);
+hipError_t launch_gemv(int wfmt, const GemvArgs &a, const GemvPlan &p, hipStream_t st);
+
+hipError_t launch_pack_q8(const int8_t *W, const float *S, int N, int K, uint8_t *Wp, float *Sp,
+                          hipStream_t st);
+hipError_t launch_pack_q4(const uint8_t *W, const uint16_t *S, int N, int K, int group, uint8_t *Wp,
+                          uint16_t *Sp, hipStream_t st);
+
+// ---------------------------------------------------------------------------------- attention
+struct AttnArgs {
+  const float *q;          // [Hq][D] (already rotated)
+  void *k_pool, *v_pool;
+  int kv_fmt;
+  const int32_t *page_table;
+  int n_pages;
+  const int32_t *pos;      // device scalar: token index of the newest key (T = pos + 1)
+  int Hq, Hkv, D;
+  float scale_log2;        // sm_scale * log2(e)
+  int splits;              // <= kMaxMergeSplits
+  float *ws;               // [splits][Hq][D + 2] partials
+  unsigned *counters;      // [Hkv] arrival counters, zero between launches
+  float *out;              // [Hq][D]
+};
+constexpr int kMaxMergeSplits = 256;
+constexpr size_t kAttnCounterBytes = 256;  // counters of up to 64 KV heads
+size_t attn_workspace_bytes(int Hq, int D, int splits);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+
+// Append one token's k, v ([Hkv][D] fp32) into the pools at *pos.
+hipError_t launch_kv_append(const float *k, const float *v, void *k_pool, void *v_pool, int kv_fmt,
+                            const int32_t *page_table, int n_pages, const int32_t *pos, int Hkv,
+                            int D, hipStream_t st);
+
+// ---------------------------------------------------------------------------------- small ops
+// Per-head post-processing of a fused qkv vector: optional per-head RMSNorm of q and k, RoPE of
+// q and k at *pos, then k and v stored into the pools (when k_pool != null).
+struct QkvPostArgs {
+  float *qkv;              // [(Hq + 2 Hkv) D], q and k rewritten in place
+  const float *g_q, *g_k;  // [D] or null
+  float eps;
+  float rope_base;         // <= 0: no rotation
+  const int32_t *pos;
+  int Hq, Hkv, D;
+  void *k_pool, *v_pool;   // null: no append
+  int kv_fmt;
+  const int32_t *page_table;
+  int n_pages;
+};
+hipError_t launch_qkv_post(const QkvPostArgs &a, hipStream_t st);
+
+hipError_t launch_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
+                               float eps, float rope_base, const int32_t *pos, hipStream_t st);
+hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStream_t st);
+// h = bf16 -> fp32 row E[*token] (E null: h is given), ssq[t] = sum of h^2 over rows 64t..64t+63
+hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
+                        hipStream_t st);
+// argmax over logits; writes *token, token_log[*step_count] (if log), advances *pos and
+// *step_count.  With logits == null it only advances *pos.
+hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int32_t *pos,
+                                int32_t *token_log, int32_t *step_count, int log_len,
+                                hipStream_t st);
+hipError_t launch_copy(const float *src, float *dst, int n, hipStream_t st);
+
+}  // namespace qdec

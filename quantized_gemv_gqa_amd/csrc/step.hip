@@ -1,0 +1,330 @@
+// One batch-1 decode step of a Qwen-style GQA decoder as a fixed list of kernel launches, run
+// eagerly or captured once into a hipGraph and replayed.
+//
+// Every per-step scalar the kernels need (token id, position, step count) lives in device memory
+// and is read by the kernels themselves, so one captured graph stays valid as the context grows
+// and across page boundaries (FlashQwen README, "Optimization study", stage 6: a single graph
+// whose kernels read token id / position from device buffers; the H100 runtime instead captured
+// two graphs and patched scalars before each launch, "How To Construct Your Personal LLM Runtime
+// From Scratch", section 6).  Region order per layer follows that post's ITL breakdown:
+// qkv_gemv -> append_tail_kv (with RoPE) -> paged_attention -> o_proj -> gate_up_gemv ->
+// swiglu_down.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "qdec_internal.h"
+
+struct qdec_step {
+  qdec_config cfg;
+  std::vector<qdec_layer_weights> layers;
+  qdec_model model;
+  std::vector<void *> kpools, vpools;
+  qdec_state state;
+  // workspace carve-up
+  float *qkv = nullptr, *attn = nullptr, *mlp = nullptr, *ssq = nullptr, *attn_ws = nullptr;
+  void *gemv_ws = nullptr;
+  qdec::GemvPlan p_qkv, p_o, p_gu, p_down, p_lm;
+  int ssq_n = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipStream_t graph_stream = nullptr;
+  int n_kernels = 0;
+};
+
+namespace qdec {
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, total;
+};
+
+Layout layout_of(const qdec_config &c) {
+  Layout L{};
+  const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int qd = c.n_heads * c.head_dim;
+  size_t off = 0;
+  L.qkv = off; off += align256((size_t)nqkv * 4);
+  L.attn = off; off += align256((size_t)qd * 4);
+  L.mlp = off; off += align256((size_t)c.inter * 4);
+  L.ssq = off; off += align256((size_t)((c.hidden + 63) / 64) * 4);
+  L.attn_ws = off; off += align256(attn_workspace_bytes(c.n_heads, c.head_dim, c.num_splits));
+  size_t g = gemv_workspace_bytes(c.wfmt, nqkv, c.hidden);
+  g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, qd));
+  g = std::max(g, gemv_workspace_bytes(c.wfmt, 2 * c.inter, c.hidden));
+  g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, c.inter));
+  if (c.vocab > 0) g = std::max(g, gemv_workspace_bytes(c.wfmt, c.vocab, c.hidden, true));
+  L.gemv_ws = off; off += align256(g);
+  L.total = off;
+  return L;
+}
+
+qdec_status validate(const qdec_config *c) {
+  QDEC_REQUIRE(c, QDEC_EINVAL, "qdec_step: null config");
+  QDEC_REQUIRE(c->n_layers >= 1 && c->hidden >= 16 && c->n_heads >= 1 && c->n_kv_heads >= 1 &&
+                   c->inter >= 32 && c->vocab >= 0,
+               QDEC_EINVAL, "qdec_step: bad model sizes");
+  QDEC_REQUIRE(c->n_heads % c->n_kv_heads == 0 && c->n_heads / c->n_kv_heads <= 8, QDEC_EUNSUPPORTED,
+               "qdec_step: need n_heads a multiple of n_kv_heads with at most 8 q heads per kv head");
+  QDEC_REQUIRE(c->head_dim == 64 || c->head_dim == 128, QDEC_EUNSUPPORTED,
+               "qdec_step: head_dim must be 64 or 128");
+  QDEC_REQUIRE(c->wfmt == QDEC_W_Q8_ROW || c->wfmt == QDEC_W_Q4_G_ZP8, QDEC_EUNSUPPORTED,
+               "qdec_step: unknown weight format %d", c->wfmt);
+  QDEC_REQUIRE(c->kv_fmt == QDEC_KV_F32 || c->kv_fmt == QDEC_KV_BF16, QDEC_EUNSUPPORTED,
+               "qdec_step: unknown kv format %d", c->kv_fmt);
+  QDEC_REQUIRE(c->page_size == QDEC_PAGE_SIZE && c->n_pages >= 1, QDEC_EUNSUPPORTED,
+               "qdec_step: page_size must be 16 and n_pages >= 1");
+  QDEC_REQUIRE(c->num_splits >= 1 && c->num_splits <= kMaxMergeSplits, QDEC_EINVAL,
+               "qdec_step: num_splits in [1, %d]", kMaxMergeSplits);
+  QDEC_REQUIRE(c->n_kv_heads <= (int)(kAttnCounterBytes / 4), QDEC_EUNSUPPORTED, "qdec_step: too many KV heads");
+  QDEC_REQUIRE(c->inter % 32 == 0, QDEC_EUNSUPPORTED, "qdec_step: inter must be a multiple of 32");
+  const int qd = c->n_heads * c->head_dim;
+  if (c->wfmt == QDEC_W_Q8_ROW) {
+    QDEC_REQUIRE(c->hidden % 16 == 0 && qd % 16 == 0 && c->inter % 16 == 0, QDEC_EINVAL,
+                 "qdec_step: Q8 needs hidden, n_heads*head_dim, inter multiples of 16");
+  } else {
+    QDEC_REQUIRE(c->group >= 32 && c->group <= 4096 && (c->group & (c->group - 1)) == 0, QDEC_EUNSUPPORTED, "qdec_step: bad Q4 group");
+    QDEC_REQUIRE(c->hidden % c->group == 0 && qd % c->group == 0 && c->inter % c->group == 0,
+                 QDEC_EINVAL, "qdec_step: Q4 needs hidden, n_heads*head_dim, inter multiples of group");
+  }
+  QDEC_REQUIRE(std::isfinite(c->rms_eps) && c->rms_eps >= 0.f && c->rope_base > 0.f, QDEC_EINVAL,
+               "qdec_step: bad eps / rope_base");
+  return QDEC_OK;
+}
+
+GemvArgs gemv_args(const qdec_step *h, const void *W, const void *S, const float *x, float *y, int N,
+                   int K, const GemvPlan &p) {
+  GemvArgs a{};
+  a.W = reinterpret_cast<const uint8_t *>(W);
+  a.S = S;
+  a.x = x;
+  a.y = y;
+  a.N = N;
+  a.K = K;
+  a.group = h->cfg.group;
+  a.eps = h->cfg.rms_eps;
+  a.ssq = h->ssq;
+  a.ssq_n = h->ssq_n;
+  a.epi = EPI_STORE;
+  gemv_bind_workspace(a, p, h->gemv_ws);
+  return a;
+}
+
+#define QDEC_CK(expr)                                      \
+  do {                                                     \
+    hipError_t e_ = (expr);                                \
+    if (e_ != hipSuccess) {                                \
+      set_error("%s: %s", #expr, hipGetErrorString(e_));   \
+      return QDEC_EHIP;                                    \
+    }                                                      \
+    ++n;                                                   \
+  } while (0)
+
+// Enqueue one whole step; returns the number of kernels launched through `count`.
+qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
+  const qdec_config &c = h->cfg;
+  const qdec_state &s = h->state;
+  const int H = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.inter;
+  const int qd = Hq * D, nqkv = (Hq + 2 * Hkv) * D;
+  const int wf = c.wfmt;
+  int n = 0;
+  QDEC_CK(launch_embed(h->model.embed, s.token, H, c.vocab, s.hidden, h->ssq, st));
+  if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace, H, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const qdec_layer_weights &w = h->layers[l];
+    // attention block
+    GemvArgs a = gemv_args(h, w.w_qkv, w.s_qkv, s.hidden, h->qkv, nqkv, H, h->p_qkv);
+    a.gamma = w.g_attn;
+    a.bias = c.has_qkv_bias ? w.b_qkv : nullptr;
+    QDEC_CK(launch_gemv(wf, a, h->p_qkv, st));
+    QkvPostArgs qp{};
+    qp.qkv = h->qkv;
+    qp.g_q = c.has_qk_norm ? w.g_q : nullptr;
+    qp.g_k = c.has_qk_norm ? w.g_k : nullptr;
+    qp.eps = c.rms_eps;
+    qp.rope_base = c.rope_base;
+    qp.pos = s.pos;
+    qp.Hq = Hq;
+    qp.Hkv = Hkv;
+    qp.D = D;
+    qp.k_pool = h->kpools[l];
+    qp.v_pool = h->vpools[l];
+    qp.kv_fmt = c.kv_fmt;
+    qp.page_table = s.page_table;
+    qp.n_pages = c.n_pages;
+    QDEC_CK(launch_qkv_post(qp, st));
+    AttnArgs at{};
+    at.q = h->qkv;
+    at.k_pool = h->kpools[l];
+    at.v_pool = h->vpools[l];
+    at.kv_fmt = c.kv_fmt;
+    at.page_table = s.page_table;
+    at.n_pages = c.n_pages;
+    at.pos = s.pos;
+    at.Hq = Hq;
+    at.Hkv = Hkv;
+    at.D = D;
+    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    at.splits = c.num_splits;
+    at.counters = reinterpret_cast<unsigned *>(h->attn_ws);
+    at.ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
+    at.out = h->attn;
+    QDEC_CK(launch_attention(at, st));
+    GemvArgs o = gemv_args(h, w.w_o, w.s_o, h->attn, s.hidden, H, qd, h->p_o);
+    o.residual = s.hidden;
+    o.ssq_out = h->ssq;
+    QDEC_CK(launch_gemv(wf, o, h->p_o, st));
+    // MLP block
+    GemvArgs g = gemv_args(h, w.w_gu, w.s_gu, s.hidden, h->mlp, 2 * I, H, h->p_gu);
+    g.gamma = w.g_ffn;
+    g.epi = EPI_SWIGLU;
+    QDEC_CK(launch_gemv(wf, g, h->p_gu, st));
+    GemvArgs d = gemv_args(h, w.w_down, w.s_down, h->mlp, s.hidden, H, I, h->p_down);
+    d.residual = s.hidden;
+    d.ssq_out = h->ssq;
+    QDEC_CK(launch_gemv(wf, d, h->p_down, st));
+    if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace + (size_t)(l + 1) * H, H, st));
+  }
+  if (h->model.w_lm) {
+    // lm head with the greedy argmax, token write and position advance fused in its epilogue
+    GemvArgs a = gemv_args(h, h->model.w_lm, h->model.s_lm, s.hidden, s.logits, c.vocab, H, h->p_lm);
+    a.gamma = h->model.g_out;
+    a.epi = EPI_ARGMAX;
+    a.token = s.token;
+    a.pos = s.pos;
+    a.token_log = s.token_log;
+    a.step_count = s.step_count;
+    a.log_len = s.log_len;
+    QDEC_CK(launch_gemv(wf, a, h->p_lm, st));
+  } else {
+    QDEC_CK(launch_argmax_finish(nullptr, 0, nullptr, s.pos, nullptr, s.step_count, 0, st));
+  }
+  if (count) *count = n;
+  return QDEC_OK;
+}
+
+}  // namespace
+}  // namespace qdec
+
+using namespace qdec;
+
+extern "C" {
+
+size_t qdec_step_workspace_bytes(const qdec_config *cfg) {
+  if (validate(cfg) != QDEC_OK) return 0;
+  return layout_of(*cfg).total;
+}
+
+qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const qdec_state *s,
+                             qdec_step **out) {
+  qdec_status r = validate(cfg);
+  if (r != QDEC_OK) return r;
+  QDEC_REQUIRE(m && s && out && m->layers, QDEC_EINVAL, "qdec_step_create: null argument");
+  QDEC_REQUIRE(s->k_pools && s->v_pools && s->page_table && s->pos && s->hidden && s->workspace,
+               QDEC_EINVAL, "qdec_step_create: state is missing pools, page table, pos, hidden or workspace");
+  const bool lm = m->w_lm != nullptr;
+  QDEC_REQUIRE(!lm || (cfg->vocab >= 1 && m->s_lm && m->g_out && s->logits && s->token), QDEC_EINVAL,
+               "qdec_step_create: an lm head needs vocab, s_lm, g_out, logits and token");
+  QDEC_REQUIRE(!m->embed || (cfg->vocab >= 1 && s->token), QDEC_EINVAL,
+               "qdec_step_create: an embedding needs vocab and token");
+  QDEC_REQUIRE(!s->token_log || (s->step_count && s->log_len >= 1), QDEC_EINVAL,
+               "qdec_step_create: token_log needs step_count and log_len");
+  const Layout L = layout_of(*cfg);
+  QDEC_REQUIRE(s->workspace_bytes >= L.total, QDEC_EINVAL,
+               "qdec_step_create: workspace too small (%zu < %zu bytes)", s->workspace_bytes, L.total);
+  QDEC_REQUIRE((reinterpret_cast<uintptr_t>(s->workspace) % 256) == 0, QDEC_EINVAL, "qdec_step_create: workspace must be 256-byte aligned");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const qdec_layer_weights &w = m->layers[l];
+    QDEC_REQUIRE(w.w_qkv && w.s_qkv && w.w_o && w.s_o && w.w_gu && w.s_gu && w.w_down && w.s_down &&
+                     w.g_attn && w.g_ffn,
+                 QDEC_EINVAL, "qdec_step_create: layer %d is missing a weight", l);
+    QDEC_REQUIRE(!cfg->has_qkv_bias || w.b_qkv, QDEC_EINVAL, "qdec_step_create: layer %d has no qkv bias", l);
+    QDEC_REQUIRE(!cfg->has_qk_norm || (w.g_q && w.g_k), QDEC_EINVAL,
+                 "qdec_step_create: layer %d has no q/k norm gains", l);
+    QDEC_REQUIRE(s->k_pools[l] && s->v_pools[l], QDEC_EINVAL, "qdec_step_create: layer %d has no KV pool", l);
+  }
+  qdec_step *h = new qdec_step();
+  h->cfg = *cfg;
+  h->layers.assign(m->layers, m->layers + cfg->n_layers);
+  h->model = *m;
+  h->model.layers = h->layers.data();
+  h->kpools.assign(s->k_pools, s->k_pools + cfg->n_layers);
+  h->vpools.assign(s->v_pools, s->v_pools + cfg->n_layers);
+  h->state = *s;
+  h->state.k_pools = h->kpools.data();
+  h->state.v_pools = h->vpools.data();
+  char *ws = reinterpret_cast<char *>(s->workspace);
+  h->qkv = reinterpret_cast<float *>(ws + L.qkv);
+  h->attn = reinterpret_cast<float *>(ws + L.attn);
+  h->mlp = reinterpret_cast<float *>(ws + L.mlp);
+  h->ssq = reinterpret_cast<float *>(ws + L.ssq);
+  h->attn_ws = reinterpret_cast<float *>(ws + L.attn_ws);
+  h->gemv_ws = ws + L.gemv_ws;
+  h->ssq_n = (cfg->hidden + 63) / 64;
+  const int qd = cfg->n_heads * cfg->head_dim;
+  const int nqkv = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+  h->p_qkv = gemv_plan(cfg->wfmt, nqkv, cfg->hidden, true);
+  h->p_o = gemv_plan(cfg->wfmt, cfg->hidden, qd, true);
+  h->p_gu = gemv_plan(cfg->wfmt, 2 * cfg->inter, cfg->hidden, true);
+  h->p_down = gemv_plan(cfg->wfmt, cfg->hidden, cfg->inter, true);
+  if (lm) h->p_lm = gemv_plan(cfg->wfmt, cfg->vocab, cfg->hidden, true);
+  *out = h;
+  return QDEC_OK;
+}
+
+qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
+  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_decode_step: null handle");
+  hipStream_t st = (hipStream_t)stream;
+  if (mode == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels);
+  QDEC_REQUIRE(mode == QDEC_STEP_GRAPH, QDEC_EINVAL, "qdec_decode_step: unknown mode %d", mode);
+  if (!h->exec) {
+    QDEC_REQUIRE(st != nullptr, QDEC_ESTATE,
+                 "qdec_decode_step: graph capture needs a non-default stream");
+    hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+      set_error("hipStreamBeginCapture: %s", hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    qdec_status r = enqueue_step(h, st, &h->n_kernels);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(st, &g);
+    if (r != QDEC_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return r;
+    }
+    if (e != hipSuccess) {
+      set_error("hipStreamEndCapture: %s", hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    e = hipGraphInstantiate(&h->exec, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      set_error("hipGraphInstantiate: %s", hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    h->graph = g;
+    h->graph_stream = st;
+  }
+  QDEC_REQUIRE(st == h->graph_stream, QDEC_ESTATE,
+               "qdec_decode_step: graph was captured on another stream");
+  hipError_t e = hipGraphLaunch(h->exec, st);
+  if (e != hipSuccess) {
+    set_error("hipGraphLaunch: %s", hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  return QDEC_OK;
+}
+
+int qdec_step_kernel_count(const qdec_step *h) { return h ? h->n_kernels : 0; }
+
+void qdec_step_destroy(qdec_step *h) {
+  if (!h) return;
+  if (h->exec) (void)hipGraphExecDestroy(h->exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+"""Per-op parity of the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bars: packing and dequant probes bit-exact; GEMV max-abs error over max-abs reference <= 2e-5
+(fp32 accumulation vs fp64); RMSNorm/RoPE/SwiGLU <= 2e-6 relative; attention <= 2e-5 relative,
+gather probes bit-exact; argmax exact (smallest index among the maxima).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import bf16_bits, dev, host, rel_max_err, sync
+
+q = pytest.importorskip("quantized_gemv_gqa_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_weights(rng, wfmt, N, K, group=64, jitter=True):
+    if wfmt == "q8":
+        W = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        s = (0.02 / 127) * (rng.uniform(0.5, 1.5, N) if jitter else np.ones(N))
+        return W, s.astype(np.float32)
+    W = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    S = rng.uniform(0.005, 0.02, (N, K // group)).astype(np.float16).view(np.uint16)
+    return W, S
+
+
+def _pack(wfmt, W, S, group=64):
+    if wfmt == "q8":
+        return q.pack_q8(dev(W), dev(S))
+    return q.pack_q4(dev(W), dev(S), group)
+
+
+# ----------------------------------------------------------------------------- packing
+@pytest.mark.parametrize("wfmt,N,K", [("q8", 100, 48), ("q8", 64, 16), ("q4", 130, 128), ("q4", 1, 64)])
+def test_pack_is_the_documented_permutation(wfmt, N, K):
+    rng = np.random.default_rng(1)
+    W, S = _rand_weights(rng, wfmt, N, K)
+    Wp, Sp = _pack(wfmt, W, S)
+    sync()
+    wp = host(Wp)
+    tiles = -(-N // 64)
+    rows = np.zeros((tiles * 64, W.shape[1]), np.uint8)
+    rows[:N] = W.view(np.uint8)
+    runs = W.shape[1] // 16
+    want = rows.reshape(tiles, 64, runs, 16).transpose(0, 2, 1, 3).reshape(-1)
+    assert np.array_equal(wp, want)
+    if wfmt == "q4":
+        ng = K // 64
+        srows = np.zeros((tiles * 64, ng), np.uint16)
+        srows[:N] = S
+        assert np.array_equal(host(Sp).view(np.uint16), srows.reshape(tiles, 64, ng).transpose(0, 2, 1).reshape(-1))
+    else:
+        sp = host(Sp)
+        assert np.array_equal(sp[:N], S) and np.all(sp[N:] == 0)
+
+
+# ----------------------------------------------------------------------------- GEMV
+GEMV_SHAPES = [
+    # single layer at hidden 896 (int8 rows): fused qkv, o, gate/up, down
+    ("q8", 1152, 896), ("q8", 896, 896), ("q8", 9728, 896), ("q8", 896, 4864),
+    # Qwen2.5-7B shape, INT4 groups of 64: fused qkv, o, gate/up, down
+    ("q4", 4608, 3584), ("q4", 3584, 3584), ("q4", 37888, 3584), ("q4", 3584, 18944),
+    # Qwen3-8B shape (int8): qkv, down
+    ("q8", 6144, 4096), ("q8", 4096, 12288),
+    # ragged rows and short K
+    ("q8", 200, 64), ("q4", 1000, 320), ("q4", 65, 64), ("q8", 1, 16), ("q4", 4097, 128),
+]
+
+
+@pytest.mark.parametrize("wfmt,N,K", GEMV_SHAPES)
+@pytest.mark.parametrize("split", [True, False])
+def test_gemv_parity(wfmt, N, K, split):
+    rng = np.random.default_rng(N * 7 + K)
+    W, S = _rand_weights(rng, wfmt, N, K)
+    x = rng.standard_normal(K).astype(np.float32)
+    b = (0.02 * rng.standard_normal(N)).astype(np.float32)
+    r = rng.standard_normal(N).astype(np.float32)
+    Wp, Sp = _pack(wfmt, W, S)
+    ws = q.gemv_workspace(wfmt, N, K) if split else None
+    y0 = q.gemv(wfmt, Wp, Sp, dev(x), N, workspace=ws)
+    y1 = q.gemv(wfmt, Wp, Sp, dev(x), N, bias=dev(b), residual=dev(r), workspace=ws)
+    sync()
+    ref0 = oracle.gemv(wfmt, W, S, x)
+    ref1 = oracle.gemv(wfmt, W, S, x, bias=b, residual=r)
+    assert rel_max_err(host(y0), ref0) <= 2e-5
+    assert rel_max_err(host(y1), ref1) <= 2e-5
+
+
+@pytest.mark.parametrize("wfmt,N,K", [("q8", 300, 256), ("q4", 300, 256), ("q4", 64, 18944)])
+def test_gemv_onehot_is_bit_exact(wfmt, N, K):
+    """x = e_k returns column k of the dequantised matrix bit for bit (no rounding is involved)."""
+    rng = np.random.default_rng(3)
+    W, S = _rand_weights(rng, wfmt, N, K)
+    Wp, Sp = _pack(wfmt, W, S)
+    ws = q.gemv_workspace(wfmt, N, K)
+    for k in (0, 1, 31, 32, 63, 64, K - 1, int(rng.integers(0, K))):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y = q.gemv(wfmt, Wp, Sp, dev(x), N, workspace=ws)
+        sync()
+        col = np.array([oracle.dequant_row(wfmt, W, S, n, K)[k] for n in range(N)], np.float32)
+        assert np.array_equal(host(y).view(np.uint32), col.view(np.uint32)), k
+
+
+@pytest.mark.parametrize("wfmt", ["q8", "q4"])
+def test_gemv_zero_scales_give_bias_plus_residual(wfmt):
+    rng = np.random.default_rng(4)
+    N, K = 257, 512
+    W, S = _rand_weights(rng, wfmt, N, K)
+    S = np.zeros_like(S)
+    b = rng.standard_normal(N).astype(np.float32)
+    r = rng.standard_normal(N).astype(np.float32)
+    Wp, Sp = _pack(wfmt, W, S)
+    y = q.gemv(wfmt, Wp, Sp, dev(rng.standard_normal(K).astype(np.float32)), N, bias=dev(b),
+               residual=dev(r), workspace=q.gemv_workspace(wfmt, N, K))
+    sync()
+    assert np.array_equal(host(y), (b + r).astype(np.float32))
+
+
+def test_gemv_workspace_is_reusable_and_deterministic():
+    rng = np.random.default_rng(5)
+    N, K = 3584, 18944
+    W, S = _rand_weights(rng, "q4", N, K)
+    Wp, Sp = _pack("q4", W, S)
+    ws = q.gemv_workspace("q4", N, K)
+    x = dev(rng.standard_normal(K).astype(np.float32))
+    ys = [host(q.gemv("q4", Wp, Sp, x, N, workspace=ws)) for _ in range(4)]
+    sync()
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+    assert not host(ws)[:65536].any()  # the tile arrival counters (first 64 KiB) are back at 0
+
+
+# ----------------------------------------------------------------------------- RMSNorm / RoPE / SwiGLU
+@pytest.mark.parametrize("dim", [64, 128])
+@pytest.mark.parametrize("pos", [0, 1, 4096, 32768])
+@pytest.mark.parametrize("with_gamma", [True, False])
+def test_rmsnorm_rope_parity(dim, pos, with_gamma):
+    rng = np.random.default_rng(dim + pos)
+    rows = 36
+    x = (3 * rng.standard_normal((rows, dim))).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(dim)).astype(np.float32) if with_gamma else None
+    p = torch.tensor([pos], dtype=torch.int32, device="cuda")
+    y = q.rmsnorm_rope(dev(x), None if g is None else dev(g), 1e-6, 1e6, p)
+    sync()
+    ref = oracle.rope(oracle.rmsnorm(x, g, 1e-6) if with_gamma else x, pos, 1e6)
+    assert rel_max_err(host(y), ref) <= 2e-6
+    yn = q.rmsnorm_rope(dev(x), None if g is None else dev(g), 1e-6, 0.0, None)  # no rotation
+    sync()
+    assert rel_max_err(host(yn), oracle.rmsnorm(x, g, 1e-6) if with_gamma else x) <= 2e-6
+
+
+@pytest.mark.parametrize("n", [1, 1000, 18944])
+def test_swiglu_parity(n):
+    rng = np.random.default_rng(n)
+    g = (4 * rng.standard_normal(n)).astype(np.float32)
+    u = (4 * rng.standard_normal(n)).astype(np.float32)
+    m = q.swiglu(dev(g), dev(u))
+    sync()
+    ref = oracle.swiglu(g, u)
+    assert np.allclose(host(m), ref, rtol=2e-6, atol=1e-7)
+
+
+def test_argmax_ties_and_nan():
+    v = np.zeros(152064, np.float32)
+    v[[70000, 9, 152063]] = 4.0
+    assert int(host(q.argmax(dev(v)))[0]) == 9
+    v[5] = np.nan
+    assert int(host(q.argmax(dev(v)))[0]) == 9
+    rng = np.random.default_rng(6)
+    for n in (1, 7, 1025, 151936):
+        w = rng.standard_normal(n).astype(np.float32)
+        assert int(host(q.argmax(dev(w)))[0]) == oracle.argmax(w)
+    assert int(host(q.argmax(dev(np.full(100, -np.inf, np.float32))))[0]) == 0
+
+
+# ----------------------------------------------------------------------------- attention
+def _pools(rng, P, Hkv, D, fmt):
+    k = rng.standard_normal((P, Hkv, 16, D)).astype(np.float32)
+    v = rng.standard_normal((P, Hkv, 16, D)).astype(np.float32)
+    if fmt == "bf16":
+        return bf16_bits(k), bf16_bits(v)
+    return k, v
+
+
+def _devpool(a, fmt):
+    return dev(a, torch.int16) if fmt == "bf16" else dev(a)
+
+
+ATTN_CASES = [
+    # (fmt, Hq, Hkv, D, T, splits)
+    ("f32", 14, 2, 64, 257, 8), ("f32", 14, 2, 64, 1, 1), ("bf16", 28, 4, 128, 4097, 64),
+    ("bf16", 28, 4, 128, 49, 16), ("bf16", 28, 4, 128, 17, 2), ("bf16", 28, 4, 128, 16, 4),
+    ("bf16", 28, 4, 128, 15, 1), ("bf16", 12, 2, 128, 1025, 128), ("bf16", 32, 8, 128, 4097, 32),
+    ("bf16", 8, 8, 128, 300, 7), ("bf16", 8, 1, 64, 33, 3), ("f32", 6, 3, 128, 100, 256),
+]
+
+
+@pytest.mark.parametrize("fmt,Hq,Hkv,D,T,splits", ATTN_CASES)
+def test_attention_parity(fmt, Hq, Hkv, D, T, splits):
+    rng = np.random.default_rng(T * 31 + Hq + splits)
+    P = -(-T // 16) + 2
+    pt = rng.permutation(P).astype(np.int32)
+    kp, vp = _pools(rng, P, Hkv, D, fmt)
+    qv = (2 * rng.standard_normal((Hq, D))).astype(np.float32)
+    kn = rng.standard_normal((Hkv, D)).astype(np.float32)
+    vn = rng.standard_normal((Hkv, D)).astype(np.float32)
+    pos = T - 1
+    dk, dv = _devpool(kp, fmt), _devpool(vp, fmt)
+    out = q.attn_decode_paged(dev(qv), dk, dv, fmt, dev(pt), torch.tensor([pos], dtype=torch.int32, device="cuda"),
+                              Hkv, k_new=dev(kn), v_new=dev(vn), num_splits=splits)
+    sync()
+    # oracle: store the new token the same way, then attend
+    ok, ov = kp.copy(), vp.copy()
+    oracle.kv_store(ok, fmt, pt, 16, pos, kn)
+    oracle.kv_store(ov, fmt, pt, 16, pos, vn)
+    ref = oracle.attention(qv, ok, ov, fmt, pt, T)
+    assert rel_max_err(host(out), ref) <= 2e-5
+    # the append wrote exactly the oracle's bytes, and nothing else changed
+    gk, gv = host(dk), host(dv)
+    if fmt == "bf16":
+        gk, gv = gk.view(np.uint16), gv.view(np.uint16)
+    assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+
+
+@pytest.mark.parametrize("fmt,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("splits", [1, 5, 64])
+def test_attention_gather_probe_bit_exact(fmt, D, splits):
+    """Every query head of KV group j sees one key t*_j aligned with it (score/ln2 ~ 2000/sqrt(D)
+    >> 150) and all other keys zero, so softmax is exactly one-hot and out_h = V[j][t*_j] bit for
+    bit: this pins the page-table gather, the in-page slot and the head-to-group map."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, T = 28, 4, 16 * 9 + 1
+    P = 12
+    pt = rng.permutation(P).astype(np.int32)
+    k = np.zeros((P, Hkv, 16, D), np.float32)
+    v = rng.standard_normal((P, Hkv, 16, D)).astype(np.float32)
+    targets = [0, 15, 16 * 5 + 7, T - 1]  # a page head, a page tail, a middle page, the last token
+    for j, t in enumerate(targets):
+        k[pt[t // 16], j, t % 16, 0] = 1.0
+    if fmt == "bf16":
+        k, v = bf16_bits(k), bf16_bits(v)
+    qv = np.zeros((Hq, D), np.float32)
+    qv[:, 0] = 2000.0
+    out = q.attn_decode_paged(dev(qv), _devpool(k, fmt), _devpool(v, fmt), fmt, dev(pt),
+                              torch.tensor([T - 1], dtype=torch.int32, device="cuda"), Hkv, num_splits=splits)
+    sync()
+    got = host(out)
+    G = Hq // Hkv
+    for h in range(Hq):
+        j = h // G
+        t = targets[j]
+        row = v[pt[t // 16], j, t % 16, :]
+        want = row.astype(np.float32) if fmt == "f32" else (row.astype(np.uint32) << 16).view(np.float32)
+        assert np.array_equal(got[h].view(np.uint32), want.view(np.uint32)), h
+
+
+def test_attention_split_count_independence():
+    rng = np.random.default_rng(12)
+    Hq, Hkv, D, T = 28, 4, 128, 1000
+    P = -(-T // 16)
+    pt = rng.permutation(P).astype(np.int32)
+    kp, vp = _pools(rng, P, Hkv, D, "bf16")
+    qv = (2 * rng.standard_normal((Hq, D))).astype(np.float32)
+    pos = torch.tensor([T - 1], dtype=torch.int32, device="cuda")
+    outs = [host(q.attn_decode_paged(dev(qv), dev(kp, torch.int16), dev(vp, torch.int16), "bf16", dev(pt), pos, Hkv,
+                                     num_splits=s)) for s in (1, 2, 16, 63, P)]
+    sync()
+    for o in outs[1:]:
+        assert rel_max_err(o, outs[0]) <= 1e-6

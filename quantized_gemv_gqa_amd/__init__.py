@@ -23,7 +23,7 @@ INCLUDE = os.path.join(_ROOT, "include")
 QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EHIP, QDEC_ESTATE = 0, -1, -2, -3, -4
 W_Q8, W_Q4 = 1, 2
 KV_F32, KV_BF16 = 1, 2
-STEP_EAGER, STEP_GRAPH = 0, 1
+STEP_EAGER, STEP_GRAPH, STEP_FUSED = 0, 1, 2
 PAGE = 16
 TILE = 64
 
@@ -132,6 +132,9 @@ def lib():
         L.qdec_decode_step.argtypes = [_P, _I, _P]; L.qdec_decode_step.restype = S
         L.qdec_step_kernel_count.argtypes = [_P]; L.qdec_step_kernel_count.restype = _I
         L.qdec_step_destroy.argtypes = [_P]; L.qdec_step_destroy.restype = None
+        L.qdec_step_fused_supported.argtypes = [_P]; L.qdec_step_fused_supported.restype = _I
+        L.qdec_step_read_error.argtypes = [_P, ctypes.POINTER(_I)]; L.qdec_step_read_error.restype = S
+        L.qdec_step_phase_times.argtypes = [_P, _P]; L.qdec_step_phase_times.restype = S
         _lib = L
     return _lib
 
@@ -141,7 +144,8 @@ EXPORTED = [
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
-    "qdec_step_kernel_count", "qdec_step_destroy",
+    "qdec_step_kernel_count", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
+    "qdec_step_phase_times",
 ]
 
 
@@ -397,6 +401,22 @@ class DecodeStep:
     @property
     def kernel_count(self) -> int:
         return lib().qdec_step_kernel_count(self.handle)
+
+    @property
+    def fused_supported(self) -> bool:
+        return bool(lib().qdec_step_fused_supported(self.handle))
+
+    def phase_times(self, ts=None):
+        """Record per-phase completion times of fused steps into `ts` (int64 device tensor of
+        3 + 5 * n_layers entries, 100 MHz ticks); None stops recording."""
+        _check(lib().qdec_step_phase_times(self.handle, _ptr(ts)), "qdec_step_phase_times")
+        self._ts = ts
+
+    def read_error(self) -> int:
+        """The step's device error flag (a bounded wait gave up), cleared after reading."""
+        f = _I()
+        _check(lib().qdec_step_read_error(self.handle, ctypes.byref(f)), "qdec_step_read_error")
+        return int(f.value)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
   const int j = blockIdx.x;
   const int s = blockIdx.y;
   const int T = *a.pos + 1;
-  const int P = (T + 15) >> 4;
+  const int P = min((T + 15) >> 4, a.n_pages);  // never index past the page table
   const int pps = (P + a.splits - 1) / a.splits;
   const int p0 = s * pps;
   const int p1 = min(P, p0 + pps);

@@ -39,6 +39,7 @@ struct GemvArgs {
   const float *bias;       // [N] or null
   const float *residual;   // [N] or null (may alias y)
   float *y;                // output
+  float *y2;               // optional second copy of y (plain stores; read after the kernel)
   float *ssq_out;          // if non-null: per-tile sum of y^2 over the tile's valid rows
   float *part;             // split-K partials [tiles][ks][64]
   unsigned *counters;      // [tiles] arrival counters, zero between launches
@@ -49,7 +50,19 @@ struct GemvArgs {
   float *cand;
   int32_t *token, *pos, *token_log, *step_count;
   int log_len;
+  // persistent step only: tiles finished are counted in *done; the argmax finisher zeroes
+  // done_reset[0 .. done_reset_n) for the next step
+  unsigned *done;
+  unsigned done_target;    // tiles of this phase: the finisher that completes it publishes progress
+  unsigned done_phase;     // this phase's index; completion publishes progress = done_phase + 1
+  unsigned *progress;      // replicated "phases completed" value (kProgressReplicas lines)
+  unsigned long long *phase_ts;  // optional: completion time of each phase (100 MHz clock)
+  unsigned *done_reset;
+  int done_reset_n;
 };
+constexpr int kProgressReplicas = 64;  // one 128-byte line each: spreads the polling
+constexpr size_t kCounterBytes = 64 * 1024;  // GEMV arrival-counter region of a workspace
+constexpr int kArgmaxCounter = (int)(kCounterBytes / sizeof(unsigned)) - 1;
 
 struct GemvPlan {
   int tiles, nch, ks, cps, units, blocks;

@@ -11,9 +11,11 @@
 // swiglu_down.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
+#include "qdec_fused.h"
 #include "qdec_internal.h"
 
 struct qdec_step {
@@ -31,6 +33,11 @@ struct qdec_step {
   hipGraphExec_t exec = nullptr;
   hipStream_t graph_stream = nullptr;
   int n_kernels = 0;
+  // persistent step
+  bool fused_ok = false;
+  int fused_blocks = 0;
+  qdec::FusedArgs fa{};
+  unsigned *err = nullptr;
 };
 
 namespace qdec {
@@ -39,7 +46,7 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, fused_layers, done, err, progress, rope, total;
 };
 
 Layout layout_of(const qdec_config &c) {
@@ -58,6 +65,11 @@ Layout layout_of(const qdec_config &c) {
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, c.inter));
   if (c.vocab > 0) g = std::max(g, gemv_workspace_bytes(c.wfmt, c.vocab, c.hidden, true));
   L.gemv_ws = off; off += align256(g);
+  L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
+  L.done = off; off += align256((size_t)(2 + 5 * c.n_layers) * sizeof(unsigned));
+  L.err = off; off += 256;
+  L.progress = off; off += (size_t)kProgressReplicas * 128;
+  L.rope = off; off += align256(64 * 2 * sizeof(double));
   L.total = off;
   return L;
 }
@@ -206,6 +218,89 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
   return QDEC_OK;
 }
 
+GemvArgs fused_gemv(const qdec_step *h, const float *x, float *y, int N, int K, const GemvPlan &p) {
+  GemvArgs a = gemv_args(h, nullptr, nullptr, x, y, N, K, p);
+  a.ks = p.ks;
+  a.cps = p.cps;
+  int gshift = 0;
+  if (h->cfg.wfmt == QDEC_W_Q4_G_ZP8)
+    while ((32 << gshift) < h->cfg.group) ++gshift;
+  a.group = gshift;  // the unit code reads the Q4 group as log2(group / 32)
+  return a;
+}
+
+qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
+  const qdec_config &c = h->cfg;
+  const qdec_state &s = h->state;
+  char *ws = reinterpret_cast<char *>(s.workspace);
+  std::vector<FusedLayer> tab(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const qdec_layer_weights &w = h->layers[l];
+    FusedLayer &f = tab[l];
+    f.w_qkv = reinterpret_cast<const uint8_t *>(w.w_qkv);
+    f.w_o = reinterpret_cast<const uint8_t *>(w.w_o);
+    f.w_gu = reinterpret_cast<const uint8_t *>(w.w_gu);
+    f.w_down = reinterpret_cast<const uint8_t *>(w.w_down);
+    f.s_qkv = w.s_qkv; f.s_o = w.s_o; f.s_gu = w.s_gu; f.s_down = w.s_down;
+    f.b_qkv = c.has_qkv_bias ? w.b_qkv : nullptr;
+    f.g_attn = w.g_attn; f.g_ffn = w.g_ffn;
+    f.g_q = c.has_qk_norm ? w.g_q : nullptr;
+    f.g_k = c.has_qk_norm ? w.g_k : nullptr;
+    f.k_pool = h->kpools[l]; f.v_pool = h->vpools[l];
+  }
+  hipError_t e = hipMemcpy(ws + L.fused_layers, tab.data(), tab.size() * sizeof(FusedLayer), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    set_error("qdec_step_create: copying the layer table: %s", hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+    set_error("qdec_step_create: cannot read the CU count");
+    return QDEC_EHIP;
+  }
+  const int per_cu = std::min(2, fused_blocks_per_cu(c.wfmt, G));
+  if (per_cu < 1) return QDEC_OK;  // not co-resident: the fused mode stays unavailable
+  h->fused_blocks = cus * per_cu;
+  FusedArgs &a = h->fa;
+  const int H = c.hidden, D = c.head_dim, qd = c.n_heads * D, nqkv = (c.n_heads + 2 * c.n_kv_heads) * D;
+  a.layers = reinterpret_cast<const FusedLayer *>(ws + L.fused_layers);
+  a.L = c.n_layers; a.H = H; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.V = c.vocab;
+  a.splits = c.num_splits; a.n_pages = c.n_pages;
+  a.eps = c.rms_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D)); a.rope_base = c.rope_base;
+  a.embed = h->model.embed; a.page_table = s.page_table; a.pos = s.pos; a.token = s.token;
+  a.hidden = s.hidden; a.trace = s.trace; a.qkv = h->qkv; a.attn = h->attn; a.ssq = h->ssq;
+  a.attn_cnt = reinterpret_cast<unsigned *>(h->attn_ws);
+  a.attn_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
+  a.rope_cs = reinterpret_cast<double *>(ws + L.rope);
+  a.done = reinterpret_cast<unsigned *>(ws + L.done);
+  a.progress = reinterpret_cast<unsigned *>(ws + L.progress);
+  a.err = h->err;
+  a.p_qkv = h->p_qkv; a.p_o = h->p_o; a.p_gu = h->p_gu; a.p_down = h->p_down; a.p_lm = h->p_lm;
+  a.g_qkv = fused_gemv(h, s.hidden, h->qkv, nqkv, H, h->p_qkv);
+  a.g_o = fused_gemv(h, h->attn, s.hidden, H, qd, h->p_o);
+  a.g_o.residual = s.hidden;
+  a.g_o.ssq_out = h->ssq;
+  a.g_gu = fused_gemv(h, s.hidden, h->mlp, 2 * c.inter, H, h->p_gu);
+  a.g_gu.epi = EPI_SWIGLU;
+  a.g_down = fused_gemv(h, h->mlp, s.hidden, H, c.inter, h->p_down);
+  a.g_down.residual = s.hidden;
+  a.g_down.ssq_out = h->ssq;
+  a.g_lm = fused_gemv(h, s.hidden, s.logits, c.vocab, H, h->p_lm);
+  a.g_lm.W = reinterpret_cast<const uint8_t *>(h->model.w_lm);
+  a.g_lm.S = h->model.s_lm;
+  a.g_lm.gamma = h->model.g_out;
+  a.g_lm.epi = EPI_ARGMAX;
+  a.g_lm.token = s.token; a.g_lm.pos = s.pos; a.g_lm.token_log = s.token_log;
+  a.g_lm.step_count = s.step_count; a.g_lm.log_len = s.log_len;
+  a.g_lm.done_reset = a.done; a.g_lm.done_reset_n = 2 + 5 * c.n_layers;
+  // every wave needs a unit of the last phase (its finisher clears the phase counters once all
+  // other waves are past their waits)
+  if (h->p_lm.tiles * h->p_lm.ks < h->fused_blocks * 4) return QDEC_OK;
+  h->fused_ok = true;
+  return QDEC_OK;
+}
+
 }  // namespace
 }  // namespace qdec
 
@@ -271,6 +366,15 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   h->p_gu = gemv_plan(cfg->wfmt, 2 * cfg->inter, cfg->hidden, true);
   h->p_down = gemv_plan(cfg->wfmt, cfg->hidden, cfg->inter, true);
   if (lm) h->p_lm = gemv_plan(cfg->wfmt, cfg->vocab, cfg->hidden, true);
+  h->err = reinterpret_cast<unsigned *>(ws + L.err);
+  const int G = cfg->n_heads / cfg->n_kv_heads;
+  if (lm && m->embed && fused_supported(cfg->wfmt, G, cfg->head_dim, cfg->kv_fmt)) {
+    qdec_status r2 = setup_fused(h, L, G);
+    if (r2 != QDEC_OK) {
+      delete h;
+      return r2;
+    }
+  }
   *out = h;
   return QDEC_OK;
 }
@@ -279,6 +383,17 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
   QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_decode_step: null handle");
   hipStream_t st = (hipStream_t)stream;
   if (mode == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels);
+  if (mode == QDEC_STEP_FUSED) {
+    QDEC_REQUIRE(h->fused_ok, QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step is not available for this model");
+    const int G = h->cfg.n_heads / h->cfg.n_kv_heads;
+    hipError_t e = launch_fused(h->fa, h->cfg.wfmt, G, h->fused_blocks, st);
+    if (e != hipSuccess) {
+      set_error("qdec_decode_step (fused): %s", hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    h->n_kernels = 1;
+    return QDEC_OK;
+  }
   QDEC_REQUIRE(mode == QDEC_STEP_GRAPH, QDEC_EINVAL, "qdec_decode_step: unknown mode %d", mode);
   if (!h->exec) {
     QDEC_REQUIRE(st != nullptr, QDEC_ESTATE,
@@ -319,6 +434,30 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
 }
 
 int qdec_step_kernel_count(const qdec_step *h) { return h ? h->n_kernels : 0; }
+
+int qdec_step_fused_supported(const qdec_step *h) { return h && h->fused_ok ? 1 : 0; }
+
+qdec_status qdec_step_phase_times(qdec_step *h, uint64_t *ts) {
+  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_phase_times: null handle");
+  h->fa.phase_ts = reinterpret_cast<unsigned long long *>(ts);
+  return QDEC_OK;
+}
+
+qdec_status qdec_step_read_error(qdec_step *h, int *flag) {
+  QDEC_REQUIRE(h && flag, QDEC_EINVAL, "qdec_step_read_error: null argument");
+  unsigned v = 0;
+  hipError_t e = hipMemcpy(&v, h->err, sizeof(v), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && v) {
+    const unsigned z = 0;
+    e = hipMemcpy(h->err, &z, sizeof(z), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    set_error("qdec_step_read_error: %s", hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  *flag = (int)v;
+  return QDEC_OK;
+}
 
 void qdec_step_destroy(qdec_step *h) {
   if (!h) return;

@@ -46,8 +46,63 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, fused_layers, done, err, progress, rope, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, fused_layers, err, total;
+  // persistent step
+  size_t hB, xa, xb, ssqA, ssqB, sync, gu_flag, tile_cnt, cand, sub_cand, part[5];
+  size_t part_bytes[5];
+  int tiles[5], nch[5];
 };
+
+// Largest wave count the stream-K partitions are sized for (512 CUs x 8 waves); a larger grid
+// leaves the extra waves idle in the GEMV phases.
+constexpr int kMaxFusedWaves = 4096;
+
+// Sync region of the persistent step, in 128-byte lines
+struct SyncLines {
+  int epoch, qkv_done, attn_all, o_done, down_done, progress, lm_sub, lm_top, total;
+};
+SyncLines sync_lines(const qdec_config &c) {
+  SyncLines s{};
+  int o = 0;
+  s.epoch = o; o += 1;
+  s.qkv_done = o; o += c.n_layers * c.n_kv_heads;
+  s.attn_all = o; o += c.n_layers;
+  s.o_done = o; o += c.n_layers;
+  s.down_done = o; o += c.n_layers;
+  s.progress = o; o += kProgressReplicas;
+  s.lm_sub = o; o += 64;
+  s.lm_top = o; o += 1;
+  s.total = o;
+  return s;
+}
+
+int sk_wave_h(const SkPhase &p, long r) {
+  const long big = (long)p.rem * (p.q + 1);
+  return (int)(r < big ? r / (p.q + 1) : p.rem + (r - big) / p.q);
+}
+
+// Stream-K partition of a GEMV of `tiles` x `nch` runs over at most `waves` waves, with at most
+// kMaxSlots contributors per tile (fewer waves take part if needed).
+SkPhase plan_sk(int tiles, int nch, int waves) {
+  SkPhase p{};
+  p.tiles = tiles;
+  p.nch = nch;
+  const long R = (long)tiles * nch;
+  int nw = (int)std::min<long>(std::min(waves, kMaxFusedWaves), R);
+  for (;;) {
+    p.nw = nw;
+    p.q = (int)(R / nw);
+    p.rem = (int)(R % nw);
+    int mx = 1;
+    for (int t = 0; t < tiles; ++t)
+      mx = std::max(mx, sk_wave_h(p, (long)t * nch + nch - 1) - sk_wave_h(p, (long)t * nch) + 1);
+    if (mx <= kMaxSlots || nw == 1) {
+      p.slots = mx;
+      return p;
+    }
+    nw = std::max(1, (int)((long)nw * (kMaxSlots - 1) / mx));
+  }
+}
 
 Layout layout_of(const qdec_config &c) {
   Layout L{};
@@ -65,11 +120,35 @@ Layout layout_of(const qdec_config &c) {
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, c.inter));
   if (c.vocab > 0) g = std::max(g, gemv_workspace_bytes(c.wfmt, c.vocab, c.hidden, true));
   L.gemv_ws = off; off += align256(g);
-  L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
-  L.done = off; off += align256((size_t)(2 + 5 * c.n_layers) * sizeof(unsigned));
   L.err = off; off += 256;
-  L.progress = off; off += (size_t)kProgressReplicas * 128;
-  L.rope = off; off += align256(64 * 2 * sizeof(double));
+  // persistent step: activations, sync lines, per-phase split state
+  L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
+  L.hB = off; off += align256((size_t)c.hidden * 4);
+  L.xa = off; off += align256((size_t)c.hidden * 4);
+  L.xb = off; off += align256((size_t)c.hidden * 4);
+  L.ssqA = off; off += 256;
+  L.ssqB = off; off += 256;
+  L.sync = off; off += (size_t)sync_lines(c).total * 128;
+  const int ck = (c.wfmt == QDEC_W_Q4_G_ZP8) ? 32 : 16;
+  const int Ns[5] = {nqkv, c.hidden, 2 * c.inter, c.hidden, std::max(c.vocab, 1)};
+  const int Ks[5] = {c.hidden, qd, c.hidden, c.inter, c.hidden};
+  size_t ntiles = 0;
+  for (int i = 0; i < 5; ++i) {
+    L.tiles[i] = (Ns[i] + kTile - 1) / kTile;
+    L.nch[i] = Ks[i] / ck;
+    ntiles += (size_t)L.tiles[i];
+    // sized for the largest grid; a smaller one has fewer contributors per tile
+    const SkPhase p = plan_sk(L.tiles[i], std::max(L.nch[i], 1), kMaxFusedWaves);
+    L.part_bytes[i] = p.slots > 1 ? (size_t)L.tiles[i] * p.slots * kTile * 4 : 0;
+  }
+  L.gu_flag = off; off += align256((size_t)c.n_layers * L.tiles[2] * 4);
+  L.tile_cnt = off; off += align256(ntiles * 4);
+  L.cand = off; off += align256((size_t)L.tiles[4] * 8);
+  L.sub_cand = off; off += align256(64 * 8);
+  for (int i = 0; i < 5; ++i) {
+    L.part[i] = off;
+    off += align256(L.part_bytes[i]);
+  }
   L.total = off;
   return L;
 }
@@ -218,17 +297,6 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
   return QDEC_OK;
 }
 
-GemvArgs fused_gemv(const qdec_step *h, const float *x, float *y, int N, int K, const GemvPlan &p) {
-  GemvArgs a = gemv_args(h, nullptr, nullptr, x, y, N, K, p);
-  a.ks = p.ks;
-  a.cps = p.cps;
-  int gshift = 0;
-  if (h->cfg.wfmt == QDEC_W_Q4_G_ZP8)
-    while ((32 << gshift) < h->cfg.group) ++gshift;
-  a.group = gshift;  // the unit code reads the Q4 group as log2(group / 32)
-  return a;
-}
-
 qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
   const qdec_config &c = h->cfg;
   const qdec_state &s = h->state;
@@ -262,41 +330,57 @@ qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
   const int per_cu = std::min(2, fused_blocks_per_cu(c.wfmt, G));
   if (per_cu < 1) return QDEC_OK;  // not co-resident: the fused mode stays unavailable
   h->fused_blocks = cus * per_cu;
+  const int waves = h->fused_blocks * 4;
   FusedArgs &a = h->fa;
-  const int H = c.hidden, D = c.head_dim, qd = c.n_heads * D, nqkv = (c.n_heads + 2 * c.n_kv_heads) * D;
+  const int D = c.head_dim;
   a.layers = reinterpret_cast<const FusedLayer *>(ws + L.fused_layers);
-  a.L = c.n_layers; a.H = H; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.V = c.vocab;
+  a.L = c.n_layers; a.H = c.hidden; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.V = c.vocab; a.I = c.inter;
   a.splits = c.num_splits; a.n_pages = c.n_pages;
+  int gshift = 0;
+  if (c.wfmt == QDEC_W_Q4_G_ZP8)
+    while ((32 << gshift) < c.group) ++gshift;
+  a.gshift = gshift;
   a.eps = c.rms_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D)); a.rope_base = c.rope_base;
-  a.embed = h->model.embed; a.page_table = s.page_table; a.pos = s.pos; a.token = s.token;
-  a.hidden = s.hidden; a.trace = s.trace; a.qkv = h->qkv; a.attn = h->attn; a.ssq = h->ssq;
+  a.embed = h->model.embed;
+  a.w_lm = reinterpret_cast<const uint8_t *>(h->model.w_lm);
+  a.s_lm = h->model.s_lm;
+  a.g_out = h->model.g_out;
+  a.page_table = s.page_table; a.pos = s.pos; a.token = s.token;
+  a.token_log = s.token_log; a.step_count = s.step_count; a.log_len = s.log_len;
+  a.hA = s.hidden;
+  a.hB = reinterpret_cast<float *>(ws + L.hB);
+  a.xa = reinterpret_cast<float *>(ws + L.xa);
+  a.xb = reinterpret_cast<float *>(ws + L.xb);
+  a.ssqA = reinterpret_cast<float *>(ws + L.ssqA);
+  a.ssqB = reinterpret_cast<float *>(ws + L.ssqB);
+  a.trace = s.trace; a.logits = s.logits;
+  a.qkv = h->qkv; a.attn = h->attn; a.mlp = h->mlp;
   a.attn_cnt = reinterpret_cast<unsigned *>(h->attn_ws);
   a.attn_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
-  a.rope_cs = reinterpret_cast<double *>(ws + L.rope);
-  a.done = reinterpret_cast<unsigned *>(ws + L.done);
-  a.progress = reinterpret_cast<unsigned *>(ws + L.progress);
+  const SyncLines sl = sync_lines(c);
+  unsigned *sync = reinterpret_cast<unsigned *>(ws + L.sync);
+  a.epoch = sync + sl.epoch * 32;
+  a.qkv_done = sync + sl.qkv_done * 32;
+  a.attn_all = sync + sl.attn_all * 32;
+  a.o_done = sync + sl.o_done * 32;
+  a.down_done = sync + sl.down_done * 32;
+  a.progress = sync + sl.progress * 32;
+  a.lm_sub = sync + sl.lm_sub * 32;
+  a.lm_top = sync + sl.lm_top * 32;
+  a.gu_flag = reinterpret_cast<unsigned *>(ws + L.gu_flag);
+  a.cand = reinterpret_cast<float *>(ws + L.cand);
+  a.sub_cand = reinterpret_cast<float *>(ws + L.sub_cand);
   a.err = h->err;
-  a.p_qkv = h->p_qkv; a.p_o = h->p_o; a.p_gu = h->p_gu; a.p_down = h->p_down; a.p_lm = h->p_lm;
-  a.g_qkv = fused_gemv(h, s.hidden, h->qkv, nqkv, H, h->p_qkv);
-  a.g_o = fused_gemv(h, h->attn, s.hidden, H, qd, h->p_o);
-  a.g_o.residual = s.hidden;
-  a.g_o.ssq_out = h->ssq;
-  a.g_gu = fused_gemv(h, s.hidden, h->mlp, 2 * c.inter, H, h->p_gu);
-  a.g_gu.epi = EPI_SWIGLU;
-  a.g_down = fused_gemv(h, h->mlp, s.hidden, H, c.inter, h->p_down);
-  a.g_down.residual = s.hidden;
-  a.g_down.ssq_out = h->ssq;
-  a.g_lm = fused_gemv(h, s.hidden, s.logits, c.vocab, H, h->p_lm);
-  a.g_lm.W = reinterpret_cast<const uint8_t *>(h->model.w_lm);
-  a.g_lm.S = h->model.s_lm;
-  a.g_lm.gamma = h->model.g_out;
-  a.g_lm.epi = EPI_ARGMAX;
-  a.g_lm.token = s.token; a.g_lm.pos = s.pos; a.g_lm.token_log = s.token_log;
-  a.g_lm.step_count = s.step_count; a.g_lm.log_len = s.log_len;
-  a.g_lm.done_reset = a.done; a.g_lm.done_reset_n = 2 + 5 * c.n_layers;
-  // every wave needs a unit of the last phase (its finisher clears the phase counters once all
-  // other waves are past their waits)
-  if (h->p_lm.tiles * h->p_lm.ks < h->fused_blocks * 4) return QDEC_OK;
+  SkPhase *ph[5] = {&a.p_qkv, &a.p_o, &a.p_gu, &a.p_down, &a.p_lm};
+  unsigned *tc = reinterpret_cast<unsigned *>(ws + L.tile_cnt);
+  for (int i = 0; i < 5; ++i) {
+    SkPhase p = plan_sk(L.tiles[i], std::max(L.nch[i], 1), waves);
+    if (p.slots > 1 && (size_t)L.tiles[i] * p.slots * kTile * 4 > L.part_bytes[i]) return QDEC_OK;
+    p.part = reinterpret_cast<float *>(ws + L.part[i]);
+    p.tile_cnt = tc;
+    tc += L.tiles[i];
+    *ph[i] = p;
+  }
   h->fused_ok = true;
   return QDEC_OK;
 }
@@ -368,7 +452,8 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   if (lm) h->p_lm = gemv_plan(cfg->wfmt, cfg->vocab, cfg->hidden, true);
   h->err = reinterpret_cast<unsigned *>(ws + L.err);
   const int G = cfg->n_heads / cfg->n_kv_heads;
-  if (lm && m->embed && fused_supported(cfg->wfmt, G, cfg->head_dim, cfg->kv_fmt)) {
+  if (lm && m->embed && cfg->hidden % 64 == 0 && cfg->hidden <= 4096 &&
+      fused_supported(cfg->wfmt, G, cfg->head_dim, cfg->kv_fmt)) {
     qdec_status r2 = setup_fused(h, L, G);
     if (r2 != QDEC_OK) {
       delete h;

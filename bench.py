@@ -7,6 +7,7 @@ its launch duration measured with HIP events on its own stream; `cpu_baseline` t
 oracle on a bounded sample (whole decode steps) of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -19,6 +20,31 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+# HBM traffic of the roofline kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs, scaled by
+# the same counters on a plain copy of known size; valid only for the kernel sources it was taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemv_q4_traffic.json")
+KERNEL_SOURCES = ("quantized_gemv_gqa_amd/csrc/gemv.hip", "quantized_gemv_gqa_amd/csrc/qdec_device.h",
+                  "quantized_gemv_gqa_amd/csrc/qdec_internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per launch from the committed counter record, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def step_bytes(wl, T: int) -> int:
@@ -63,6 +89,8 @@ def main():
     ap.add_argument("--workload", default="qwen2.5-7b-q4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=512,
+                    help="size of one plain device copy run after the timed region (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the decode step on a single MI355X; "
@@ -121,13 +149,24 @@ def main():
 
         for i in range(5):
             gu(i)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
-            a.record(stream)
+        # back-to-back launches between one event pair: the per-launch average then matches the
+        # kernel-trace duration (which runs from one dispatch's start to its end)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(reps):
             gu(i)
-            b.record(stream)
+        ev1.record(stream)
         torch.cuda.synchronize()
-    us_gu = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    us_gu = ev0.elapsed_time(ev1) * 1e3 / reps
+    # one plain copy of known size (read + write of calib-copy-mib MiB), the reference the HBM
+    # byte counters are scaled by when this command runs under rocprofv3 --pmc
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     gu_bytes = dominant_kernel_bytes(wl)
     gu_gbps = gu_bytes / (us_gu * 1e-6) / 1e9
 
@@ -155,7 +194,8 @@ def main():
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "kernel": "gate/up GEMV (INT4, %dx%d)" % (2 * wl.inter, wl.hidden),
                      "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gu_gbps / HBM_PEAK_GBPS,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": us_gu, "traffic": None},
+                     "bytes_per_launch": gu_bytes, "us_per_launch": us_gu, "traffic": measured_traffic(),
+                     "kernel_source_hash": kernel_source_hash()},
         "tokens_head": [int(t) for t in tokens[:8]],
     }
 

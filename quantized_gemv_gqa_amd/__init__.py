@@ -135,6 +135,8 @@ def lib():
         L.qdec_step_fused_supported.argtypes = [_P]; L.qdec_step_fused_supported.restype = _I
         L.qdec_step_read_error.argtypes = [_P, ctypes.POINTER(_I)]; L.qdec_step_read_error.restype = S
         L.qdec_step_phase_times.argtypes = [_P, _P]; L.qdec_step_phase_times.restype = S
+        L.qdec_step_wave_times.argtypes = [_P, _P]; L.qdec_step_wave_times.restype = S
+        L.qdec_step_fused_waves.argtypes = [_P]; L.qdec_step_fused_waves.restype = _I
         _lib = L
     return _lib
 
@@ -145,7 +147,7 @@ EXPORTED = [
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
     "qdec_step_kernel_count", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
-    "qdec_step_phase_times",
+    "qdec_step_phase_times", "qdec_step_wave_times", "qdec_step_fused_waves",
 ]
 
 
@@ -322,11 +324,16 @@ def upload_kv(kv: dict, kv_fmt: str, device="cuda") -> dict:
             "v": [_to_dev(a, device, dt) for a in kv["v"]]}
 
 
-def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 2) -> int:
-    """Attention split count: about `pages_per_wave` KV pages for each of a split's 4 waves, at
-    most 256 splits (the merge folds them in one workgroup)."""
+def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 1) -> int:
+    """Attention split count: about `pages_per_wave` KV pages for each of a split's 4 waves (pages
+    are dealt round-robin over all waves of a KV head), at most 256 splits (the merge folds them in
+    one workgroup).  Above 32 splits a small excess over a multiple of 32 is dropped: the merge
+    reads 32 splits' partials per pass, so 65 splits cost a third pass for one split's worth of
+    pages."""
     pages = max(1, -(-(ctx + 1) // PAGE))
     s = -(-pages // (4 * pages_per_wave))
+    if s > 32 and s % 32 <= (s // 32) * 8:
+        s -= s % 32
     return int(max(1, min(s, 256)))
 
 
@@ -408,9 +415,20 @@ class DecodeStep:
 
     def phase_times(self, ts=None):
         """Record per-phase completion times of fused steps into `ts` (int64 device tensor of
-        3 + 5 * n_layers entries, 100 MHz ticks); None stops recording."""
+        2 + 5 * n_layers entries, zeroed by the caller before each step, 100 MHz ticks); None stops
+        recording."""
         _check(lib().qdec_step_phase_times(self.handle, _ptr(ts)), "qdec_step_phase_times")
         self._ts = ts
+
+    @property
+    def fused_waves(self) -> int:
+        return lib().qdec_step_fused_waves(self.handle)
+
+    def wave_times(self, ts=None):
+        """Record per-wave marks of fused steps into `ts` (int32 device tensor of
+        (5 * n_layers + 1) * fused_waves * 4 entries); None stops recording."""
+        _check(lib().qdec_step_wave_times(self.handle, _ptr(ts)), "qdec_step_wave_times")
+        self._wts = ts
 
     def read_error(self) -> int:
         """The step's device error flag (a bounded wait gave up), cleared after reading."""

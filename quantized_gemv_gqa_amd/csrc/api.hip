@@ -200,8 +200,8 @@ qdec_status qdec_attn_decode_paged(const float *q, const float *k_new, const flo
                "%s: head_dim must be 64 or 128 (got %d)", nm, head_dim);
   QDEC_REQUIRE(num_splits >= 1 && num_splits <= kMaxMergeSplits, QDEC_EINVAL, "%s: num_splits in [1, %d]", nm,
                kMaxMergeSplits);
-  QDEC_REQUIRE(n_kv_heads <= (int)(kAttnCounterBytes / 4), QDEC_EUNSUPPORTED, "%s: at most %d KV heads", nm,
-               (int)(kAttnCounterBytes / 4));
+  QDEC_REQUIRE(n_kv_heads <= (int)(kAttnCounterBytes / 128), QDEC_EUNSUPPORTED, "%s: at most %d KV heads", nm,
+               (int)(kAttnCounterBytes / 128));
   QDEC_REQUIRE(n_pages >= 1, QDEC_EINVAL, "%s: n_pages must be >= 1", nm);
   QDEC_REQUIRE(std::isfinite(sm_scale), QDEC_EINVAL, "%s: sm_scale must be finite", nm);
   QDEC_REQUIRE(workspace_bytes >= attn_workspace_bytes(n_heads, head_dim, num_splits), QDEC_EINVAL,

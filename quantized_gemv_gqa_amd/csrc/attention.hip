@@ -20,91 +20,254 @@
 // "Challenge 1").
 #include <hip/hip_runtime.h>
 
-#include "qdec_internal.h"
+#include <cmath>
+
+#include "qdec_device.h"
 
 namespace qdec {
 
 namespace {
 
-constexpr float kNegBig = -1e30f;  // finite "minus infinity" for running maxima
-constexpr int kAuxSc1 = 16;        // sc1: device-coherent load (bypasses non-coherent L2 copies)
+using namespace dev;
 
-__device__ __forceinline__ float bf16_to_float(uint16_t b) {
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
-
-__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
-  uint32_t b = __builtin_bit_cast(uint32_t, f);
-  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
-
+// One lane's piece of a token row: DPL = D / 16 values, kept packed as W dwords until used.
 template <int D, int KVF>
-struct RowLoad {
-  static constexpr int DPL = D / 16;  // elements per lane
-  // load DPL elements of a token row starting at element e0
-  __device__ __forceinline__ static void load(const void *pool, size_t e0, float (&r)[DPL]) {
-    if constexpr (KVF == QDEC_KV_BF16) {
-      const uint16_t *p = reinterpret_cast<const uint16_t *>(pool) + e0;
-      if constexpr (DPL == 8) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(p);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          r[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-          r[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
-        }
-      } else {
-        static_assert(DPL == 4, "head_dim 64 or 128");
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
-        const uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          r[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-          r[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
-        }
-      }
+struct Row {
+  static constexpr int DPL = D / 16;
+  static constexpr int EB = KVF == QDEC_KV_BF16 ? 2 : 4;  // bytes per element
+  static constexpr int W = DPL * EB / 4;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (W == 2) {
+      // (a 64-bit load is read as one 64-bit integer: a two-lane vector view of it compiles to a
+      // single dword load)
+      const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      w[0] = (uint32_t)v; w[1] = (uint32_t)(v >> 32);
     } else {
-      const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(pool) + e0);
 #pragma unroll
-      for (int i = 0; i < DPL / 4; ++i) {
-        const float4 v = p[i];
-        r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
+      for (int c = 0; c < W / 4; ++c) {
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * c, 0, 0));
+        w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
       }
     }
   }
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (KVF == QDEC_KV_BF16)
+      return __builtin_bit_cast(float, (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    else
+      return __builtin_bit_cast(float, w[e]);
+  }
+  // the stored form of fp32 values: bf16 round-to-nearest-even, or the fp32 bits
+  __device__ __forceinline__ void set(const float (&v)[DPL]) {
+    if constexpr (KVF == QDEC_KV_BF16) {
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        w[i] = (uint32_t)float_to_bf16_rne(v[2 * i]) | ((uint32_t)float_to_bf16_rne(v[2 * i + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) w[i] = __builtin_bit_cast(uint32_t, v[i]);
+    }
+  }
+  __device__ __forceinline__ void store(void *pool, size_t elem) const {
+    uint32_t *d = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(pool) + elem * EB);
+#pragma unroll
+    for (int i = 0; i < W; ++i) d[i] = w[i];
+  }
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = 0u;
+  }
 };
 
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
-  return v;
+// Online-softmax update of one wave with one 16-token page: token slot sub*4 + slot of the page
+// sits in this lane's kp[sub] / vp[sub]; tokens at or past T are masked.
+template <int D, int G, int KVF>
+__device__ __forceinline__ void attend_page(Row<D, KVF> (&kp)[4], Row<D, KVF> (&vp)[4], int p, int T, int slot,
+                                            const float (&q)[G][D / 16], float (&m)[G], float (&l)[G],
+                                            float (&o)[G][D / 16]) {
+  constexpr int DPL = D / 16;
+  float sc[4][G];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const bool valid = p * 16 + sub * 4 + slot < T;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) d = fmaf(q[h][e], kp[sub].get(e), d);
+      d = sum16(d);
+      sc[sub][h] = valid ? d : -INFINITY;
+    }
+    // slots past the newest token may hold stale bits (even NaN): zero them, never multiply
+    // them by a zero weight
+    if (!valid) vp[sub].clear();
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
+    const float alpha = exp2f(m[h] - mx);
+    m[h] = mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      sc[sub][h] = exp2f(sc[sub][h] - mx);
+      ls += sc[sub][h];
+    }
+    l[h] = fmaf(l[h], alpha, ls);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+  }
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float vv = vp[sub].get(e);
+#pragma unroll
+      for (int h = 0; h < G; ++h) o[h][e] = fmaf(sc[sub][h], vv, o[h][e]);
+    }
 }
 
-template <int D, int G, int KVF>
+// Optional RMSNorm over the head (DPL dims per lane, 16 lanes) and RoPE rotation of one head
+// vector: `own` are the lane's dims, `mate` the dims D/2 away; cs holds the fp64 (cos, sin) of
+// the lane's DPL rotation pairs.
+template <int D>
+__device__ __forceinline__ void norm_rope(float (&own)[D / 16], float (&mate)[D / 16], int part, const float *gamma,
+                                          float eps, const double *cs) {
+  constexpr int DPL = D / 16, HALF = D / 2;
+  const int d0 = part * DPL;
+  const bool lo = d0 < HALF;
+  if (gamma) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ss = fmaf(own[e], own[e], ss);
+    ss = sum16(ss);
+    const float r = rsqrtf(ss / (float)D + eps);
+    const int dm = lo ? d0 + HALF : d0 - HALF;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      own[e] = gamma[d0 + e] * (own[e] * r);
+      mate[e] = gamma[dm + e] * (mate[e] * r);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const double c = cs[2 * e], sn = cs[2 * e + 1];
+    const double x = own[e], y = mate[e];
+    // low half: x' = x c - y s (y = x[i + D/2]); high half: x' = x c + y s (y = x[i - D/2])
+    own[e] = (float)(lo ? (x * c - y * sn) : (x * c + y * sn));
+  }
+}
+
+constexpr int kMergeChunk = 32;  // splits whose partial outputs one merge pass loads at once
+
+// ROPE: q, k and v come raw from the fused qkv vector; the kernel applies the optional q/k
+// RMSNorm and RoPE itself, appends the new token's k and v (the split owning the last page), and
+// takes the newest key and value from registers.  Otherwise q is given rotated and the new
+// token's k and v were appended before the launch.
+template <int D, int G, int KVF, bool ROPE>
 __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
   constexpr int DPL = D / 16;
+  constexpr int EB = Row<D, KVF>::EB;
   __shared__ float sm_m[4][G], sm_l[4][G], sm_o[4][G][D];
+  __shared__ float sw[kMaxMergeSplits][G], sl[kMaxMergeSplits][G];
+  __shared__ float sM[G], sL[G];
+  __shared__ float sq[ROPE ? (G + 2) * D : 1];
+  __shared__ unsigned last;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane >> 4;
   const int part = lane & 15;
   const int j = blockIdx.x;
   const int s = blockIdx.y;
-  const int T = *a.pos + 1;
+  const int pos = *a.pos;
+  const int T = pos + 1;
   const int P = min((T + 15) >> 4, a.n_pages);  // never index past the page table
-  const int pps = (P + a.splits - 1) / a.splits;
-  const int p0 = s * pps;
-  const int p1 = min(P, p0 + pps);
+  // pages are dealt round-robin over all 4 * splits waves of the KV head: wave gw = 4 s + wave
+  // takes pages gw, gw + nwt, gw + 2 nwt, ...
+  const int nwt = 4 * a.splits;
+  const int gw = 4 * s + wave;
+  const int last_page = ((T + 15) >> 4) - 1;
+  const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
+  const __amdgpu_buffer_rsrc_t kr = rsrc(a.k_pool, pool_bytes), vr = rsrc(a.v_pool, pool_bytes);
+  const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
+
+  // the wave's first two pages are requested before anything else
+  Row<D, KVF> kp[2][4], vp[2][4];
+  bool have[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = gw + nwt * i;
+    have[i] = false;
+    if (p < P) {
+      const int phys = a.page_table[p];
+      if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
+        have[i] = true;
+        const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
+          kp[i][sub].load(kr, off);
+          vp[i][sub].load(vr, off);
+        }
+      }
+    }
+  }
 
   float q[G][DPL];
+  Row<D, KVF> knew, vnew;
+  if constexpr (ROPE) {
+    // stage this KV head's q heads and its new k, v (one pass), then norm + rotate per lane
+    for (int i = threadIdx.x; i < (G + 2) * D / 4; i += 256) {
+      const int h = (i * 4) / D, d = i * 4 - h * D;
+      const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
+      *reinterpret_cast<f32x4 *>(&sq[h * D + d]) = *reinterpret_cast<const f32x4 *>(a.qkv + (size_t)row * D + d);
+    }
+    double cs[2 * DPL];
+    {
+      const int i0 = (part * DPL) % (D / 2);
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+      for (int e = 0; e < 2 * DPL; ++e) cs[e] = a.rope_cs[2 * i0 + e];
+    }
+    __syncthreads();
+    const int dmate = part * DPL < D / 2 ? part * DPL + D / 2 : part * DPL - D / 2;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) q[h][e] = a.q[(size_t)(j * G + h) * D + part * DPL + e] * a.scale_log2;
+    for (int h = 0; h < G; ++h) {
+      float own[DPL], mate[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        own[e] = sq[h * D + part * DPL + e];
+        mate[e] = sq[h * D + dmate + e];
+      }
+      norm_rope<D>(own, mate, part, a.g_q, a.eps, cs);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) q[h][e] = own[e] * a.scale_log2;
+    }
+    float own[DPL], mate[DPL], vv[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      own[e] = sq[G * D + part * DPL + e];
+      mate[e] = sq[G * D + dmate + e];
+      vv[e] = sq[(G + 1) * D + part * DPL + e];
+    }
+    norm_rope<D>(own, mate, part, a.g_k, a.eps, cs);
+    knew.set(own);
+    vnew.set(vv);
+    // split 0 appends them for later steps (every split uses the register copy for this token)
+    if (s == 0 && wave == 0 && slot == 0 && last_page < a.n_pages) {
+      const int phys = a.page_table[last_page];
+      if (phys >= 0 && phys < a.n_pages) {
+        const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (pos & 15)) * D + part * DPL;
+        knew.store(a.k_pool, e0);
+        vnew.store(a.v_pool, e0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) q[h][e] = a.q[(size_t)(j * G + h) * D + part * DPL + e] * a.scale_log2;
+  }
+  const int new_sub = (pos & 15) >> 2, new_slot = pos & 3;
 
   float m[G], l[G], o[G][DPL];
 #pragma unroll
@@ -114,58 +277,30 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
-
-  const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
-  for (int p = p0 + wave; p < p1; p += 4) {
+  auto page = [&](Row<D, KVF> (&kq)[4], Row<D, KVF> (&vq)[4], int p) {
+    if (ROPE && p == last_page) {  // the newest token's row comes from registers
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+        if (sub == new_sub && slot == new_slot) {
+          kq[sub] = knew;
+          vq[sub] = vnew;
+        }
+    }
+    attend_page<D, G, KVF>(kq, vq, p, T, slot, q, m, l, o);
+  };
+  if (have[0]) page(kp[0], vp[0], gw);
+  if (have[1]) page(kp[1], vp[1], gw + nwt);
+  for (int p = gw + 2 * nwt; p < P; p += nwt) {
     const int phys = a.page_table[p];
-    if (phys < 0 || phys >= a.n_pages) continue;  // documented precondition; never read outside
+    if (phys < 0 || phys >= a.n_pages) continue;
     const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-    // all K and V rows this lane needs from the page, issued before any is used
-    float kr[4][DPL], vr[4][DPL];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const size_t e = base + (size_t)(sub * 4 + slot) * D + part * DPL;
-      RowLoad<D, KVF>::load(a.k_pool, e, kr[sub]);
-      RowLoad<D, KVF>::load(a.v_pool, e, vr[sub]);
+      const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
+      kp[0][sub].load(kr, off);
+      vp[0][sub].load(vr, off);
     }
-    float sc[4][G];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const bool valid = p * 16 + sub * 4 + slot < T;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) d = fmaf(q[h][e], kr[sub][e], d);
-        d = sum16(d);
-        sc[sub][h] = valid ? d : -INFINITY;
-      }
-      // slots past the newest token may hold stale bits (even NaN): select them away, never
-      // multiply them by a zero weight
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) vr[sub][e] = valid ? vr[sub][e] : 0.f;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
-      const float alpha = exp2f(m[h] - mx);
-      m[h] = mx;
-      float pr[4];
-      float ls = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        pr[sub] = exp2f(sc[sub][h] - mx);
-        ls += pr[sub];
-      }
-      l[h] = fmaf(l[h], alpha, ls);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        float acc = o[h][e] * alpha;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) acc = fmaf(pr[sub], vr[sub][e], acc);
-        o[h][e] = acc;
-      }
-    }
+    page(kp[0], vp[0], p);
   }
 
   // merge the four token slots of this wave (lanes part, part+16, part+32, part+48)
@@ -198,89 +333,82 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
     }
   }
   __syncthreads();
-  // merge the four waves and publish the split's partial (o, m, l) for each query head through
-  // device-coherent stores (the merging block may sit on another XCD)
-  float *wsj = a.ws + (size_t)j * G * (D + 2);  // head h of split s at wsj + s * Hq * (D+2) + h * (D+2)
-  const size_t sstride = (size_t)a.Hq * (D + 2);
-  for (int idx = threadIdx.x; idx < G * (D + 2); idx += 256) {
-    const int h = idx / (D + 2);
-    const int d = idx - h * (D + 2);
+  // merge the four waves and publish the split's partial through device-coherent stores (the
+  // merging block may sit on another XCD): o at [s][head][D], (m, l) at [s][head][2]
+  float *wso = a.ws;
+  float *wsml = a.ws + (size_t)a.splits * a.Hq * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
     float mx = kNegBig;
 #pragma unroll
     for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm_m[w][h]);
     float val = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(sm_m[w][h] - mx);
-      val += f * (d < D ? sm_o[w][h][d] : (d == D + 1 ? sm_l[w][h] : 0.f));
-    }
-    if (d == D) val = mx;
-    __hip_atomic_store(wsj + s * sstride + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < 4; ++w) val += exp2f(sm_m[w][h] - mx) * sm_o[w][h][d];
+    __hip_atomic_store(wso + ((size_t)s * a.Hq + j * G + h) * D + d, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float mx = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) lsum += exp2f(sm_m[w][h] - mx) * sm_l[w][h];
+    float *dst = wsml + ((size_t)s * a.Hq + j * G + h) * 2;
+    __hip_atomic_store(dst, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  drain_stores();  // this thread's partial stores are acknowledged
   __syncthreads();
-  __shared__ unsigned last;
   if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(&a.counters[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    last = __hip_atomic_fetch_add(&a.counters[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            (unsigned)(a.splits - 1);
   __syncthreads();
   if (!last) return;
 
   // The last split block of KV head j merges all splits of its G query heads:
   //   out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.
-  __shared__ float sw[kMaxMergeSplits][G];
-  __shared__ float sM[G], sL[G];
-  const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc(wsj, (short)0, (int)(a.splits * sstride * 4), 0x00020000);
+  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.  Loads of a pass are all
+  // issued before use (one memory round trip per pass); the per-head max and sum are wave
+  // reductions.
+  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
   for (int idx = threadIdx.x; idx < a.splits * G; idx += 256) {
     const int ss = idx / G, h = idx - ss * G;
-    sw[ss][h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                    wr, (h * (D + 2) + D) * 4, (int)(ss * sstride * 4), kAuxSc1));
+    const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                           mlr, (uint32_t)(((size_t)ss * a.Hq + j * G + h) * 2 * 4), 0, kAuxSc1));
+    sw[ss][h] = __builtin_bit_cast(float, (uint32_t)v);
+    sl[ss][h] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
+  for (int h = wave; h < G; h += 4) {
     float M = kNegBig;
-    for (int ss = 0; ss < a.splits; ++ss) M = fmaxf(M, sw[ss][h]);
-    sM[h] = M;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < a.splits * G; idx += 256) {
-    const int ss = idx / G, h = idx - ss * G;
-    sw[ss][h] = exp2f(sw[ss][h] - sM[h]);
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
+    for (int ss = lane; ss < a.splits; ss += 64) M = fmaxf(M, sw[ss][h]);
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
     float L = 0.f;
-    for (int ss = 0; ss < a.splits; ++ss)
-      L = fmaf(sw[ss][h], __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                              wr, (h * (D + 2) + D + 1) * 4, (int)(ss * sstride * 4), kAuxSc1)), L);
-    sL[h] = L;
+    for (int ss = lane; ss < a.splits; ss += 64) L = fmaf(exp2f(sw[ss][h] - M), sl[ss][h], L);
+    L = wave_sum(L);
+    for (int ss = lane; ss < a.splits; ss += 64) sw[ss][h] = exp2f(sw[ss][h] - M) / L;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
-    float O = 0.f;
-    int ss = 0;
-    for (; ss + 8 <= a.splits; ss += 8) {
-      float t[8];
+  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
+  for (int t = threadIdx.x; t < G * D / 4; t += 256) {
+    const int h = t / (D / 4), d4 = (t - h * (D / 4)) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.splits; s0 += kMergeChunk) {
+      f32x4 v[kMergeChunk];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        t[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                   wr, (h * (D + 2) + d) * 4, (int)((ss + u) * sstride * 4), kAuxSc1));
+      for (int u = 0; u < kMergeChunk; ++u)  // splits past the last lie outside the resource: 0
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   orr, (uint32_t)((((size_t)(s0 + u) * a.Hq + j * G + h) * D + d4) * 4), 0, kAuxSc1));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) O = fmaf(sw[ss + u][h], t[u], O);
+      for (int u = 0; u < kMergeChunk; ++u)
+        if (s0 + u < a.splits) acc += sw[s0 + u][h] * v[u];
     }
-    for (; ss < a.splits; ++ss)
-      O = fmaf(sw[ss][h], __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                              wr, (h * (D + 2) + d) * 4, (int)(ss * sstride * 4), kAuxSc1)), O);
-    a.out[(size_t)(j * G + h) * D + d] = O / sL[h];
+    *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + h) * D + d4) = acc;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void kv_append(const float *__restrict__ k, const float *__restrict__ v, void *k_pool,
@@ -306,8 +434,13 @@ template <int D, int KVF>
 hipError_t launch_g(const AttnArgs &a, int G, hipStream_t st) {
   dim3 grid(a.Hkv, a.splits);
   switch (G) {
-#define QDEC_G(g) \
-  case g: hipLaunchKernelGGL((attn_split<D, g, KVF>), grid, dim3(256), 0, st, a); break;
+#define QDEC_G(g)                                                                         \
+  case g:                                                                                 \
+    if (a.qkv)                                                                            \
+      hipLaunchKernelGGL((attn_split<D, g, KVF, true>), grid, dim3(256), 0, st, a);       \
+    else                                                                                  \
+      hipLaunchKernelGGL((attn_split<D, g, KVF, false>), grid, dim3(256), 0, st, a);      \
+    break;
     QDEC_G(1) QDEC_G(2) QDEC_G(3) QDEC_G(4) QDEC_G(5) QDEC_G(6) QDEC_G(7) QDEC_G(8)
 #undef QDEC_G
     default: return hipErrorInvalidValue;
@@ -317,7 +450,8 @@ hipError_t launch_g(const AttnArgs &a, int G, hipStream_t st) {
 
 }  // namespace
 
-// [256 B of per-KV-head arrival counters, zero between launches][splits][Hq][D + 2] partials
+// [per-KV-head arrival counters, one 128-byte line each, zero between launches]
+// [splits][Hq][D] partial outputs, then [splits][Hq][2] partial (max, sum)
 size_t attn_workspace_bytes(int Hq, int D, int splits) {
   return kAttnCounterBytes + (size_t)splits * Hq * (D + 2) * sizeof(float);
 }

@@ -141,8 +141,21 @@ __global__ void swiglu_k(const float *__restrict__ g, const float *__restrict__ 
 
 // grid: ceil(H/64) waves.  E == null: h is given, only the per-tile sums of squares are written.
 __global__ void __launch_bounds__(64) embed_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ token,
-                                              int H, int V, float *h, float *__restrict__ ssq) {
+                                              int H, int V, float *h, float *__restrict__ ssq,
+                                              const int32_t *__restrict__ pos, float base, int D,
+                                              double *__restrict__ cs) {
   const int i = blockIdx.x * 64 + threadIdx.x;
+  if (cs && blockIdx.x == 0) {
+    // same angle as the per-row rotation above: theta_i = base^(-2i/D), phi = pos * theta_i
+    const int t = *pos;
+    for (int k = threadIdx.x; k < D / 2; k += 64) {
+      const double theta = pow((double)base, -2.0 * (double)k / (double)D);
+      double sn, c;
+      sincos((double)t * theta, &sn, &c);
+      cs[2 * k] = c;
+      cs[2 * k + 1] = sn;
+    }
+  }
   float v = 0.f;
   if (E) {
     int tok = *token;
@@ -239,8 +252,9 @@ hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStr
 }
 
 hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(embed_k, dim3((H + 63) / 64), dim3(64), 0, st, E, token, H, V, h, ssq);
+                        const int32_t *pos, float rope_base, int D, double *rope_cs, hipStream_t st) {
+  hipLaunchKernelGGL(embed_k, dim3((H + 63) / 64), dim3(64), 0, st, E, token, H, V, h, ssq, pos, rope_base,
+                     D, rope_cs);
   return hipGetLastError();
 }
 

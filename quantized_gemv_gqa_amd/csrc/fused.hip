@@ -52,6 +52,7 @@ struct AttnSmem {
   float wm[kMaxMergeSplits][G];  // split maxima, then their weights
   float wl[kMaxMergeSplits][G];  // split sums
   float M[G], L[G];
+  float qkv[(G + 2) * D];        // this KV head's q heads, then its new k and v (pre-RoPE)
   unsigned last;
 };
 
@@ -136,6 +137,11 @@ __device__ __forceinline__ void mark_time(unsigned long long *ts, int idx, int l
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// Per-wave diagnostic marks: slot [phase][wave][mark] = low 32 bits of the 100 MHz clock.
+__device__ __forceinline__ void wave_mark(unsigned *ts, int phase, int waves, int w, int mark, int lane) {
+  if (ts && lane == 0) ts[((size_t)phase * waves + w) * 4 + mark] = (unsigned)wall_clock64();
+}
 
 // A pointer every lane holds the same value of (read from the layer table in memory), moved to
 // scalar registers so buffer descriptors built from it stay scalar.
@@ -369,11 +375,11 @@ __device__ __forceinline__ void finish_tile(const FusedArgs &a, const SkPhase &p
     __hip_atomic_store(pt + (w - wf) * kTile + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     drain_stores();
     unsigned prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(p.tile_cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) prev = __hip_atomic_fetch_add(p.tile_cnt + t * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != (unsigned)(ns - 1)) return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) __hip_atomic_store(p.tile_cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(p.tile_cnt + t * kLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     v = sum_slots(pt, ns, lane);
   }
   v *= rn;
@@ -440,9 +446,11 @@ template <int FMT, int E, bool EMB>
 __device__ __forceinline__ void sk_gemv(const FusedArgs &a, const SkPhase &p, const StepCtx &c, const FusedLayer &Lw,
                                         const uint8_t *W, const void *S, const float *x, const float *ssq, int K,
                                         int w, XStage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm, int lane,
-                                        const unsigned long long *prog, unsigned long long dep) {
+                                        const unsigned long long *prog, unsigned long long dep, int slot) {
   constexpr int CK = (FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16;
   constexpr bool NORM = E == FE_QKV || E == FE_GU || E == FE_LM;
+  const int NWall = gridDim.x * 4;
+  wave_mark(a.wave_ts, slot, NWall, w, 0, lane);
   if (w >= p.nw) return;
   const int r0 = w * p.q + min(w, p.rem);
   const int r1 = r0 + p.q + (w < p.rem ? 1 : 0);
@@ -483,6 +491,7 @@ __device__ __forceinline__ void sk_gemv(const FusedArgs &a, const SkPhase &p, co
     ok = wait_progress(prog, dep, a.err);
   }
   if (!ok) return;
+  wave_mark(a.wave_ts, slot, NWall, w, 1, lane);
 
   float rn = 1.f;
   if constexpr (NORM) {
@@ -506,6 +515,7 @@ __device__ __forceinline__ void sk_gemv(const FusedArgs &a, const SkPhase &p, co
   }
   const float *const g_emb = EMB ? uniform(Lw.g_attn) : nullptr;
   stage_round<FMT, EMB>(sm, x, xe, g_emb, K, nch, rr, rend - rr, lane);
+  wave_mark(a.wave_ts, slot, NWall, w, 2, lane);
 
   float acc = 0.f;
   // two copies of the loop body with the buffers' roles swapped (no register moves)
@@ -538,27 +548,25 @@ __device__ __forceinline__ void sk_gemv(const FusedArgs &a, const SkPhase &p, co
     if (!body(A, B, n)) break;
     if (!body(B, A, n)) break;
   }
+  wave_mark(a.wave_ts, slot, NWall, w, 3, lane);
 }
 
 // ------------------------------------------------------------------------------ attention
 // bf16 KV row piece of one lane: 8 values (D = 128) at byte offset `off` of the pool, packed
-__device__ __forceinline__ u32x4 load_row8_raw(__amdgpu_buffer_rsrc_t pool, uint32_t off, bool coherent) {
-  return coherent ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool, off, 0, kAuxSc1))
-                  : __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool, off, 0, 0));
+__device__ __forceinline__ u32x4 load_row8_raw(__amdgpu_buffer_rsrc_t pool, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pool, off, 0, 0));
 }
-__device__ __forceinline__ void unpack8(u32x4 v, float (&r)[8]) {
+__device__ __forceinline__ float bf16_at(u32x4 v, int e) {
+  const uint32_t w = v[e >> 1];
+  return __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+// pack 8 floats to bf16 (round to nearest even), the layout of a row piece
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&v)[8]) {
+  u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[2 * i] = __builtin_bit_cast(float, v[i] << 16);
-    r[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
-  }
-}
-
-// 8 consecutive fp32 values written earlier in this kernel (sc1 buffer loads, pipelined)
-__device__ __forceinline__ void load8_coh(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[8]) {
-  const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxSc1));
-  const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kAuxSc1));
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  for (int i = 0; i < 4; ++i)
+    r[i] = (uint32_t)float_to_bf16_rne(v[2 * i]) | ((uint32_t)float_to_bf16_rne(v[2 * i + 1]) << 16);
+  return r;
 }
 
 // Normalise (optional) and rotate one head vector held 8 dims per lane (lanes `part` of a 16-lane
@@ -591,6 +599,53 @@ __device__ __forceinline__ void norm_rope8(float (&own)[8], float (&mate)[8], in
   }
 }
 
+// One wave, one 16-token page: token slot sub*4 + slot sits in this lane's kp[sub] / vp[sub];
+// tokens at or past T are masked.
+template <int G>
+__device__ __forceinline__ void attend_page8(u32x4 (&kp)[4], u32x4 (&vp)[4], int p, int T, int slot,
+                                             const float (&q)[G][8], float (&m)[G], float (&l)[G],
+                                             float (&o)[G][8]) {
+  float sc[4][G];
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) {
+    const bool valid = p * 16 + sub * 4 + slot < T;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(q[h][e], bf16_at(kp[sub], e), d);
+      d = sum16(d);
+      sc[sub][h] = valid ? d : -INFINITY;
+    }
+    if (!valid) vp[sub] = u32x4{0u, 0u, 0u, 0u};  // masked slots add 0 * 0
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
+    const float alpha = exp2f(m[h] - mx);
+    m[h] = mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      sc[sub][h] = exp2f(sc[sub][h] - mx);
+      ls += sc[sub][h];
+    }
+    l[h] = fmaf(l[h], alpha, ls);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+  }
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float vv = bf16_at(vp[sub], e);
+#pragma unroll
+      for (int h = 0; h < G; ++h) o[h][e] = fmaf(sc[sub][h], vv, o[h][e]);
+    }
+}
+
+constexpr int kMergeChunk = 32;  // splits whose partial outputs one merge pass loads at once
+
 // Attention work unit (KV head j, split s) executed by a whole workgroup (4 waves).
 template <int G>
 __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, const FusedLayer &Lw, int j, int s, int pos,
@@ -606,74 +661,94 @@ __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, 
   const int p0 = s * pps;
   const int p1 = min(P, p0 + pps);
   const int last_page = P - 1;
-  const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * 2);
   void *const k_pool = uniform(Lw.k_pool), *const v_pool = uniform(Lw.v_pool);
+  const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * 2);
   const __amdgpu_buffer_rsrc_t kpool = rsrc(k_pool, pool_bytes);
   const __amdgpu_buffer_rsrc_t vpool = rsrc(v_pool, pool_bytes);
   const __amdgpu_buffer_rsrc_t qkvr = rsrc(a.qkv, (uint32_t)((a.Hq + 2 * a.Hkv) * D * 4));
   const size_t head_stride = (size_t)16 * D;
 
-  // prefetch the wave's first page (packed) unless it is the one the new token lands in
-  u32x4 kp[4], vp[4];
-  const int pf = p0 + wave;
-  bool have = false;
-  if (pf < p1 && pf != last_page) {
-    const int phys = a.page_table[pf];
-    if (phys >= 0 && phys < a.n_pages) {
-      const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
+  // the wave's first two pages are requested before the wait (the newest token's row of the last
+  // page is replaced by the freshly computed k and v below, so no page depends on this step)
+  u32x4 kp[2][4], vp[2][4];
+  bool have[2];
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const uint32_t e = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * 2);
-        kp[sub] = load_row8_raw(kpool, e, false);
-        vp[sub] = load_row8_raw(vpool, e, false);
+  for (int i = 0; i < 2; ++i) {
+    const int p = p0 + wave + 4 * i;
+    have[i] = false;
+    if (p < p1) {
+      const int phys = a.page_table[p];
+      if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
+        have[i] = true;
+        const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          const uint32_t e = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * 2);
+          kp[i][sub] = load_row8_raw(kpool, e);
+          vp[i][sub] = load_row8_raw(vpool, e);
+        }
       }
-      have = true;
     }
   }
 
+  const int gwv = blockIdx.x * 4 + wave, NWall = gridDim.x * 4;
+  wave_mark(a.wave_ts, 5 * c.l + 1, NWall, gwv, 0, lane);
   // the qkv tiles of KV head j: G q heads plus one k and one v head, D / 64 tiles each
   const unsigned tiles_j = (unsigned)((G + 2) * (D / kTile));
   const bool ok = wait_count(a.qkv_done + (c.l * a.Hkv + j) * 32, (c.e + 1u) * tiles_j, a.err);
+  wave_mark(a.wave_ts, 5 * c.l + 1, NWall, gwv, 1, lane);
+
+  // stage this KV head's q heads and its new k, v in LDS (device-coherent loads, one round trip)
+  for (int i = threadIdx.x; i < (G + 2) * D / 4; i += 256) {
+    const int h = (i * 4) / D, d = i * 4 - h * D;
+    const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
+    *reinterpret_cast<f32x4 *>(&sm.qkv[h * D + d]) =
+        __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qkvr, (uint32_t)((row * D + d) * 4), 0, kAuxSc1));
+  }
+  __syncthreads();
 
   // q of the G query heads: normalised (Qwen3), rotated, scaled into the log2 domain
   float q[G][DPL];
   const int dmate = part * DPL < 64 ? part * DPL + 64 : part * DPL - 64;
+  const float *gq = uniform(Lw.g_q), *gk = uniform(Lw.g_k);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float own[8], mate[8];
-    const uint32_t qoff = (uint32_t)((j * G + h) * D) * 4;
-    load8_coh(qkvr, qoff + part * DPL * 4, own);
-    load8_coh(qkvr, qoff + dmate * 4, mate);
-    norm_rope8(own, mate, part, Lw.g_q, a.eps, cs);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      own[e] = sm.qkv[h * D + part * DPL + e];
+      mate[e] = sm.qkv[h * D + dmate + e];
+    }
+    norm_rope8(own, mate, part, gq, a.eps, cs);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) q[h][e] = own[e] * a.scale_log2;
   }
-
-  // the split that owns the last page appends the new token's k (normalised, rotated) and v
+  // the new token's k (normalised, rotated) and v, rounded to bf16 like every cached key
+  u32x4 knew, vnew;
+  {
+    float own[8], mate[8], vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      own[e] = sm.qkv[G * D + part * DPL + e];
+      mate[e] = sm.qkv[G * D + dmate + e];
+      vv[e] = sm.qkv[(G + 1) * D + part * DPL + e];
+    }
+    norm_rope8(own, mate, part, gk, a.eps, cs);
+    knew = pack_bf16x8(own);
+    vnew = pack_bf16x8(vv);
+  }
+  // the split that owns the last page appends them for later steps (nothing reads them in this
+  // step: the newest row is taken from registers below)
   const bool mine_last = p0 <= last_page && last_page < p1;
   if (mine_last && ok && wave == 0 && slot == 0) {
-    float own[8], mate[8], vv[8];
-    const uint32_t koff = (uint32_t)((a.Hq + j) * D) * 4, voff = (uint32_t)((a.Hq + a.Hkv + j) * D) * 4;
-    load8_coh(qkvr, koff + part * DPL * 4, own);
-    load8_coh(qkvr, koff + dmate * 4, mate);
-    load8_coh(qkvr, voff + part * DPL * 4, vv);
-    norm_rope8(own, mate, part, Lw.g_k, a.eps, cs);
     const int phys = a.page_table[last_page];
     if (phys >= 0 && phys < a.n_pages) {
       const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (pos & 15)) * D + part * DPL;
-      uint32_t *kd = reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(k_pool) + e0);
-      uint32_t *vd = reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(v_pool) + e0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t kw = (uint32_t)float_to_bf16_rne(own[2 * e]) | ((uint32_t)float_to_bf16_rne(own[2 * e + 1]) << 16);
-        const uint32_t vw = (uint32_t)float_to_bf16_rne(vv[2 * e]) | ((uint32_t)float_to_bf16_rne(vv[2 * e + 1]) << 16);
-        __hip_atomic_store(kd + e, kw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(vd + e, vw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(k_pool) + e0) = knew;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(v_pool) + e0) = vnew;
     }
-    drain_stores();
   }
-  __syncthreads();  // the appended row is acknowledged before any wave reads the last page
+  const int new_sub = (pos & 15) >> 2, new_slot = pos & 3;
 
   float m[G], l[G], o[G][DPL];
 #pragma unroll
@@ -683,62 +758,31 @@ __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, 
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
-  for (int p = p0 + wave; p < p1 && ok; p += 4) {
-    if (!(have && p == pf)) {
+  auto page = [&](u32x4 (&kq)[4], u32x4 (&vq)[4], int p) {
+    if (p == last_page) {  // the newest token's row comes from registers
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+        if (sub == new_sub && slot == new_slot) {
+          kq[sub] = knew;
+          vq[sub] = vnew;
+        }
+    }
+    attend_page8<G>(kq, vq, p, T, slot, q, m, l, o);
+  };
+  if (ok) {
+    if (have[0]) page(kp[0], vp[0], p0 + wave);
+    if (have[1]) page(kp[1], vp[1], p0 + wave + 4);
+    for (int p = p0 + wave + 8; p < p1; p += 4) {
       const int phys = a.page_table[p];
-      if (phys < 0 || phys >= a.n_pages) continue;  // documented precondition; never read outside
+      if (phys < 0 || phys >= a.n_pages) continue;
       const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-      const bool coh = p == last_page;  // rows written by this step must bypass stale L2 copies
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         const uint32_t e = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * 2);
-        kp[sub] = load_row8_raw(kpool, e, coh);
-        vp[sub] = load_row8_raw(vpool, e, coh);
+        kp[0][sub] = load_row8_raw(kpool, e);
+        vp[0][sub] = load_row8_raw(vpool, e);
       }
-    }
-    // scores of the wave's 4 token slots for the G heads (K unpacked one slot at a time)
-    float sc[4][G];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const bool valid = p * 16 + sub * 4 + slot < T;
-      float kr[DPL];
-      unpack8(kp[sub], kr);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) d = fmaf(q[h][e], kr[e], d);
-        d = sum16(d);
-        sc[sub][h] = valid ? d : -INFINITY;
-      }
-      if (!valid) vp[sub] = u32x4{0u, 0u, 0u, 0u};  // masked slots add 0 * 0
-    }
-    // online softmax update; sc becomes the probabilities
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
-      const float alpha = exp2f(m[h] - mx);
-      m[h] = mx;
-      float ls = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        sc[sub][h] = exp2f(sc[sub][h] - mx);
-        ls += sc[sub][h];
-      }
-      l[h] = fmaf(l[h], alpha, ls);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
-    }
-    // o += p v, V unpacked one value at a time
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const uint32_t wv = vp[sub][e >> 1];
-        const float vv = __builtin_bit_cast(float, (e & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h][e] = fmaf(sc[sub][h], vv, o[h][e]);
-      }
+      page(kp[0], vp[0], p);
     }
   }
   // merge the four token slots of the wave
@@ -771,41 +815,49 @@ __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, 
     }
   }
   __syncthreads();
-  // publish the split's (o, m, l) per query head
-  float *wsj = a.attn_ws + (size_t)j * G * (D + 2);
-  const size_t sstride = (size_t)a.Hq * (D + 2);
-  for (int idx = threadIdx.x; idx < G * (D + 2); idx += 256) {
-    const int h = idx / (D + 2);
-    const int d = idx - h * (D + 2);
+  // publish the split's partial: o at [s][head][D], (m, l) at [s][head][2]
+  float *wso = a.attn_ws;
+  float *wsml = a.attn_ws + (size_t)a.splits * a.Hq * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
     float mx = kNegBig;
 #pragma unroll
     for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.m[w][h]);
     float val = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(sm.m[w][h] - mx);
-      val += f * (d < D ? sm.o[w][h][d] : (d == D + 1 ? sm.l[w][h] : 0.f));
-    }
-    if (d == D) val = mx;
-    __hip_atomic_store(wsj + s * sstride + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < 4; ++w) val += exp2f(sm.m[w][h] - mx) * sm.o[w][h][d];
+    __hip_atomic_store(wso + ((size_t)s * a.Hq + j * G + h) * D + d, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float mx = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm.m[w][h]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) lsum += exp2f(sm.m[w][h] - mx) * sm.l[w][h];
+    float *dst = wsml + ((size_t)s * a.Hq + j * G + h) * 2;
+    __hip_atomic_store(dst, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   drain_stores();
+  wave_mark(a.wave_ts, 5 * c.l + 1, NWall, gwv, 2, lane);
   __syncthreads();
   if (threadIdx.x == 0)
-    sm.last = __hip_atomic_fetch_add(&a.attn_cnt[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    sm.last = __hip_atomic_fetch_add(&a.attn_cnt[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               (unsigned)(a.splits - 1);
   __syncthreads();
   if (!sm.last) return;
 
-  // the last split of KV head j merges the splits of its G query heads (every load of a pass is
-  // independent, so each pass costs one memory round trip)
-  const __amdgpu_buffer_rsrc_t wr = rsrc(wsj, (uint32_t)(a.splits * sstride * 4));
+  // the last split of KV head j merges the splits of its G query heads; every pass issues all of
+  // its loads before using them (one memory round trip per pass)
+  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
   for (int idx = threadIdx.x; idx < a.splits * G; idx += 256) {
     const int ss = idx / G, h = idx - ss * G;
-    const float mv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, (h * (D + 2) + D) * 4, (int)(ss * sstride * 4), kAuxSc1));
-    const float lv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, (h * (D + 2) + D + 1) * 4, (int)(ss * sstride * 4), kAuxSc1));
-    sm.wm[ss][h] = mv;
-    sm.wl[ss][h] = lv;
+    const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                           mlr, (uint32_t)(((size_t)ss * a.Hq + j * G + h) * 2 * 4), 0, kAuxSc1));
+    sm.wm[ss][h] = __builtin_bit_cast(float, (uint32_t)v);
+    sm.wl[ss][h] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -820,31 +872,26 @@ __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, 
   __syncthreads();
   for (int idx = threadIdx.x; idx < a.splits * G; idx += 256) {
     const int ss = idx / G, h = idx - ss * G;
-    sm.wm[ss][h] = exp2f(sm.wm[ss][h] - sm.M[h]);
+    sm.wm[ss][h] = exp2f(sm.wm[ss][h] - sm.M[h]) / sm.L[h];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
-    float O = 0.f;
-    int ss = 0;
-    for (; ss + 16 <= a.splits; ss += 16) {
-      float t[16];
+  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
+  for (int t = threadIdx.x; t < G * D / 4; t += 256) {
+    const int h = t / (D / 4), d4 = (t - h * (D / 4)) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.splits; s0 += kMergeChunk) {
+      f32x4 v[kMergeChunk];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        t[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, (h * (D + 2) + d) * 4, (int)((ss + u) * sstride * 4), kAuxSc1));
+      for (int u = 0; u < kMergeChunk; ++u)  // splits past the last lie outside the resource: 0
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   orr, (uint32_t)((((size_t)(s0 + u) * a.Hq + j * G + h) * D + d4) * 4), 0, kAuxSc1));
 #pragma unroll
-      for (int u = 0; u < 16; ++u) O = fmaf(sm.wm[ss + u][h], t[u], O);
+      for (int u = 0; u < kMergeChunk; ++u)
+        if (s0 + u < a.splits) acc += sm.wm[s0 + u][h] * v[u];
     }
-    {
-      float t[16];
+    float *dst = a.attn + (size_t)(j * G + h) * D + d4;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)  // past the last split: outside the resource, reads 0
-        t[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr, (h * (D + 2) + d) * 4, (int)((ss + u) * sstride * 4), kAuxSc1));
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (ss + u < a.splits) O = fmaf(sm.wm[ss + u][h], t[u], O);
-    }
-    st_f<true>(a.attn + (size_t)(j * G + h) * D + d, O / sm.L[h]);
+    for (int e = 0; e < 4; ++e) st_f<true>(dst + e, acc[e]);
   }
   drain_stores();
   __syncthreads();
@@ -852,13 +899,14 @@ __device__ __forceinline__ void attn_unit(const FusedArgs &a, const StepCtx &c, 
     const int ln = threadIdx.x;
     unsigned prev = 0;
     if (ln == 0) {
-      __hip_atomic_store(&a.attn_cnt[j], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.attn_cnt[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = __hip_atomic_fetch_add(a.attn_all + c.l * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev + 1 == (c.e + 1u) * (unsigned)a.Hkv)
       publish(reinterpret_cast<unsigned long long *>(a.progress), c.e * c.pps + 3ull * c.l + 1, ln);
     mark_time(a.phase_ts, 1 + 5 * c.l + 1, ln);
+    wave_mark(a.wave_ts, 5 * c.l + 1, NWall, gwv, 3, ln);
   }
 }
 
@@ -904,10 +952,11 @@ __global__ void __launch_bounds__(256, 2) decode_step_fused(const FusedArgs a) {
     const FusedLayer &Lw = a.layers[l];
     // qkv GEMV: RMSNorm prologue (layer 0 reads the embedding row itself), bias
     if (l == 0)
-      sk_gemv<FMT, FE_QKV, true>(a, a.p_qkv, c, Lw, Lw.w_qkv, Lw.s_qkv, nullptr, nullptr, a.H, gw, xs, lane, prog, 0);
+      sk_gemv<FMT, FE_QKV, true>(a, a.p_qkv, c, Lw, Lw.w_qkv, Lw.s_qkv, nullptr, nullptr, a.H, gw, xs, lane, prog, 0,
+                                 5 * l);
     else
       sk_gemv<FMT, FE_QKV, false>(a, a.p_qkv, c, Lw, Lw.w_qkv, Lw.s_qkv, a.xa, a.ssqA, a.H, gw, xs, lane, prog,
-                                  base + 3ull * l);
+                                  base + 3ull * l, 5 * l);
     // attention: q/k norm, RoPE, KV append, split partials, merge
     for (int u = blockIdx.x; u < a.Hkv * a.splits; u += gridDim.x) {
       const int jh = u / a.splits, s = u - jh * a.splits;
@@ -916,18 +965,18 @@ __global__ void __launch_bounds__(256, 2) decode_step_fused(const FusedArgs a) {
     }
     // o GEMV + residual (writes hB, its sums of squares and hB * g_ffn)
     sk_gemv<FMT, FE_O, false>(a, a.p_o, c, Lw, Lw.w_o, Lw.s_o, a.attn, nullptr, a.Hq * 128, gw, xs, lane, prog,
-                              base + 3ull * l + 1);
+                              base + 3ull * l + 1, 5 * l + 2);
     // gate/up GEMV (RMSNorm prologue) + SwiGLU
     sk_gemv<FMT, FE_GU, false>(a, a.p_gu, c, Lw, Lw.w_gu, Lw.s_gu, a.xb, a.ssqB, a.H, gw, xs, lane, prog,
-                               base + 3ull * l + 2);
+                               base + 3ull * l + 2, 5 * l + 3);
     // down GEMV + residual (writes hA); waits per gate/up tile
     sk_gemv<FMT, FE_DOWN, false>(a, a.p_down, c, Lw, Lw.w_down, Lw.s_down, a.mlp, nullptr, a.I, gw, xs, lane,
-                                 prog, 0);
+                                 prog, 0, 5 * l + 4);
   }
   // lm head (final RMSNorm prologue) + greedy argmax; its last finisher completes the step
   c.l = L;
   sk_gemv<FMT, FE_LM, false>(a, a.p_lm, c, a.layers[0], a.w_lm, a.s_lm, a.xa, a.ssqA, a.H, gw, xs, lane, prog,
-                             base + 3ull * L);
+                             base + 3ull * L, 5 * L);
 }
 
 template <int FMT, int G>

@@ -10,13 +10,14 @@
 // wave owns a tile of 64 output rows, one row per lane, so
 //   * every weight load is one coalesced 1 KiB wave access (the packed "tile64" layout puts the
 //     16-byte runs of 64 rows side by side),
-//   * the activation chunk is the same for all lanes and is broadcast through scalar registers
-//     (v_readlane), so there is no LDS staging and no cross-lane reduction of the dot product,
+//   * the activation chunk is the same for all lanes: it is staged once per batch of runs in LDS
+//     and read back as a broadcast, so the dot product needs no cross-lane reduction,
 //   * the K dimension is split across waves to fill the 256 CUs when N is small; partial sums
 //     go to a workspace and the last wave to arrive at a tile adds them in a fixed order
 //     (deterministic, no float atomics) and runs the epilogue.
-// INT4 codes are unpacked with one AND (low nibbles) and one shift+AND (high nibbles) per 8
-// codes, then v_cvt_f32_ubyte{0..3}; the zero point is folded out of the inner loop:
+// INT4 codes are unpacked with two AND masks per 8 codes (low nibbles in place, high nibbles in
+// place as 16 c, met by activations pre-divided by 16), then v_cvt_f32_ubyte{0..3}; the zero
+// point is folded out of the inner loop:
 //   sum_k (c_k - 8) x_k = sum_k c_k x_k - 8 sum_k x_k,  with sum_k x_k computed once per chunk.
 // INT8 codes are biased to unsigned by XOR 0x80 (c + 128) and folded the same way.
 #include <hip/hip_runtime.h>
@@ -33,7 +34,6 @@ using namespace dev;
 
 constexpr int kTargetUnits = 2048;  // ~8 waves per CU on 256 CUs
 constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
-constexpr int kMaxSplitTiles = kArgmaxCounter;  // larger N: no split
 
 // Standalone launch: one wave per (tile, k-split) unit, no cross-phase dependency.
 template <int FMT, bool NORM, int EPI>
@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) gemv_tile64(const GemvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * 4 + wave;
   if (unit >= ((a.N + kTile - 1) / kTile) * a.ks) return;  // whole wave
-  gemv_unit<FMT, NORM, EPI, false>(a, unit, stage_all[wave], lane, nullptr, 0, nullptr);
+  gemv_unit<FMT, NORM, EPI>(a, unit, stage_all[wave], lane);
 }
 
 template <int FMT>
@@ -126,14 +126,16 @@ GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split) {
   return p;
 }
 
-// Workspace layout, shared by every GEMV that runs on it one after another: the tile arrival
-// counters sit in a fixed region at the start (each launch leaves the ones it used at zero, so
-// the region stays zero between launches whatever the shape), the split-K partials follow.
+// Workspace layout, shared by every GEMV that runs on it one after another: the arrival counters
+// (one per 128-byte line: tile counters from line 0, then the argmax top and group counters at
+// the end of the region) sit in a fixed region at the start; each launch leaves the ones it used
+// at zero, so the region stays zero between launches whatever the shape.  Split-K partials
+// follow, then the argmax candidates (per tile, then per group).
 size_t gemv_workspace_bytes(int wfmt, int N, int K, bool argmax) {
   GemvPlan p = gemv_plan(wfmt, N, K, true);
   size_t b = kCounterBytes;
   if (p.ks > 1) b += (size_t)p.tiles * p.ks * kTile * sizeof(float);
-  if (argmax) b += (size_t)p.tiles * 2 * sizeof(float);
+  if (argmax) b += (size_t)(p.tiles + kArgGroups) * 2 * sizeof(float);
   return b;
 }
 

@@ -111,45 +111,6 @@ __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Bounded wait until *ctr >= target (device-coherent polls).  On timeout sets *err and returns
-// false; once *err is set every later wait returns false at once, so a failed step ends within
-// one timeout instead of one per phase.  The caller then skips its work (every wave still runs
-// to the end of the kernel).
-__device__ __forceinline__ bool wait_counter(const unsigned *ctr, unsigned target, unsigned *err) {
-  if (!ctr) return true;
-  unsigned spins = 0;
-  while (__hip_atomic_load(const_cast<unsigned *>(ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    ++spins;
-    if ((spins & 1023u) == 0 && err &&
-        __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-      return false;
-    if (spins > kSpinLimit) {
-      if (err) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
-    }
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return true;
-}
-
-// Count one finished piece of a phase; the caller whose count completes the phase publishes the
-// new progress value to every replica (lanes 0..kProgressReplicas-1 store one line each).
-// Phases complete strictly in order, so progress is monotonic within a step.
-__device__ __forceinline__ void count_done(unsigned *ctr, unsigned target, unsigned phase,
-                                           unsigned *progress, int lane,
-                                           unsigned long long *phase_ts = nullptr) {
-  drain_stores();
-  unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev + 1 == target && progress) {
-    if (lane < kProgressReplicas)
-      __hip_atomic_store(progress + lane * 32, phase + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (phase_ts && lane == 0) phase_ts[1 + phase] = wall_clock64();
-  }
-}
-
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
 __device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
 __device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
@@ -204,8 +165,8 @@ struct Stage {
 };
 
 // Stage NB runs starting at run c.  Lane l covers values 4l .. 4l+3 of the batch; CK/4 lanes
-// cover one run.  COH: the activation was written by other workgroups of the same kernel.
-template <int CK, int NB, bool NORM, bool COH>
+// cover one run.
+template <int CK, int NB, bool NORM>
 __device__ __forceinline__ void stage_batch(Stage<CK> &sm, __amdgpu_buffer_rsrc_t xr,
                                             __amdgpu_buffer_rsrc_t gr, int c, int lane) {
   constexpr int LPR = CK / 4;  // lanes per run
@@ -213,7 +174,7 @@ __device__ __forceinline__ void stage_batch(Stage<CK> &sm, __amdgpu_buffer_rsrc_
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
   if (active) {
     const int soff = c * CK * 4;
-    v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, lane * 16, soff, COH ? kAuxSc1 : 0));
+    v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, lane * 16, soff, 0));
     if constexpr (NORM)
       v *= __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, lane * 16, soff, 0));
   }
@@ -278,16 +239,80 @@ __device__ __forceinline__ void compute_batch(float &acc, const GemvBatchRegs<FM
   __builtin_amdgcn_wave_barrier();  // the next batch overwrites this wave's stage
 }
 
-// One GEMV work unit (64-row tile t, k-split s) executed by one wave.
-//   * the first batch of weights is requested before `dep` is waited on, so the dependency
-//     latency overlaps the weight stream (dep may be null: no dependency);
+// Greedy token over the tiles of an lm-head GEMV: every tile posts its (max, row) candidate; the
+// last tile of each group (tile mod kArgGroups) reduces its group, the last group reduces the
+// groups, writes the token and advances the step scalars.  Two levels, because same-line
+// atomics serialize: one counter for thousands of tiles would take tens of microseconds.
+__device__ __forceinline__ void argmax_tiles(const GemvArgs &a, int tile, int tiles, float bv, int bi, int lane) {
+  if (lane == 0) {
+    __hip_atomic_store(&a.cand[2 * tile], bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.cand[2 * tile + 1], __builtin_bit_cast(float, bi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  drain_stores();
+  const int g = tile % kArgGroups;
+  const int in_g = (tiles - 1 - g) / kArgGroups + 1;  // tiles of this group
+  unsigned *gc = a.counters + (kArgGroupLine0 + g) * kLine;
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev + 1 != (unsigned)in_g) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (lane == 0) __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const __amdgpu_buffer_rsrc_t cr = rsrc(a.cand, (uint32_t)(tiles + kArgGroups) * 8);
+  float gv = -INFINITY;
+  int gi = INT_MAX;
+  for (int i = lane; i < in_g; i += 64) {
+    const int t = g + kArgGroups * i;
+    const float cv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cr, t * 8, 0, kAuxSc1));
+    const int ci = (int)__builtin_amdgcn_raw_buffer_load_b32(cr, t * 8 + 4, 0, kAuxSc1);
+    if (ci != INT_MAX && (gi == INT_MAX || cv > gv || (cv == gv && ci < gi))) {
+      gv = cv;
+      gi = ci;
+    }
+  }
+  wave_argmax(gv, gi);
+  float *gcand = a.cand + 2 * tiles;
+  if (lane == 0) {
+    __hip_atomic_store(&gcand[2 * g], gv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&gcand[2 * g + 1], __builtin_bit_cast(float, gi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  drain_stores();
+  const int groups = tiles < kArgGroups ? tiles : kArgGroups;
+  unsigned *tc = a.counters + kArgTopLine * kLine;
+  prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(tc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev + 1 != (unsigned)groups) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  gv = -INFINITY;
+  gi = INT_MAX;
+  if (lane < groups) {
+    const float cv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cr, (tiles + lane) * 8, 0, kAuxSc1));
+    const int ci = (int)__builtin_amdgcn_raw_buffer_load_b32(cr, (tiles + lane) * 8 + 4, 0, kAuxSc1);
+    if (ci != INT_MAX) {
+      gv = cv;
+      gi = ci;
+    }
+  }
+  wave_argmax(gv, gi);
+  if (lane == 0) {
+    __hip_atomic_store(tc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int tok = (gi == INT_MAX) ? 0 : gi;
+    *a.token = tok;
+    if (a.token_log && a.step_count) {
+      const int stc = *a.step_count;
+      if (stc >= 0 && stc < a.log_len) a.token_log[stc] = tok;
+    }
+    if (a.step_count) *a.step_count += 1;
+    if (a.pos) *a.pos += 1;
+  }
+}
+
+// One GEMV work unit (64-row tile t, k-split s) executed by one wave of a standalone launch.
 //   * split-K partials travel through device-coherent memory and the last wave of a tile adds
-//     them in a fixed order, then runs the epilogue; with a.done it then counts the tile done;
-//   * COH: activations, residuals and outputs are shared with other workgroups of the same
-//     kernel (the persistent step), so they move through device-coherent accesses.
-template <int FMT, bool NORM, int EPI, bool COH>
-__device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm, int lane,
-                          const unsigned *dep, unsigned dep_target, unsigned *err) {
+//     them in a fixed order, then runs the epilogue.
+template <int FMT, bool NORM, int EPI>
+__device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm, int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;  // k per 16-byte run
   const int ks = a.ks, K = a.K, N = a.N;
@@ -312,33 +337,27 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
   int cb = c0;
   const int n_full = (c1 - c0) / kBatch;
   const int rem = (c1 - c0) - n_full * kBatch;
-  // prefetch the first batch, then wait for the activation's producer
-  if (n_full > 0) load_batch<FMT, kBatch>(r, wr, sr, cb, gshift, lane);
-  else if (rem & 4) load_batch<FMT, 4>(r, wr, sr, cb, gshift, lane);
-  else if (rem & 2) load_batch<FMT, 2>(r, wr, sr, cb, gshift, lane);
-  else if (rem & 1) load_batch<FMT, 1>(r, wr, sr, cb, gshift, lane);
-  if (!wait_counter(dep, dep_target, err)) return;
   for (int b = 0; b < n_full; ++b) {
-    if (b > 0) load_batch<FMT, kBatch>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, kBatch, NORM, COH>(sm, xr, gr, cb, lane);
+    load_batch<FMT, kBatch>(r, wr, sr, cb, gshift, lane);
+    stage_batch<CK, kBatch, NORM>(sm, xr, gr, cb, lane);
     compute_batch<FMT, kBatch>(acc, r, sm);
     cb += kBatch;
   }
   if (rem & 4) {
-    if (n_full > 0) load_batch<FMT, 4>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 4, NORM, COH>(sm, xr, gr, cb, lane);
+    load_batch<FMT, 4>(r, wr, sr, cb, gshift, lane);
+    stage_batch<CK, 4, NORM>(sm, xr, gr, cb, lane);
     compute_batch<FMT, 4>(acc, r, sm);
     cb += 4;
   }
   if (rem & 2) {
-    if (n_full > 0 || (rem & 4)) load_batch<FMT, 2>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 2, NORM, COH>(sm, xr, gr, cb, lane);
+    load_batch<FMT, 2>(r, wr, sr, cb, gshift, lane);
+    stage_batch<CK, 2, NORM>(sm, xr, gr, cb, lane);
     compute_batch<FMT, 2>(acc, r, sm);
     cb += 2;
   }
   if (rem & 1) {
-    if (n_full > 0 || (rem & 6)) load_batch<FMT, 1>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 1, NORM, COH>(sm, xr, gr, cb, lane);
+    load_batch<FMT, 1>(r, wr, sr, cb, gshift, lane);
+    stage_batch<CK, 1, NORM>(sm, xr, gr, cb, lane);
     compute_batch<FMT, 1>(acc, r, sm);
   }
 
@@ -349,9 +368,9 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
     float *pp = a.part + (size_t)tile * ks * kTile + lane;
     __hip_atomic_store(pp + (size_t)ksi * kTile, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     drain_stores();
+    unsigned *ctr = a.counters + tile * kLine;
     unsigned prev = 0;
-    if (lane == 0)
-      prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != (unsigned)(ks - 1)) return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -370,14 +389,14 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
     }
     for (; i < ks; ++i)
       acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, i * kTile * 4, kAuxSc1));
-    if (lane == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ------------------------------------------------------------------ epilogue (one tile)
   float v = acc;
   if constexpr (NORM) {
     float t = 0.f;
-    for (int i = lane; i < a.ssq_n; i += 64) t += ld_f<COH>(a.ssq + i);
+    for (int i = lane; i < a.ssq_n; i += 64) t += a.ssq[i];
     const float ms = wave_sum(t) / (float)K;
     v *= rsqrtf(ms + a.eps);
   }
@@ -387,81 +406,26 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
     const bool valid = n < N;
     if (valid) {
       if (a.bias) v += a.bias[n];
-      if (a.residual) v += ld_f<COH>(a.residual + n);
-      st_f<COH>(a.y + n, v);
-      if (a.y2) a.y2[n] = v;
+      if (a.residual) v += a.residual[n];
+      a.y[n] = v;
     }
     if (EPI == EPI_STORE && a.ssq_out) {
       const float sq = wave_sum(valid ? v * v : 0.f);
-      if (lane == 0) st_f<COH>(a.ssq_out + tile, sq);
+      if (lane == 0) a.ssq_out[tile] = sq;
     }
     if constexpr (EPI == EPI_ARGMAX) {
       // tile candidate: largest value, smallest row on ties (NaN never wins)
       float bv = (valid && v == v) ? v : -INFINITY;
       int bi = (valid && v == v) ? n : INT_MAX;
       wave_argmax(bv, bi);
-      if (lane == 0) {
-        __hip_atomic_store(&a.cand[2 * tile], bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.cand[2 * tile + 1], __builtin_bit_cast(float, bi), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-      drain_stores();
-      const int tiles = (N + kTile - 1) / kTile;
-      unsigned prev = 0;
-      if (lane == 0)
-        prev = __hip_atomic_fetch_add(&a.counters[kArgmaxCounter], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      prev = __builtin_amdgcn_readfirstlane(prev);
-      if (prev != (unsigned)(tiles - 1)) return;
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      // last tile: reduce every tile's candidate (8 loads in flight per lane)
-      const __amdgpu_buffer_rsrc_t cr = rsrc(a.cand, (uint32_t)tiles * 8);
-      float gv = -INFINITY;
-      int gi = INT_MAX;
-      for (int t0 = 0; t0 < tiles; t0 += 64 * 8) {
-        float cv[8];
-        int ci[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int t = t0 + u * 64 + lane;  // out-of-range t reads zeros: index 0 is masked below
-          cv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cr, t * 8, 0, kAuxSc1));
-          ci[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(cr, t * 8 + 4, 0, kAuxSc1);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int t = t0 + u * 64 + lane;
-          if (t < tiles && ci[u] != INT_MAX && (gi == INT_MAX || cv[u] > gv || (cv[u] == gv && ci[u] < gi))) {
-            gv = cv[u];
-            gi = ci[u];
-          }
-        }
-      }
-      wave_argmax(gv, gi);
-      if (lane == 0) {
-        const int tok = (gi == INT_MAX) ? 0 : gi;
-        st_f<COH>(reinterpret_cast<float *>(a.token), __builtin_bit_cast(float, tok));
-        if (a.token_log && a.step_count) {
-          const int stc = *a.step_count;
-          if (stc >= 0 && stc < a.log_len) a.token_log[stc] = tok;
-        }
-        if (a.step_count) *a.step_count += 1;
-        if (a.pos) *a.pos += 1;
-        if (a.phase_ts) a.phase_ts[1 + a.done_phase] = wall_clock64();
-        __hip_atomic_store(&a.counters[kArgmaxCounter], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // every other unit of the step is finished: clear the step's phase counters and progress
-      for (int i = lane; i < a.done_reset_n; i += 64)
-        __hip_atomic_store(a.done_reset + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.progress && lane < kProgressReplicas)
-        __hip_atomic_store(a.progress + lane * 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
+      argmax_tiles(a, tile, (N + kTile - 1) / kTile, bv, bi, lane);
     }
   } else {
     // lanes 0..31: gate rows 32 tile + lane; lanes 32..63: the matching up rows
     const float u = __shfl(v, lane + 32, 64);
     const int i = tile * 32 + lane;
-    if (lane < 32 && i < N / 2) st_f<COH>(a.y + i, silu(v) * u);
+    if (lane < 32 && i < N / 2) a.y[i] = silu(v) * u;
   }
-  if (a.done) count_done(a.done, a.done_target, a.done_phase, a.progress, lane, a.phase_ts);
 }
 
 }  // namespace dev

@@ -22,7 +22,7 @@ struct SkPhase {
   int tiles, nch, nw, q, rem;
   int slots;                   // partial slots per tile (>= max contributors)
   float *part;                 // [tiles][slots][64] partial sums
-  unsigned *tile_cnt;          // [tiles] arrival counters, zero between uses
+  unsigned *tile_cnt;          // arrival counter of tile t at [t * kLine], zero between uses
 };
 
 struct FusedArgs {
@@ -52,13 +52,14 @@ struct FusedArgs {
   unsigned *down_done;         // [L]: down tiles finished
   unsigned *gu_flag;           // [L][tiles_gu] (packed): e + 1 once gate/up tile t is stored
   unsigned *progress;          // [kProgressReplicas lines]: e * (3L + 1) + phases completed
-  unsigned *attn_cnt;          // [Hkv] split arrivals (reset by the merger)
+  unsigned *attn_cnt;          // split arrivals of KV head j at [j * kLine] (reset by the merger)
   unsigned *lm_sub;            // [64 lines] argmax arrivals per tile group (reset by the last)
   unsigned *lm_top;            // argmax groups finished (reset by the last)
   float *cand;                 // [tiles_lm][2] per-tile (value, index)
   float *sub_cand;             // [64][2] per-group (value, index)
   unsigned *err;               // set when a bounded wait gives up
   unsigned long long *phase_ts;  // optional [2 + 5 L]: start, per-phase last finish, lm finish
+  unsigned *wave_ts;           // optional [5 L + 1][waves][4]: per-wave marks (low 32 bits of the clock)
   SkPhase p_qkv, p_o, p_gu, p_down, p_lm;
 };
 

@@ -39,30 +39,27 @@ struct GemvArgs {
   const float *bias;       // [N] or null
   const float *residual;   // [N] or null (may alias y)
   float *y;                // output
-  float *y2;               // optional second copy of y (plain stores; read after the kernel)
   float *ssq_out;          // if non-null: per-tile sum of y^2 over the tile's valid rows
   float *part;             // split-K partials [tiles][ks][64]
-  unsigned *counters;      // [tiles] arrival counters, zero between launches
+  unsigned *counters;      // arrival counters (one per 128-byte line), zero between launches
   int N, K, group;
   int ks, cps;             // k splits, chunks per split
   int epi;
-  // EPI_ARGMAX: per-tile (value, index) candidates [2 * tiles] and the step scalars
+  // EPI_ARGMAX: per-tile then per-group (value, index) candidates and the step scalars
   float *cand;
   int32_t *token, *pos, *token_log, *step_count;
   int log_len;
-  // persistent step only: tiles finished are counted in *done; the argmax finisher zeroes
-  // done_reset[0 .. done_reset_n) for the next step
-  unsigned *done;
-  unsigned done_target;    // tiles of this phase: the finisher that completes it publishes progress
-  unsigned done_phase;     // this phase's index; completion publishes progress = done_phase + 1
-  unsigned *progress;      // replicated "phases completed" value (kProgressReplicas lines)
-  unsigned long long *phase_ts;  // optional: completion time of each phase (100 MHz clock)
-  unsigned *done_reset;
-  int done_reset_n;
 };
-constexpr int kProgressReplicas = 64;  // one 128-byte line each: spreads the polling
-constexpr size_t kCounterBytes = 64 * 1024;  // GEMV arrival-counter region of a workspace
-constexpr int kArgmaxCounter = (int)(kCounterBytes / sizeof(unsigned)) - 1;
+// Device atomics to one cache line serialize (about 13 ns each on MI355X), so every arrival
+// counter sits on a 128-byte line of its own.
+constexpr int kLine = 32;                        // unsigned per 128-byte line
+constexpr size_t kCounterBytes = 256 * 1024;     // GEMV arrival-counter region of a workspace
+constexpr int kCounterLines = (int)(kCounterBytes / 128);
+constexpr int kArgGroups = 64;                   // argmax reduction groups (tile mod 64)
+constexpr int kArgGroupLine0 = kCounterLines - kArgGroups;
+constexpr int kArgTopLine = kArgGroupLine0 - 1;
+constexpr int kMaxSplitTiles = kArgTopLine;      // tiles 0 .. kMaxSplitTiles-1 own lines 0 ..
+constexpr int kProgressReplicas = 64;            // persistent step: one 128-byte line each
 
 struct GemvPlan {
   int tiles, nch, ks, cps, units, blocks;
@@ -79,7 +76,15 @@ hipError_t launch_pack_q4(const uint8_t *W, const uint16_t *S, int N, int K, int
 
 // ---------------------------------------------------------------------------------- attention
 struct AttnArgs {
-  const float *q;          // [Hq][D] (already rotated)
+  const float *q;          // [Hq][D] (already rotated); unused when qkv is set
+  // Step form: when qkv != null, q, k and v are read raw from the fused vector [(Hq + 2 Hkv) D];
+  // the kernel applies the optional per-head q/k RMSNorm (g_q, g_k, eps) and RoPE from rope_cs
+  // ([D/2] fp64 (cos, sin) pairs of the angle pos * theta_i), appends the rotated k and v at pos,
+  // and uses them for the newest token.
+  const float *qkv;
+  const float *g_q, *g_k;
+  float eps;
+  const double *rope_cs;
   void *k_pool, *v_pool;
   int kv_fmt;
   const int32_t *page_table;
@@ -89,11 +94,11 @@ struct AttnArgs {
   float scale_log2;        // sm_scale * log2(e)
   int splits;              // <= kMaxMergeSplits
   float *ws;               // [splits][Hq][D + 2] partials
-  unsigned *counters;      // [Hkv] arrival counters, zero between launches
+  unsigned *counters;      // arrival counter of KV head j at [j * kLine], zero between launches
   float *out;              // [Hq][D]
 };
 constexpr int kMaxMergeSplits = 256;
-constexpr size_t kAttnCounterBytes = 256;  // counters of up to 64 KV heads
+constexpr size_t kAttnCounterBytes = 64 * 128;  // one line per KV head, up to 64 KV heads
 size_t attn_workspace_bytes(int Hq, int D, int splits);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
 
@@ -122,9 +127,11 @@ hipError_t launch_qkv_post(const QkvPostArgs &a, hipStream_t st);
 hipError_t launch_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
                                float eps, float rope_base, const int32_t *pos, hipStream_t st);
 hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStream_t st);
-// h = bf16 -> fp32 row E[*token] (E null: h is given), ssq[t] = sum of h^2 over rows 64t..64t+63
+// h = bf16 -> fp32 row E[*token] (E null: h is given), ssq[t] = sum of h^2 over rows 64t..64t+63.
+// With rope_cs != null it also writes the RoPE table of *pos: rope_cs[2i], rope_cs[2i+1] =
+// cos, sin of pos * base^(-2i/D) in fp64, i < D/2.
 hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
-                        hipStream_t st);
+                        const int32_t *pos, float rope_base, int D, double *rope_cs, hipStream_t st);
 // argmax over logits; writes *token, token_log[*step_count] (if log), advances *pos and
 // *step_count.  With logits == null it only advances *pos.
 hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int32_t *pos,

@@ -26,6 +26,7 @@ struct qdec_step {
   qdec_state state;
   // workspace carve-up
   float *qkv = nullptr, *attn = nullptr, *mlp = nullptr, *ssq = nullptr, *attn_ws = nullptr;
+  double *rope_cs = nullptr;  // this step's RoPE (cos, sin) table, written by the embed kernel
   void *gemv_ws = nullptr;
   qdec::GemvPlan p_qkv, p_o, p_gu, p_down, p_lm;
   int ssq_n = 0;
@@ -46,7 +47,7 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, gemv_ws, fused_layers, err, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, fused_layers, err, total;
   // persistent step
   size_t hB, xa, xb, ssqA, ssqB, sync, gu_flag, tile_cnt, cand, sub_cand, part[5];
   size_t part_bytes[5];
@@ -114,6 +115,7 @@ Layout layout_of(const qdec_config &c) {
   L.mlp = off; off += align256((size_t)c.inter * 4);
   L.ssq = off; off += align256((size_t)((c.hidden + 63) / 64) * 4);
   L.attn_ws = off; off += align256(attn_workspace_bytes(c.n_heads, c.head_dim, c.num_splits));
+  L.rope_cs = off; off += align256((size_t)c.head_dim * sizeof(double));
   size_t g = gemv_workspace_bytes(c.wfmt, nqkv, c.hidden);
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, qd));
   g = std::max(g, gemv_workspace_bytes(c.wfmt, 2 * c.inter, c.hidden));
@@ -142,7 +144,7 @@ Layout layout_of(const qdec_config &c) {
     L.part_bytes[i] = p.slots > 1 ? (size_t)L.tiles[i] * p.slots * kTile * 4 : 0;
   }
   L.gu_flag = off; off += align256((size_t)c.n_layers * L.tiles[2] * 4);
-  L.tile_cnt = off; off += align256(ntiles * 4);
+  L.tile_cnt = off; off += align256(ntiles * 128);
   L.cand = off; off += align256((size_t)L.tiles[4] * 8);
   L.sub_cand = off; off += align256(64 * 8);
   for (int i = 0; i < 5; ++i) {
@@ -170,7 +172,7 @@ qdec_status validate(const qdec_config *c) {
                "qdec_step: page_size must be 16 and n_pages >= 1");
   QDEC_REQUIRE(c->num_splits >= 1 && c->num_splits <= kMaxMergeSplits, QDEC_EINVAL,
                "qdec_step: num_splits in [1, %d]", kMaxMergeSplits);
-  QDEC_REQUIRE(c->n_kv_heads <= (int)(kAttnCounterBytes / 4), QDEC_EUNSUPPORTED, "qdec_step: too many KV heads");
+  QDEC_REQUIRE(c->n_kv_heads <= (int)(kAttnCounterBytes / 128), QDEC_EUNSUPPORTED, "qdec_step: too many KV heads");
   QDEC_REQUIRE(c->inter % 32 == 0, QDEC_EUNSUPPORTED, "qdec_step: inter must be a multiple of 32");
   const int qd = c->n_heads * c->head_dim;
   if (c->wfmt == QDEC_W_Q8_ROW) {
@@ -222,7 +224,8 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
   const int qd = Hq * D, nqkv = (Hq + 2 * Hkv) * D;
   const int wf = c.wfmt;
   int n = 0;
-  QDEC_CK(launch_embed(h->model.embed, s.token, H, c.vocab, s.hidden, h->ssq, st));
+  QDEC_CK(launch_embed(h->model.embed, s.token, H, c.vocab, s.hidden, h->ssq, s.pos, c.rope_base, D, h->rope_cs,
+                       st));
   if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace, H, st));
   for (int l = 0; l < c.n_layers; ++l) {
     const qdec_layer_weights &w = h->layers[l];
@@ -231,24 +234,13 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
     a.gamma = w.g_attn;
     a.bias = c.has_qkv_bias ? w.b_qkv : nullptr;
     QDEC_CK(launch_gemv(wf, a, h->p_qkv, st));
-    QkvPostArgs qp{};
-    qp.qkv = h->qkv;
-    qp.g_q = c.has_qk_norm ? w.g_q : nullptr;
-    qp.g_k = c.has_qk_norm ? w.g_k : nullptr;
-    qp.eps = c.rms_eps;
-    qp.rope_base = c.rope_base;
-    qp.pos = s.pos;
-    qp.Hq = Hq;
-    qp.Hkv = Hkv;
-    qp.D = D;
-    qp.k_pool = h->kpools[l];
-    qp.v_pool = h->vpools[l];
-    qp.kv_fmt = c.kv_fmt;
-    qp.page_table = s.page_table;
-    qp.n_pages = c.n_pages;
-    QDEC_CK(launch_qkv_post(qp, st));
+    // attention takes q, k, v raw: it applies the q/k norm and RoPE and appends k, v itself
     AttnArgs at{};
-    at.q = h->qkv;
+    at.qkv = h->qkv;
+    at.g_q = c.has_qk_norm ? w.g_q : nullptr;
+    at.g_k = c.has_qk_norm ? w.g_k : nullptr;
+    at.eps = c.rms_eps;
+    at.rope_cs = h->rope_cs;
     at.k_pool = h->kpools[l];
     at.v_pool = h->vpools[l];
     at.kv_fmt = c.kv_fmt;
@@ -378,7 +370,7 @@ qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
     if (p.slots > 1 && (size_t)L.tiles[i] * p.slots * kTile * 4 > L.part_bytes[i]) return QDEC_OK;
     p.part = reinterpret_cast<float *>(ws + L.part[i]);
     p.tile_cnt = tc;
-    tc += L.tiles[i];
+    tc += (size_t)L.tiles[i] * kLine;
     *ph[i] = p;
   }
   h->fused_ok = true;
@@ -441,6 +433,7 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   h->mlp = reinterpret_cast<float *>(ws + L.mlp);
   h->ssq = reinterpret_cast<float *>(ws + L.ssq);
   h->attn_ws = reinterpret_cast<float *>(ws + L.attn_ws);
+  h->rope_cs = reinterpret_cast<double *>(ws + L.rope_cs);
   h->gemv_ws = ws + L.gemv_ws;
   h->ssq_n = (cfg->hidden + 63) / 64;
   const int qd = cfg->n_heads * cfg->head_dim;
@@ -527,6 +520,14 @@ qdec_status qdec_step_phase_times(qdec_step *h, uint64_t *ts) {
   h->fa.phase_ts = reinterpret_cast<unsigned long long *>(ts);
   return QDEC_OK;
 }
+
+qdec_status qdec_step_wave_times(qdec_step *h, uint32_t *ts) {
+  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_wave_times: null handle");
+  h->fa.wave_ts = reinterpret_cast<unsigned *>(ts);
+  return QDEC_OK;
+}
+
+int qdec_step_fused_waves(const qdec_step *h) { return h && h->fused_ok ? h->fused_blocks * 4 : 0; }
 
 qdec_status qdec_step_read_error(qdec_step *h, int *flag) {
   QDEC_REQUIRE(h && flag, QDEC_EINVAL, "qdec_step_read_error: null argument");

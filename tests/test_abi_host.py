@@ -52,7 +52,7 @@ def test_packed_sizes(L):
 
 
 def test_workspace_sizes(L):
-    assert L.qdec_attn_workspace_bytes(28, 128, 64) == 256 + 64 * 28 * 130 * 4
+    assert L.qdec_attn_workspace_bytes(28, 128, 64) == 8192 + 64 * 28 * 130 * 4
     assert L.qdec_attn_workspace_bytes(0, 128, 64) == 0
     assert L.qdec_gemv_workspace_bytes(q.W_Q4, 4608, 3584) > 0
     assert L.qdec_gemv_workspace_bytes(9, 4608, 3584) == 0

@@ -325,16 +325,16 @@ def upload_kv(kv: dict, kv_fmt: str, device="cuda") -> dict:
 
 
 def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 1) -> int:
-    """Attention split count: about `pages_per_wave` KV pages for each of a split's 4 waves (pages
-    are dealt round-robin over all waves of a KV head), at most 256 splits (the merge folds them in
-    one workgroup).  Above 32 splits a small excess over a multiple of 32 is dropped: the merge
-    reads 32 splits' partials per pass, so 65 splits cost a third pass for one split's worth of
-    pages."""
+    """Attention split count: about `pages_per_wave` KV pages for each of a split's 8 waves (pages
+    are dealt round-robin over all waves of a KV head), at most 64 splits: the merge reads 32
+    splits' partials per pass, so past that a longer context gives each wave more pages instead.
+    Just above a multiple of 32 it rounds down (33 splits would cost a second pass for one
+    split's worth of pages)."""
     pages = max(1, -(-(ctx + 1) // PAGE))
-    s = -(-pages // (4 * pages_per_wave))
+    s = -(-pages // (8 * pages_per_wave))
     if s > 32 and s % 32 <= (s // 32) * 8:
         s -= s % 32
-    return int(max(1, min(s, 256)))
+    return int(max(1, min(s, 64)))
 
 
 # ----------------------------------------------------------------------------- decode step

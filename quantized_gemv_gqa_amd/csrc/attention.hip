@@ -9,7 +9,7 @@
 // workgroup, and a second pass merges the partial (max, sum, output) triples (FlashQwen README,
 // "Optimization study", stage 7).
 //
-// How, on CDNA4: a workgroup (4 waves) owns one (KV head, split) pair and serves all G query
+// How, on CDNA4: a workgroup (8 waves) owns one (KV head, split) pair and serves all G query
 // heads of that KV head from registers, so each KV byte is read from HBM once per KV head.  In a
 // wave, lane = (slot g = lane / 16, part i = lane % 16): the 16 lanes of a slot read one token's
 // row (16 B each for bf16 at D = 128), four slots cover four tokens per load instruction, and a
@@ -105,12 +105,12 @@ __device__ __forceinline__ void attend_page(Row<D, KVF> (&kp)[4], Row<D, KVF> (&
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
-    const float alpha = exp2f(m[h] - mx);
+    const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
     m[h] = mx;
     float ls = 0.f;
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      sc[sub][h] = exp2f(sc[sub][h] - mx);
+      sc[sub][h] = __builtin_amdgcn_exp2f(sc[sub][h] - mx);
       ls += sc[sub][h];
     }
     l[h] = fmaf(l[h], alpha, ls);
@@ -158,19 +158,28 @@ __device__ __forceinline__ void norm_rope(float (&own)[D / 16], float (&mate)[D 
   }
 }
 
-constexpr int kMergeChunk = 32;  // splits whose partial outputs one merge pass loads at once
+constexpr int kAttnWaves = 8;                  // waves per workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kMergeLoads = 16;                // partial outputs a merging thread loads per pass
+
+__device__ __forceinline__ void store_sc1_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAuxSc1);
+}
 
 // ROPE: q, k and v come raw from the fused qkv vector; the kernel applies the optional q/k
-// RMSNorm and RoPE itself, appends the new token's k and v (the split owning the last page), and
-// takes the newest key and value from registers.  Otherwise q is given rotated and the new
-// token's k and v were appended before the launch.
+// RMSNorm and RoPE itself, appends the new token's k and v (split 0), and takes the newest key
+// and value from registers.  Otherwise q is given rotated and the new token's k and v were
+// appended before the launch.
 template <int D, int G, int KVF, bool ROPE>
-__global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads) attn_split(AttnArgs a) {
   constexpr int DPL = D / 16;
   constexpr int EB = Row<D, KVF>::EB;
-  __shared__ float sm_m[4][G], sm_l[4][G], sm_o[4][G][D];
+  constexpr int NW = kAttnWaves;
+  constexpr int C = G * D / 4;                                                // f32x4 columns
+  constexpr int R = (kAttnThreads / C) < NW ? (kAttnThreads / C) : NW;        // merge threads per column
+  __shared__ float sm_m[NW][G], sm_l[NW][G];
+  __shared__ f32x4 sm_o[NW * C];  // per-wave partial outputs, then the merge's per-thread sums
   __shared__ float sw[kMaxMergeSplits][G], sl[kMaxMergeSplits][G];
-  __shared__ float sM[G], sL[G];
   __shared__ float sq[ROPE ? (G + 2) * D : 1];
   __shared__ unsigned last;
   const int lane = threadIdx.x & 63;
@@ -182,20 +191,22 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
   const int pos = *a.pos;
   const int T = pos + 1;
   const int P = min((T + 15) >> 4, a.n_pages);  // never index past the page table
-  // pages are dealt round-robin over all 4 * splits waves of the KV head: wave gw = 4 s + wave
+  // pages are dealt round-robin over all NW * splits waves of the KV head: wave gw = NW s + wave
   // takes pages gw, gw + nwt, gw + 2 nwt, ...
-  const int nwt = 4 * a.splits;
-  const int gw = 4 * s + wave;
+  const int nwt = NW * a.splits;
+  const int gw = NW * s + wave;
   const int last_page = ((T + 15) >> 4) - 1;
   const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
   const __amdgpu_buffer_rsrc_t kr = rsrc(a.k_pool, pool_bytes), vr = rsrc(a.v_pool, pool_bytes);
   const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
 
-  // the wave's first two pages are requested before anything else
-  Row<D, KVF> kp[2][4], vp[2][4];
-  bool have[2];
+  // the wave's first PF pages are requested before anything else (one for fp32 rows of 128,
+  // whose two pages would not fit the registers)
+  constexpr int PF = (KVF == QDEC_KV_F32 && D == 128) ? 1 : 2;
+  Row<D, KVF> kp[PF][4], vp[PF][4];
+  bool have[PF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < PF; ++i) {
     const int p = gw + nwt * i;
     have[i] = false;
     if (p < P) {
@@ -217,7 +228,7 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
   Row<D, KVF> knew, vnew;
   if constexpr (ROPE) {
     // stage this KV head's q heads and its new k, v (one pass), then norm + rotate per lane
-    for (int i = threadIdx.x; i < (G + 2) * D / 4; i += 256) {
+    for (int i = threadIdx.x; i < (G + 2) * D / 4; i += kAttnThreads) {
       const int h = (i * 4) / D, d = i * 4 - h * D;
       const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
       *reinterpret_cast<f32x4 *>(&sq[h * D + d]) = *reinterpret_cast<const f32x4 *>(a.qkv + (size_t)row * D + d);
@@ -288,9 +299,10 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
     }
     attend_page<D, G, KVF>(kq, vq, p, T, slot, q, m, l, o);
   };
-  if (have[0]) page(kp[0], vp[0], gw);
-  if (have[1]) page(kp[1], vp[1], gw + nwt);
-  for (int p = gw + 2 * nwt; p < P; p += nwt) {
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (have[i]) page(kp[i], vp[i], gw + nwt * i);
+  for (int p = gw + PF * nwt; p < P; p += nwt) {
     const int phys = a.page_table[p];
     if (phys < 0 || phys >= a.n_pages) continue;
     const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
@@ -303,29 +315,35 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
     page(kp[0], vp[0], p);
   }
 
-  // merge the four token slots of this wave (lanes part, part+16, part+32, part+48)
+  // merge the four token slots of this wave (lanes part, part+16, part+32, part+48): lane
+  // swaps give both lanes of a pair the same (first, second) states, so they agree exactly
+  auto merge_pairs = [&](auto pair) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float m2 = __shfl_xor(m[h], off, 64);
-      const float l2 = __shfl_xor(l[h], off, 64);
-      const float mx = fmaxf(m[h], m2);
-      const float a1 = exp2f(m[h] - mx), a2 = exp2f(m2 - mx);
-      l[h] = l[h] * a1 + l2 * a2;
+    for (int h = 0; h < G; ++h) {
+      float ma, mb, la, lb;
+      pair(m[h], ma, mb);
+      pair(l[h], la, lb);
+      const float mx = fmaxf(ma, mb);
+      const float a1 = __builtin_amdgcn_exp2f(ma - mx), a2 = __builtin_amdgcn_exp2f(mb - mx);
+      l[h] = la * a1 + lb * a2;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        const float o2 = __shfl_xor(o[h][e], off, 64);
-        o[h][e] = o[h][e] * a1 + o2 * a2;
+        float oa, ob;
+        pair(o[h][e], oa, ob);
+        o[h][e] = oa * a1 + ob * a2;
       }
       m[h] = mx;
     }
-  }
+  };
+  merge_pairs(pair16);
+  merge_pairs(pair32);
   if (slot == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) sm_o[wave][h][part * DPL + e] = o[h][e];
+      for (int e4 = 0; e4 < DPL / 4; ++e4)
+        sm_o[wave * C + (h * D + part * DPL) / 4 + e4] =
+            f32x4{o[h][4 * e4], o[h][4 * e4 + 1], o[h][4 * e4 + 2], o[h][4 * e4 + 3]};
       if (part == 0) {
         sm_m[wave][h] = m[h];
         sm_l[wave][h] = l[h];
@@ -333,31 +351,33 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
     }
   }
   __syncthreads();
-  // merge the four waves and publish the split's partial through device-coherent stores (the
+  // merge the NW waves and publish the split's partial through device-coherent stores (the
   // merging block may sit on another XCD): o at [s][head][D], (m, l) at [s][head][2]
   float *wso = a.ws;
   float *wsml = a.ws + (size_t)a.splits * a.Hq * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx - h * D;
+  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
+  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
+  for (int c = threadIdx.x; c < C; c += kAttnThreads) {
+    const int h = c / (D / 4);
     float mx = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float val = 0.f;
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    f32x4 val = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) val += exp2f(sm_m[w][h] - mx) * sm_o[w][h][d];
-    __hip_atomic_store(wso + ((size_t)s * a.Hq + j * G + h) * D + d, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < NW; ++w) val += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_o[w * C + c];
+    store_sc1_b128(orr, (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 4), val);
   }
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float mx = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
     float lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) lsum += exp2f(sm_m[w][h] - mx) * sm_l[w][h];
-    float *dst = wsml + ((size_t)s * a.Hq + j * G + h) * 2;
-    __hip_atomic_store(dst, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < NW; ++w) lsum += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_l[w][h];
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = {__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + h) * 2) * 4), 0, kAuxSc1);
   }
   drain_stores();  // this thread's partial stores are acknowledged
   __syncthreads();
@@ -369,46 +389,76 @@ __global__ void __launch_bounds__(256) attn_split(AttnArgs a) {
 
   // The last split block of KV head j merges all splits of its G query heads:
   //   out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.  Loads of a pass are all
-  // issued before use (one memory round trip per pass); the per-head max and sum are wave
-  // reductions.
-  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
-  for (int idx = threadIdx.x; idx < a.splits * G; idx += 256) {
-    const int ss = idx / G, h = idx - ss * G;
-    const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                           mlr, (uint32_t)(((size_t)ss * a.Hq + j * G + h) * 2 * 4), 0, kAuxSc1));
-    sw[ss][h] = __builtin_bit_cast(float, (uint32_t)v);
-    sl[ss][h] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.  Every (m, l) pair and
+  // the first kMergeLoads partial outputs of each thread are requested in one burst; thread
+  // (r, c) takes column c of splits r, r + R, r + 2R, ...; one wave per query head reduces the
+  // maxima and sums in LDS.
+  const int t = threadIdx.x;
+  const int cc = t % C, rr = t / C;
+  const bool mt = rr < R;
+  const int hc = cc / (D / 4);
+  const int nml = a.splits * G;
+  constexpr int kMlLoads = (kMaxMergeSplits * 8 + kAttnThreads - 1) / kAttnThreads;
+  uint64_t mlv[kMlLoads];
+#pragma unroll
+  for (int k = 0; k < kMlLoads; ++k) {
+    const int i = t + kAttnThreads * k;
+    const int ss = i / G, h = i - ss * G;
+    const uint32_t off = i < nml ? (uint32_t)((((size_t)ss * a.Hq + j * G + h) * 2) * 4) : 0x80000000u;
+    mlv[k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, off, 0, kAuxSc1));
+  }
+  f32x4 ov[kMergeLoads];
+  auto load_pass = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kMergeLoads; ++u) {
+      const int ss = s0 + rr + R * u;
+      const uint32_t off = (mt && ss < a.splits) ? (uint32_t)((((size_t)ss * a.Hq + j * G) * D + 4 * cc) * 4) : 0x80000000u;
+      ov[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kAuxSc1));
+    }
+  };
+  load_pass(0);
+#pragma unroll
+  for (int k = 0; k < kMlLoads; ++k) {
+    const int i = t + kAttnThreads * k;
+    if (i < nml) {
+      const int ss = i / G, h = i - ss * G;
+      sw[ss][h] = __builtin_bit_cast(float, (uint32_t)mlv[k]);
+      sl[ss][h] = __builtin_bit_cast(float, (uint32_t)(mlv[k] >> 32));
+    }
   }
   __syncthreads();
-  for (int h = wave; h < G; h += 4) {
+  if (wave < G) {
+    const int h = wave;
     float M = kNegBig;
     for (int ss = lane; ss < a.splits; ss += 64) M = fmaxf(M, sw[ss][h]);
-#pragma unroll
-    for (int o2 = 32; o2 >= 1; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2, 64));
+    M = wave_max(M);
     float L = 0.f;
-    for (int ss = lane; ss < a.splits; ss += 64) L = fmaf(exp2f(sw[ss][h] - M), sl[ss][h], L);
+    for (int ss = lane; ss < a.splits; ss += 64) L = fmaf(__builtin_amdgcn_exp2f(sw[ss][h] - M), sl[ss][h], L);
     L = wave_sum(L);
-    for (int ss = lane; ss < a.splits; ss += 64) sw[ss][h] = exp2f(sw[ss][h] - M) / L;
+    const float inv = 1.0f / L;
+    for (int ss = lane; ss < a.splits; ss += 64) sw[ss][h] = __builtin_amdgcn_exp2f(sw[ss][h] - M) * inv;
   }
   __syncthreads();
-  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
-  for (int t = threadIdx.x; t < G * D / 4; t += 256) {
-    const int h = t / (D / 4), d4 = (t - h * (D / 4)) * 4;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.splits; s0 += kMergeChunk) {
-      f32x4 v[kMergeChunk];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0;;) {
 #pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u)  // splits past the last lie outside the resource: 0
-        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                   orr, (uint32_t)((((size_t)(s0 + u) * a.Hq + j * G + h) * D + d4) * 4), 0, kAuxSc1));
-#pragma unroll
-      for (int u = 0; u < kMergeChunk; ++u)
-        if (s0 + u < a.splits) acc += sw[s0 + u][h] * v[u];
+    for (int u = 0; u < kMergeLoads; ++u) {
+      const int ss = s0 + rr + R * u;
+      if (mt && ss < a.splits) acc += sw[ss][hc] * ov[u];
     }
-    *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + h) * D + d4) = acc;
+    s0 += R * kMergeLoads;
+    if (s0 >= a.splits) break;
+    load_pass(s0);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (mt) sm_o[rr * C + cc] = acc;
+  __syncthreads();
+  if (t < C) {
+    f32x4 out = sm_o[t];
+#pragma unroll
+    for (int r = 1; r < R; ++r) out += sm_o[r * C + t];
+    *reinterpret_cast<f32x4 *>(a.out + (size_t)j * G * D + 4 * t) = out;
+  }
+  if (t == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void kv_append(const float *__restrict__ k, const float *__restrict__ v, void *k_pool,
@@ -433,13 +483,14 @@ __global__ void kv_append(const float *__restrict__ k, const float *__restrict__
 template <int D, int KVF>
 hipError_t launch_g(const AttnArgs &a, int G, hipStream_t st) {
   dim3 grid(a.Hkv, a.splits);
+  constexpr int kT = kAttnThreads;
   switch (G) {
 #define QDEC_G(g)                                                                         \
   case g:                                                                                 \
     if (a.qkv)                                                                            \
-      hipLaunchKernelGGL((attn_split<D, g, KVF, true>), grid, dim3(256), 0, st, a);       \
+      hipLaunchKernelGGL((attn_split<D, g, KVF, true>), grid, dim3(kT), 0, st, a);       \
     else                                                                                  \
-      hipLaunchKernelGGL((attn_split<D, g, KVF, false>), grid, dim3(256), 0, st, a);      \
+      hipLaunchKernelGGL((attn_split<D, g, KVF, false>), grid, dim3(kT), 0, st, a);      \
     break;
     QDEC_G(1) QDEC_G(2) QDEC_G(3) QDEC_G(4) QDEC_G(5) QDEC_G(6) QDEC_G(7) QDEC_G(8)
 #undef QDEC_G

@@ -27,12 +27,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // DPP lane permutation of a float (gfx9 dpp_ctrl encodings)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -50,6 +44,46 @@ __device__ __forceinline__ float sum16(float v) {
   v = sum8(v);
   v += dpp<0x140>(v);  // row_mirror: lane i <-> 15 - i within each 16
   return v;
+}
+
+// Whole-wave reductions without LDS: finish each 16-lane row with DPP, then fold rows with the
+// row broadcasts (lane 15 into row 1 and lane 47 into row 3, then lane 31 into rows 2 and 3), so
+// lane 63 holds the result; it is read back as a wave-uniform value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float v, float old) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  v += dpp_rows<0x142, 0xA>(v, 0.f);  // row_bcast:15
+  v += dpp_rows<0x143, 0xC>(v, 0.f);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  v = fmaxf(v, dpp_rows<0x142, 0xA>(v, -INFINITY));
+  v = fmaxf(v, dpp_rows<0x143, 0xC>(v, -INFINITY));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Exchange with the lane 16 (32) apart: every lane gets the pair (even-row value, odd-row value)
+// ((lower-half value, upper-half value)), in the same order on both lanes of a pair.
+__device__ __forceinline__ void pair16(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+  // (elements are copied out before the cast: a cast of r[1] itself reads element 0)
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void pair32(float v, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
 
 // The AND masks are kept opaque so the backend cannot fold them into per-nibble bit-field

@@ -32,13 +32,16 @@ namespace {
 
 using namespace dev;
 
-constexpr int kTargetUnits = 2048;  // ~8 waves per CU on 256 CUs
+// Waves a launch aims for: few k-splits keep the split-K tail short on small matrices (up to 128
+// tiles), more waves stream the large ones (measured on MI355X).
+constexpr int kTargetUnitsSmall = 1024;
+constexpr int kTargetUnitsLarge = 3072;
 constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
 
 // Standalone launch: one wave per (tile, k-split) unit, no cross-phase dependency.
 template <int FMT, bool NORM, int EPI>
 __global__ void __launch_bounds__(256) gemv_tile64(const GemvArgs a) {
-  __shared__ Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> stage_all[4];
+  __shared__ Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> stage_all[4][2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * 4 + wave;
@@ -116,7 +119,8 @@ GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split) {
   p.nch = K / ck;
   int ks = 1;
   if (allow_split && p.tiles <= kMaxSplitTiles) {
-    ks = (kTargetUnits + p.tiles / 2) / p.tiles;
+    const int target = p.tiles <= 128 ? kTargetUnitsSmall : kTargetUnitsLarge;
+    ks = (target + p.tiles / 2) / p.tiles;
     ks = max(1, min(ks, p.nch / kMinChunks));
   }
   p.cps = (p.nch + ks - 1) / ks;

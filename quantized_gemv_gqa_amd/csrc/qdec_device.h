@@ -174,6 +174,39 @@ __device__ __forceinline__ float dot_q4_run(u32x4 w, const f32x4 (&xs)[8]) {
   return a0 + a1;
 }
 
+// INT4 with mixed-precision FMAs: 2^-24 sum_k c_k x_k over the 32 codes of one 16-byte run, xs
+// holding the run's true activations in k order.  Masking a word with 0x000F000F leaves two codes
+// in the low bits of its 16-bit halves; read as fp16 bit patterns these are exact subnormals
+// c * 2^-24, and with 0x00F000F0 they are 16 c * 2^-24.  v_fma_mix_f32 multiplies such a half by
+// an fp32 activation in fp32, so eight codes cost four masks, one shift and eight FMAs (instead
+// of two masks, eight conversions and eight FMAs).  fp16 subnormals are kept: the kernels run in
+// the IEEE denormal mode for 16-bit values.
+__device__ __forceinline__ float lo_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFFu)); }
+__device__ __forceinline__ float hi_half(uint32_t m) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16)); }
+__device__ __forceinline__ float dot_q4_mix(u32x4 w, const f32x4 (&xs)[8]) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float a0 = 0.f, a1 = 0.f;  // a0: codes of even k (times 2^-24); a1: odd k (times 16 * 2^-24)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // byte b of word q holds k = 8q + 2b (low nibble) and 8q + 2b + 1 (high nibble)
+    const uint32_t v = wd[q], s = v >> 8;
+    const uint32_t e02 = and_opaque(v, 0x000F000Fu);  // k = 8q, 8q + 4
+    const uint32_t o02 = and_opaque(v, 0x00F000F0u);  // k = 8q + 1, 8q + 5
+    const uint32_t e13 = and_opaque(s, 0x000F000Fu);  // k = 8q + 2, 8q + 6
+    const uint32_t o13 = and_opaque(s, 0x00F000F0u);  // k = 8q + 3, 8q + 7
+    const f32x4 xa = xs[2 * q], xb = xs[2 * q + 1];   // k = 8q .. 8q+3, 8q+4 .. 8q+7
+    a0 = __builtin_fmaf(lo_half(e02), xa.x, a0);
+    a1 = __builtin_fmaf(lo_half(o02), xa.y, a1);
+    a0 = __builtin_fmaf(lo_half(e13), xa.z, a0);
+    a1 = __builtin_fmaf(lo_half(o13), xa.w, a1);
+    a0 = __builtin_fmaf(hi_half(e02), xb.x, a0);
+    a1 = __builtin_fmaf(hi_half(o02), xb.y, a1);
+    a0 = __builtin_fmaf(hi_half(e13), xb.z, a0);
+    a1 = __builtin_fmaf(hi_half(o13), xb.w, a1);
+  }
+  return __builtin_fmaf(a1, 0.0625f, a0);
+}
+
 // INT8: sum_k (c_k + 128) x_k over the 16 codes of one 16-byte run
 __device__ __forceinline__ float dot_q8_run(u32x4 w, const f32x4 (&xs)[4]) {
   const uint32_t wd[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
@@ -190,28 +223,57 @@ __device__ __forceinline__ float dot_q8_run(u32x4 w, const f32x4 (&xs)[4]) {
   return a0 + a1;
 }
 
-// Per-wave LDS staging of one batch of activations: up to kBatch runs of CK values (odd k / 16
-// for INT4) followed by the runs' sums of the true values.
+// One batch of a wave's work: kBatch 16-byte weight runs per lane, their scales (INT4), and the
+// batch's activations (kBatch * CK values, four per lane) with the RMSNorm gain.
+template <int FMT, bool NORM>
+struct GemvBatch {
+  u32x4 w[kBatch];
+  uint16_t s[kBatch];
+  f32x4 x, g;
+};
+
+// Per-wave LDS copy of a batch's activations and the runs' zero-point terms: 128 times the run's
+// sum for INT8, 8 * 2^-24 times it for INT4 (the scale of dot_q4_mix).
 template <int CK>
 struct Stage {
   float x[kBatch * CK];
-  float sum[kBatch];
+  float zp[kBatch];
 };
 
-// Stage NB runs starting at run c.  Lane l covers values 4l .. 4l+3 of the batch; CK/4 lanes
-// cover one run.
-template <int CK, int NB, bool NORM>
-__device__ __forceinline__ void stage_batch(Stage<CK> &sm, __amdgpu_buffer_rsrc_t xr,
-                                            __amdgpu_buffer_rsrc_t gr, int c, int lane) {
-  constexpr int LPR = CK / 4;  // lanes per run
-  const bool active = lane < NB * LPR;
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    const int soff = c * CK * 4;
-    v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, lane * 16, soff, 0));
-    if constexpr (NORM)
-      v *= __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, lane * 16, soff, 0));
+// Issue the loads of runs r .. r + kBatch - 1 (relative to the wave's first run).  The resources
+// cover exactly the wave's runs, scale groups and activations, so loads past its end read zero
+// (and contribute nothing); the whole offset is in the VGPR operand, which the range check uses.
+template <int FMT, bool NORM>
+__device__ __forceinline__ void load_batch(GemvBatch<FMT, NORM> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                           __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int r, int c0, int g0,
+                                           int gshift, int lane) {
+  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
+  constexpr int CK = Q4 ? 32 : 16;
+  const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) {
+    B.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, base + i * (kTile * 16), 0, kAuxStream));
+    if constexpr (Q4) {
+      const int g = ((c0 + r + i) >> gshift) - g0;
+      B.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, (uint32_t)g * (kTile * 2) + lane * 2, 0, 0);
+    }
   }
+  const uint32_t xo = (lane * 4 < kBatch * CK) ? (uint32_t)(r * CK + lane * 4) * 4u : 0x80000000u;
+  B.x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0));
+  if constexpr (NORM) B.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, xo, 0, 0));
+}
+
+// Stage a batch's activations in the wave's LDS slot, then accumulate its runs into acc (INT4:
+// times 2^-24).
+template <int FMT, bool NORM>
+__device__ __forceinline__ void compute_batch(float &acc, const GemvBatch<FMT, NORM> &B,
+                                              Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm, int lane) {
+  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
+  constexpr int CK = Q4 ? 32 : 16;
+  constexpr int LPR = CK / 4;  // lanes per run
+  constexpr int RV = CK / 4;
+  f32x4 v = B.x;
+  if constexpr (NORM) v *= B.g;
   float part = (v.x + v.y) + (v.z + v.w);
   if constexpr (LPR == 8) {
     part = sum8(part);
@@ -220,57 +282,25 @@ __device__ __forceinline__ void stage_batch(Stage<CK> &sm, __amdgpu_buffer_rsrc_
     part += dpp<0xB1>(part);
     part += dpp<0x4E>(part);
   }
-  if constexpr (CK == 32) {  // odd k carry 1/16 (exact power-of-two scaling)
-    v.y *= 0.0625f;
-    v.w *= 0.0625f;
-  }
-  if (active) {
+  if (lane * 4 < kBatch * CK) {
     *reinterpret_cast<f32x4 *>(&sm.x[4 * lane]) = v;
-    if (lane % LPR == 0) sm.sum[lane / LPR] = part;
+    if (lane % LPR == 0) sm.zp[lane / LPR] = part * (Q4 ? 4.76837158203125e-07f : 128.0f);  // 2^-21 (exact)
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int FMT>
-struct GemvBatchRegs {
-  u32x4 wv[kBatch];
-  uint16_t sraw[kBatch];
-};
-
-template <int FMT, int NB>
-__device__ __forceinline__ void load_batch(GemvBatchRegs<FMT> &r, __amdgpu_buffer_rsrc_t wr,
-                                           __amdgpu_buffer_rsrc_t sr, int cb, int gshift, int lane) {
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    r.wv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, lane * 16, (cb + i) * (kTile * 16), kAuxStream));
-    if constexpr (FMT == QDEC_W_Q4_G_ZP8)
-      r.sraw[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, lane * 2, ((cb + i) >> gshift) * (kTile * 2), 0);
-  }
-}
-
-template <int FMT, int NB>
-__device__ __forceinline__ void compute_batch(float &acc, const GemvBatchRegs<FMT> &r,
-                                              Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm) {
-  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
-  constexpr int CK = Q4 ? 32 : 16;
-  constexpr int RV = CK / 4;
-  constexpr float ZP = Q4 ? 8.0f : 128.0f;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int i = 0; i < kBatch; ++i) {
     f32x4 xs[RV];
 #pragma unroll
-    for (int v = 0; v < RV; ++v) xs[v] = *reinterpret_cast<const f32x4 *>(&sm.x[i * CK + 4 * v]);
-    const float xsum = sm.sum[i];
-    if constexpr (Q4) {
-      const float d = dot_q4_run(r.wv[i], xs);
-      acc = fmaf(half_bits_to_float(r.sraw[i]), d - ZP * xsum, acc);
-    } else {
-      acc += dot_q8_run(r.wv[i], xs) - ZP * xsum;
-    }
+    for (int q = 0; q < RV; ++q) xs[q] = *reinterpret_cast<const f32x4 *>(&sm.x[i * CK + 4 * q]);
+    const float zp = sm.zp[i];
+    if constexpr (Q4)
+      acc = fmaf(half_bits_to_float(B.s[i]), dot_q4_mix(B.w[i], xs) - zp, acc);
+    else
+      acc += dot_q8_run(B.w[i], xs) - zp;
   }
-  __builtin_amdgcn_wave_barrier();  // the next batch overwrites this wave's stage
+  __builtin_amdgcn_wave_barrier();  // the batch after next overwrites this slot
 }
 
 // Greedy token over the tiles of an lm-head GEMV: every tile posts its (max, row) candidate; the
@@ -343,10 +373,12 @@ __device__ __forceinline__ void argmax_tiles(const GemvArgs &a, int tile, int ti
 }
 
 // One GEMV work unit (64-row tile t, k-split s) executed by one wave of a standalone launch.
+//   * the wave streams its runs in batches of kBatch, one batch in flight while the previous
+//     one is computed;
 //   * split-K partials travel through device-coherent memory and the last wave of a tile adds
 //     them in a fixed order, then runs the epilogue.
 template <int FMT, bool NORM, int EPI>
-__device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> &sm, int lane) {
+__device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> (&sm)[2], int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;  // k per 16-byte run
   const int ks = a.ks, K = a.K, N = a.N;
@@ -355,45 +387,47 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
   const int nch = K / CK;
   const int c0 = ksi * a.cps;
   const int c1 = min(nch, c0 + a.cps);
+  const int nrun = c1 - c0;
   const int gshift = a.group;  // Q4: log2(group / 32), set by the launcher
-  const uint32_t tile_bytes = (uint32_t)nch * kTile * 16;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes, tile_bytes);
+  const size_t tile_bytes = (size_t)nch * kTile * 16;
+  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
   __amdgpu_buffer_rsrc_t sr = wr;
+  int g0 = 0;
   if constexpr (Q4) {
-    const uint32_t sbytes = (uint32_t)((nch >> gshift) * kTile * 2);
-    sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * sbytes, sbytes);
+    g0 = c0 >> gshift;
+    const int g1 = (c1 - 1) >> gshift;
+    sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
+              (uint32_t)(g1 - g0 + 1) * kTile * 2);
   }
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)K * 4);
-  const __amdgpu_buffer_rsrc_t gr = NORM ? rsrc(a.gamma, (uint32_t)K * 4) : xr;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x + (size_t)c0 * CK, (uint32_t)nrun * CK * 4);
+  const __amdgpu_buffer_rsrc_t gr = NORM ? rsrc(a.gamma + (size_t)c0 * CK, (uint32_t)nrun * CK * 4) : xr;
 
-  GemvBatchRegs<FMT> r;
+  // Software pipeline: batch b + 1 is in flight while batch b is staged and computed; past the
+  // last run the loads read zeros.
   float acc = 0.f;
-  int cb = c0;
-  const int n_full = (c1 - c0) / kBatch;
-  const int rem = (c1 - c0) - n_full * kBatch;
-  for (int b = 0; b < n_full; ++b) {
-    load_batch<FMT, kBatch>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, kBatch, NORM>(sm, xr, gr, cb, lane);
-    compute_batch<FMT, kBatch>(acc, r, sm);
-    cb += kBatch;
+  GemvBatch<FMT, NORM> A, B;
+  load_batch<FMT, NORM>(A, wr, sr, xr, gr, 0, c0, g0, gshift, lane);
+  // The epilogue's inputs (sums of squares, bias, residual, INT8 row scale) are fetched now, so
+  // the wave that finishes a tile does not wait on memory for them.
+  const int n = tile * kTile + lane;
+  const bool valid = n < N;
+  float pre_ssq = 0.f, pre_bias = 0.f, pre_res = 0.f, pre_scale = 1.f;
+  if constexpr (NORM)
+    for (int i = lane; i < a.ssq_n; i += 64) pre_ssq += a.ssq[i];
+  if (EPI != EPI_SWIGLU && valid) {
+    if (a.bias) pre_bias = a.bias[n];
+    if (a.residual) pre_res = a.residual[n];  // (y may alias it: only this tile's epilogue writes y[n])
   }
-  if (rem & 4) {
-    load_batch<FMT, 4>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 4, NORM>(sm, xr, gr, cb, lane);
-    compute_batch<FMT, 4>(acc, r, sm);
-    cb += 4;
+  if constexpr (FMT == QDEC_W_Q8_ROW) pre_scale = reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
+  const int nb = (nrun + kBatch - 1) / kBatch;
+  for (int b = 0; b < nb; b += 2) {
+    load_batch<FMT, NORM>(B, wr, sr, xr, gr, (b + 1) * kBatch, c0, g0, gshift, lane);
+    compute_batch<FMT, NORM>(acc, A, sm[0], lane);
+    if (b + 1 >= nb) break;
+    load_batch<FMT, NORM>(A, wr, sr, xr, gr, (b + 2) * kBatch, c0, g0, gshift, lane);
+    compute_batch<FMT, NORM>(acc, B, sm[1], lane);
   }
-  if (rem & 2) {
-    load_batch<FMT, 2>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 2, NORM>(sm, xr, gr, cb, lane);
-    compute_batch<FMT, 2>(acc, r, sm);
-    cb += 2;
-  }
-  if (rem & 1) {
-    load_batch<FMT, 1>(r, wr, sr, cb, gshift, lane);
-    stage_batch<CK, 1, NORM>(sm, xr, gr, cb, lane);
-    compute_batch<FMT, 1>(acc, r, sm);
-  }
+  if constexpr (Q4) acc *= 16777216.0f;  // 2^24, exact
 
   if (ks > 1) {
     // Split-K hand-off between waves that may sit on different XCDs: partials travel as sc1
@@ -428,19 +462,12 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
 
   // ------------------------------------------------------------------ epilogue (one tile)
   float v = acc;
-  if constexpr (NORM) {
-    float t = 0.f;
-    for (int i = lane; i < a.ssq_n; i += 64) t += a.ssq[i];
-    const float ms = wave_sum(t) / (float)K;
-    v *= rsqrtf(ms + a.eps);
-  }
-  const int n = tile * kTile + lane;
-  if constexpr (FMT == QDEC_W_Q8_ROW) v *= reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
+  if constexpr (NORM) v *= rsqrtf(wave_sum(pre_ssq) / (float)K + a.eps);
+  if constexpr (FMT == QDEC_W_Q8_ROW) v *= pre_scale;
   if constexpr (EPI == EPI_STORE || EPI == EPI_ARGMAX) {
-    const bool valid = n < N;
     if (valid) {
-      if (a.bias) v += a.bias[n];
-      if (a.residual) v += a.residual[n];
+      if (a.bias) v += pre_bias;
+      if (a.residual) v += pre_res;
       a.y[n] = v;
     }
     if (EPI == EPI_STORE && a.ssq_out) {

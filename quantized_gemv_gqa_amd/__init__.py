@@ -24,6 +24,7 @@ QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EHIP, QDEC_ESTATE = 0, -1, -2, -3,
 W_Q8, W_Q4 = 1, 2
 KV_F32, KV_BF16 = 1, 2
 STEP_EAGER, STEP_GRAPH, STEP_FUSED = 0, 1, 2
+STEP_PER_OP = 4  # flag for EAGER / GRAPH: one launch per operation instead of two per layer
 PAGE = 16
 TILE = 64
 

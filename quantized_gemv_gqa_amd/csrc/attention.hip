@@ -22,7 +22,7 @@
 
 #include <cmath>
 
-#include "qdec_device.h"
+#include "qdec_attention.h"
 
 namespace qdec {
 
@@ -30,435 +30,10 @@ namespace {
 
 using namespace dev;
 
-// One lane's piece of a token row: DPL = D / 16 values, kept packed as W dwords until used.
-template <int D, int KVF>
-struct Row {
-  static constexpr int DPL = D / 16;
-  static constexpr int EB = KVF == QDEC_KV_BF16 ? 2 : 4;  // bytes per element
-  static constexpr int W = DPL * EB / 4;
-  uint32_t w[W];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (W == 2) {
-      // (a 64-bit load is read as one 64-bit integer: a two-lane vector view of it compiles to a
-      // single dword load)
-      const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-      w[0] = (uint32_t)v; w[1] = (uint32_t)(v >> 32);
-    } else {
-#pragma unroll
-      for (int c = 0; c < W / 4; ++c) {
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * c, 0, 0));
-        w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
-      }
-    }
-  }
-  __device__ __forceinline__ float get(int e) const {
-    if constexpr (KVF == QDEC_KV_BF16)
-      return __builtin_bit_cast(float, (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-    else
-      return __builtin_bit_cast(float, w[e]);
-  }
-  // the stored form of fp32 values: bf16 round-to-nearest-even, or the fp32 bits
-  __device__ __forceinline__ void set(const float (&v)[DPL]) {
-    if constexpr (KVF == QDEC_KV_BF16) {
-#pragma unroll
-      for (int i = 0; i < W; ++i)
-        w[i] = (uint32_t)float_to_bf16_rne(v[2 * i]) | ((uint32_t)float_to_bf16_rne(v[2 * i + 1]) << 16);
-    } else {
-#pragma unroll
-      for (int i = 0; i < W; ++i) w[i] = __builtin_bit_cast(uint32_t, v[i]);
-    }
-  }
-  __device__ __forceinline__ void store(void *pool, size_t elem) const {
-    uint32_t *d = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(pool) + elem * EB);
-#pragma unroll
-    for (int i = 0; i < W; ++i) d[i] = w[i];
-  }
-  __device__ __forceinline__ void clear() {
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = 0u;
-  }
-};
-
-// Online-softmax update of one wave with one 16-token page: token slot sub*4 + slot of the page
-// sits in this lane's kp[sub] / vp[sub]; tokens at or past T are masked.
-template <int D, int G, int KVF>
-__device__ __forceinline__ void attend_page(Row<D, KVF> (&kp)[4], Row<D, KVF> (&vp)[4], int p, int T, int slot,
-                                            const float (&q)[G][D / 16], float (&m)[G], float (&l)[G],
-                                            float (&o)[G][D / 16]) {
-  constexpr int DPL = D / 16;
-  float sc[4][G];
-#pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
-    const bool valid = p * 16 + sub * 4 + slot < T;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) d = fmaf(q[h][e], kp[sub].get(e), d);
-      d = sum16(d);
-      sc[sub][h] = valid ? d : -INFINITY;
-    }
-    // slots past the newest token may hold stale bits (even NaN): zero them, never multiply
-    // them by a zero weight
-    if (!valid) vp[sub].clear();
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mx = fmaxf(fmaxf(m[h], fmaxf(sc[0][h], sc[1][h])), fmaxf(sc[2][h], sc[3][h]));
-    const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
-    m[h] = mx;
-    float ls = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      sc[sub][h] = __builtin_amdgcn_exp2f(sc[sub][h] - mx);
-      ls += sc[sub][h];
-    }
-    l[h] = fmaf(l[h], alpha, ls);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
-  }
-#pragma unroll
-  for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float vv = vp[sub].get(e);
-#pragma unroll
-      for (int h = 0; h < G; ++h) o[h][e] = fmaf(sc[sub][h], vv, o[h][e]);
-    }
-}
-
-// Optional RMSNorm over the head (DPL dims per lane, 16 lanes) and RoPE rotation of one head
-// vector: `own` are the lane's dims, `mate` the dims D/2 away; cs holds the fp64 (cos, sin) of
-// the lane's DPL rotation pairs.
-template <int D>
-__device__ __forceinline__ void norm_rope(float (&own)[D / 16], float (&mate)[D / 16], int part, const float *gamma,
-                                          float eps, const double *cs) {
-  constexpr int DPL = D / 16, HALF = D / 2;
-  const int d0 = part * DPL;
-  const bool lo = d0 < HALF;
-  if (gamma) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) ss = fmaf(own[e], own[e], ss);
-    ss = sum16(ss);
-    const float r = rsqrtf(ss / (float)D + eps);
-    const int dm = lo ? d0 + HALF : d0 - HALF;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      own[e] = gamma[d0 + e] * (own[e] * r);
-      mate[e] = gamma[dm + e] * (mate[e] * r);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const double c = cs[2 * e], sn = cs[2 * e + 1];
-    const double x = own[e], y = mate[e];
-    // low half: x' = x c - y s (y = x[i + D/2]); high half: x' = x c + y s (y = x[i - D/2])
-    own[e] = (float)(lo ? (x * c - y * sn) : (x * c + y * sn));
-  }
-}
-
-constexpr int kAttnWaves = 8;                  // waves per workgroup
-constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kMergeLoads = 16;                // partial outputs a merging thread loads per pass
-
-__device__ __forceinline__ void store_sc1_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAuxSc1);
-}
-
-// ROPE: q, k and v come raw from the fused qkv vector; the kernel applies the optional q/k
-// RMSNorm and RoPE itself, appends the new token's k and v (split 0), and takes the newest key
-// and value from registers.  Otherwise q is given rotated and the new token's k and v were
-// appended before the launch.
 template <int D, int G, int KVF, bool ROPE>
-__global__ void __launch_bounds__(kAttnThreads) attn_split(AttnArgs a) {
-  constexpr int DPL = D / 16;
-  constexpr int EB = Row<D, KVF>::EB;
-  constexpr int NW = kAttnWaves;
-  constexpr int C = G * D / 4;                                                // f32x4 columns
-  constexpr int R = (kAttnThreads / C) < NW ? (kAttnThreads / C) : NW;        // merge threads per column
-  __shared__ float sm_m[NW][G], sm_l[NW][G];
-  __shared__ f32x4 sm_o[NW * C];  // per-wave partial outputs, then the merge's per-thread sums
-  __shared__ float sw[kMaxMergeSplits][G], sl[kMaxMergeSplits][G];
-  __shared__ float sq[ROPE ? (G + 2) * D : 1];
-  __shared__ unsigned last;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = lane >> 4;
-  const int part = lane & 15;
-  const int j = blockIdx.x;
-  const int s = blockIdx.y;
-  const int pos = *a.pos;
-  const int T = pos + 1;
-  const int P = min((T + 15) >> 4, a.n_pages);  // never index past the page table
-  // pages are dealt round-robin over all NW * splits waves of the KV head: wave gw = NW s + wave
-  // takes pages gw, gw + nwt, gw + 2 nwt, ...
-  const int nwt = NW * a.splits;
-  const int gw = NW * s + wave;
-  const int last_page = ((T + 15) >> 4) - 1;
-  const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
-  const __amdgpu_buffer_rsrc_t kr = rsrc(a.k_pool, pool_bytes), vr = rsrc(a.v_pool, pool_bytes);
-  const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
-
-  // the wave's first PF pages are requested before anything else (one for fp32 rows of 128,
-  // whose two pages would not fit the registers)
-  constexpr int PF = (KVF == QDEC_KV_F32 && D == 128) ? 1 : 2;
-  Row<D, KVF> kp[PF][4], vp[PF][4];
-  bool have[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int p = gw + nwt * i;
-    have[i] = false;
-    if (p < P) {
-      const int phys = a.page_table[p];
-      if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
-        have[i] = true;
-        const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-          const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
-          kp[i][sub].load(kr, off);
-          vp[i][sub].load(vr, off);
-        }
-      }
-    }
-  }
-
-  float q[G][DPL];
-  Row<D, KVF> knew, vnew;
-  if constexpr (ROPE) {
-    // stage this KV head's q heads and its new k, v (one pass), then norm + rotate per lane
-    for (int i = threadIdx.x; i < (G + 2) * D / 4; i += kAttnThreads) {
-      const int h = (i * 4) / D, d = i * 4 - h * D;
-      const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
-      *reinterpret_cast<f32x4 *>(&sq[h * D + d]) = *reinterpret_cast<const f32x4 *>(a.qkv + (size_t)row * D + d);
-    }
-    double cs[2 * DPL];
-    {
-      const int i0 = (part * DPL) % (D / 2);
-#pragma unroll
-      for (int e = 0; e < 2 * DPL; ++e) cs[e] = a.rope_cs[2 * i0 + e];
-    }
-    __syncthreads();
-    const int dmate = part * DPL < D / 2 ? part * DPL + D / 2 : part * DPL - D / 2;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float own[DPL], mate[DPL];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        own[e] = sq[h * D + part * DPL + e];
-        mate[e] = sq[h * D + dmate + e];
-      }
-      norm_rope<D>(own, mate, part, a.g_q, a.eps, cs);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) q[h][e] = own[e] * a.scale_log2;
-    }
-    float own[DPL], mate[DPL], vv[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      own[e] = sq[G * D + part * DPL + e];
-      mate[e] = sq[G * D + dmate + e];
-      vv[e] = sq[(G + 1) * D + part * DPL + e];
-    }
-    norm_rope<D>(own, mate, part, a.g_k, a.eps, cs);
-    knew.set(own);
-    vnew.set(vv);
-    // split 0 appends them for later steps (every split uses the register copy for this token)
-    if (s == 0 && wave == 0 && slot == 0 && last_page < a.n_pages) {
-      const int phys = a.page_table[last_page];
-      if (phys >= 0 && phys < a.n_pages) {
-        const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (pos & 15)) * D + part * DPL;
-        knew.store(a.k_pool, e0);
-        vnew.store(a.v_pool, e0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) q[h][e] = a.q[(size_t)(j * G + h) * D + part * DPL + e] * a.scale_log2;
-  }
-  const int new_sub = (pos & 15) >> 2, new_slot = pos & 3;
-
-  float m[G], l[G], o[G][DPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
-  }
-  auto page = [&](Row<D, KVF> (&kq)[4], Row<D, KVF> (&vq)[4], int p) {
-    if (ROPE && p == last_page) {  // the newest token's row comes from registers
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-        if (sub == new_sub && slot == new_slot) {
-          kq[sub] = knew;
-          vq[sub] = vnew;
-        }
-    }
-    attend_page<D, G, KVF>(kq, vq, p, T, slot, q, m, l, o);
-  };
-#pragma unroll
-  for (int i = 0; i < PF; ++i)
-    if (have[i]) page(kp[i], vp[i], gw + nwt * i);
-  for (int p = gw + PF * nwt; p < P; p += nwt) {
-    const int phys = a.page_table[p];
-    if (phys < 0 || phys >= a.n_pages) continue;
-    const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
-      kp[0][sub].load(kr, off);
-      vp[0][sub].load(vr, off);
-    }
-    page(kp[0], vp[0], p);
-  }
-
-  // merge the four token slots of this wave (lanes part, part+16, part+32, part+48): lane
-  // swaps give both lanes of a pair the same (first, second) states, so they agree exactly
-  auto merge_pairs = [&](auto pair) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ma, mb, la, lb;
-      pair(m[h], ma, mb);
-      pair(l[h], la, lb);
-      const float mx = fmaxf(ma, mb);
-      const float a1 = __builtin_amdgcn_exp2f(ma - mx), a2 = __builtin_amdgcn_exp2f(mb - mx);
-      l[h] = la * a1 + lb * a2;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        float oa, ob;
-        pair(o[h][e], oa, ob);
-        o[h][e] = oa * a1 + ob * a2;
-      }
-      m[h] = mx;
-    }
-  };
-  merge_pairs(pair16);
-  merge_pairs(pair32);
-  if (slot == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e4 = 0; e4 < DPL / 4; ++e4)
-        sm_o[wave * C + (h * D + part * DPL) / 4 + e4] =
-            f32x4{o[h][4 * e4], o[h][4 * e4 + 1], o[h][4 * e4 + 2], o[h][4 * e4 + 3]};
-      if (part == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
-    }
-  }
-  __syncthreads();
-  // merge the NW waves and publish the split's partial through device-coherent stores (the
-  // merging block may sit on another XCD): o at [s][head][D], (m, l) at [s][head][2]
-  float *wso = a.ws;
-  float *wsml = a.ws + (size_t)a.splits * a.Hq * D;
-  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
-  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
-  for (int c = threadIdx.x; c < C; c += kAttnThreads) {
-    const int h = c / (D / 4);
-    float mx = kNegBig;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    f32x4 val = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) val += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_o[w * C + c];
-    store_sc1_b128(orr, (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 4), val);
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float mx = kNegBig;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) lsum += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_l[w][h];
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = {__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)};
-    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + h) * 2) * 4), 0, kAuxSc1);
-  }
-  drain_stores();  // this thread's partial stores are acknowledged
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(&a.counters[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           (unsigned)(a.splits - 1);
-  __syncthreads();
-  if (!last) return;
-
-  // The last split block of KV head j merges all splits of its G query heads:
-  //   out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.  Every (m, l) pair and
-  // the first kMergeLoads partial outputs of each thread are requested in one burst; thread
-  // (r, c) takes column c of splits r, r + R, r + 2R, ...; one wave per query head reduces the
-  // maxima and sums in LDS.
-  const int t = threadIdx.x;
-  const int cc = t % C, rr = t / C;
-  const bool mt = rr < R;
-  const int hc = cc / (D / 4);
-  const int nml = a.splits * G;
-  constexpr int kMlLoads = (kMaxMergeSplits * 8 + kAttnThreads - 1) / kAttnThreads;
-  uint64_t mlv[kMlLoads];
-#pragma unroll
-  for (int k = 0; k < kMlLoads; ++k) {
-    const int i = t + kAttnThreads * k;
-    const int ss = i / G, h = i - ss * G;
-    const uint32_t off = i < nml ? (uint32_t)((((size_t)ss * a.Hq + j * G + h) * 2) * 4) : 0x80000000u;
-    mlv[k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, off, 0, kAuxSc1));
-  }
-  f32x4 ov[kMergeLoads];
-  auto load_pass = [&](int s0) {
-#pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) {
-      const int ss = s0 + rr + R * u;
-      const uint32_t off = (mt && ss < a.splits) ? (uint32_t)((((size_t)ss * a.Hq + j * G) * D + 4 * cc) * 4) : 0x80000000u;
-      ov[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kAuxSc1));
-    }
-  };
-  load_pass(0);
-#pragma unroll
-  for (int k = 0; k < kMlLoads; ++k) {
-    const int i = t + kAttnThreads * k;
-    if (i < nml) {
-      const int ss = i / G, h = i - ss * G;
-      sw[ss][h] = __builtin_bit_cast(float, (uint32_t)mlv[k]);
-      sl[ss][h] = __builtin_bit_cast(float, (uint32_t)(mlv[k] >> 32));
-    }
-  }
-  __syncthreads();
-  if (wave < G) {
-    const int h = wave;
-    float M = kNegBig;
-    for (int ss = lane; ss < a.splits; ss += 64) M = fmaxf(M, sw[ss][h]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int ss = lane; ss < a.splits; ss += 64) L = fmaf(__builtin_amdgcn_exp2f(sw[ss][h] - M), sl[ss][h], L);
-    L = wave_sum(L);
-    const float inv = 1.0f / L;
-    for (int ss = lane; ss < a.splits; ss += 64) sw[ss][h] = __builtin_amdgcn_exp2f(sw[ss][h] - M) * inv;
-  }
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0;;) {
-#pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) {
-      const int ss = s0 + rr + R * u;
-      if (mt && ss < a.splits) acc += sw[ss][hc] * ov[u];
-    }
-    s0 += R * kMergeLoads;
-    if (s0 >= a.splits) break;
-    load_pass(s0);
-  }
-  if (mt) sm_o[rr * C + cc] = acc;
-  __syncthreads();
-  if (t < C) {
-    f32x4 out = sm_o[t];
-#pragma unroll
-    for (int r = 1; r < R; ++r) out += sm_o[r * C + t];
-    *reinterpret_cast<f32x4 *>(a.out + (size_t)j * G * D + 4 * t) = out;
-  }
-  if (t == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__global__ void __launch_bounds__(attn::kAttnThreads) attn_split(AttnArgs a) {
+  __shared__ attn::AttnSmem<D, G, ROPE> sm;
+  attn::attn_unit<D, G, KVF, ROPE, false>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 __global__ void kv_append(const float *__restrict__ k, const float *__restrict__ v, void *k_pool,
@@ -483,7 +58,7 @@ __global__ void kv_append(const float *__restrict__ k, const float *__restrict__
 template <int D, int KVF>
 hipError_t launch_g(const AttnArgs &a, int G, hipStream_t st) {
   dim3 grid(a.Hkv, a.splits);
-  constexpr int kT = kAttnThreads;
+  constexpr int kT = attn::kAttnThreads;
   switch (G) {
 #define QDEC_G(g)                                                                         \
   case g:                                                                                 \

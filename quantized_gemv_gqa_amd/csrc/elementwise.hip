@@ -143,8 +143,9 @@ __global__ void swiglu_k(const float *__restrict__ g, const float *__restrict__ 
 __global__ void __launch_bounds__(64) embed_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ token,
                                               int H, int V, float *h, float *__restrict__ ssq,
                                               const int32_t *__restrict__ pos, float base, int D,
-                                              double *__restrict__ cs) {
+                                              double *__restrict__ cs, unsigned *epoch) {
   const int i = blockIdx.x * 64 + threadIdx.x;
+  if (epoch && blockIdx.x == 0 && threadIdx.x == 0) *epoch += 1u;
   if (cs && blockIdx.x == 0) {
     // same angle as the per-row rotation above: theta_i = base^(-2i/D), phi = pos * theta_i
     const int t = *pos;
@@ -252,9 +253,10 @@ hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStr
 }
 
 hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
-                        const int32_t *pos, float rope_base, int D, double *rope_cs, hipStream_t st) {
+                        const int32_t *pos, float rope_base, int D, double *rope_cs, unsigned *epoch,
+                        hipStream_t st) {
   hipLaunchKernelGGL(embed_k, dim3((H + 63) / 64), dim3(64), 0, st, E, token, H, V, h, ssq, pos, rope_base,
-                     D, rope_cs);
+                     D, rope_cs, epoch);
   return hipGetLastError();
 }
 

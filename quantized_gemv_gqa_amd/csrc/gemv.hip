@@ -91,12 +91,7 @@ __global__ void pack_scales_q8(const float *__restrict__ S, int N, int Npad, flo
 template <int FMT, bool NORM, int EPI>
 hipError_t launch_t(const GemvArgs &a0, const GemvPlan &p, hipStream_t st) {
   GemvArgs a = a0;
-  a.ks = p.ks;
-  a.cps = p.cps;
-  int gshift = 0;
-  if (FMT == QDEC_W_Q4_G_ZP8)
-    while ((32 << gshift) < a0.group) ++gshift;  // group = 32 << gshift (checked by the callers)
-  a.group = gshift;
+  gemv_apply_plan(a, p, FMT);
   hipLaunchKernelGGL((gemv_tile64<FMT, NORM, EPI>), dim3(p.blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -111,6 +106,15 @@ hipError_t launch_e(const GemvArgs &a, const GemvPlan &p, hipStream_t st) {
 }
 
 }  // namespace
+
+void gemv_apply_plan(GemvArgs &a, const GemvPlan &p, int wfmt) {
+  a.ks = p.ks;
+  a.cps = p.cps;
+  int gshift = 0;
+  if (wfmt == QDEC_W_Q4_G_ZP8)
+    while ((32 << gshift) < a.group) ++gshift;  // group = 32 << gshift (checked by the callers)
+  a.group = gshift;
+}
 
 GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split) {
   GemvPlan p;

@@ -17,6 +17,7 @@ constexpr int kBatch = 8;       // 16-byte weight runs a lane loads before compu
 constexpr int kAuxStream = 2;   // nt: weights are read once per step, do not keep them in L2
 constexpr int kAuxSc1 = 16;     // sc1: device-coherent access (bypasses non-coherent L2 copies)
 constexpr unsigned kSpinLimit = 1u << 24;  // bounded waits: ~1 s of polling, then give up
+constexpr unsigned kLayerSpinLimit = 1u << 22;  // backed-off polls of the layer kernels: ~3.5 s
 constexpr float kNegBig = -1e30f;          // finite "minus infinity" for running maxima
 
 // ------------------------------------------------------------------------------ small helpers
@@ -145,6 +146,61 @@ __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Bounded device-coherent polls for the step-synchronised kernels.  A wait that exceeds
+// kLayerSpinLimit polls (about 3.5 s) sets *err and gives up; once *err is set every other wait gives up within 1024
+// polls, so a failed step ends (with wrong values and the error word set) instead of hanging.
+__device__ __forceinline__ bool ge_u32(unsigned v, unsigned target) { return (int)(v - target) >= 0; }
+
+// Polls back off from ~25 ns to ~0.85 us between reads: a waiting wave's device-coherent reads
+// go past the L2, and hundreds of waves polling at full rate take memory bandwidth from the
+// producers they wait for.
+__device__ __forceinline__ void poll_pause(unsigned spins) {
+  if (spins < 8)
+    __builtin_amdgcn_s_sleep(1);
+  else if (spins < 32)
+    __builtin_amdgcn_s_sleep(4);
+  else
+    __builtin_amdgcn_s_sleep(32);
+}
+
+// one thread: *p >= target
+__device__ inline bool poll_count(const unsigned *p, unsigned target, unsigned *err) {
+  unsigned spins = 0;
+  while (!ge_u32(__hip_atomic_load(const_cast<unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target)) {
+    poll_pause(spins);
+    ++spins;
+    if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+    if (spins > kLayerSpinLimit) {
+      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return true;
+}
+
+// whole wave: flags[f] >= target for every f in [f0, f1] (the lanes poll 64 flags at a time)
+__device__ inline bool poll_flags(const unsigned *flags, int f0, int f1, unsigned target, unsigned *err, int lane) {
+  for (int base = f0; base <= f1; base += 64) {
+    const int f = base + lane;
+    unsigned spins = 0;
+    for (;;) {
+      const bool ok = f > f1 ||
+                      ge_u32(__hip_atomic_load(const_cast<unsigned *>(flags + f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target);
+      if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+      poll_pause(spins);
+      ++spins;
+      if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+      if (spins > kLayerSpinLimit) {
+        if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return true;
+}
+
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
 __device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
 __device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
@@ -240,15 +296,15 @@ struct Stage {
   float zp[kBatch];
 };
 
-// Issue the loads of runs r .. r + kBatch - 1 (relative to the wave's first run).  The resources
-// cover exactly the wave's runs, scale groups and activations, so loads past its end read zero
-// (and contribute nothing); the whole offset is in the VGPR operand, which the range check uses.
+// Issue the loads of runs r .. r + kBatch - 1 (relative to the wave's first run): weights and
+// scales (load_weights), activations and gain (load_acts).  The resources cover exactly the wave's
+// runs, scale groups and activations, so loads past its end read zero (and contribute nothing);
+// the whole offset is in the VGPR operand, which the range check uses.  XCOH: the activations
+// were written earlier in the same kernel by other workgroups (device-coherent loads).
 template <int FMT, bool NORM>
-__device__ __forceinline__ void load_batch(GemvBatch<FMT, NORM> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
-                                           __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int r, int c0, int g0,
-                                           int gshift, int lane) {
+__device__ __forceinline__ void load_weights(GemvBatch<FMT, NORM> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                             int r, int c0, int g0, int gshift, int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
-  constexpr int CK = Q4 ? 32 : 16;
   const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
 #pragma unroll
   for (int i = 0; i < kBatch; ++i) {
@@ -258,9 +314,21 @@ __device__ __forceinline__ void load_batch(GemvBatch<FMT, NORM> &B, __amdgpu_buf
       B.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, (uint32_t)g * (kTile * 2) + lane * 2, 0, 0);
     }
   }
+}
+template <int FMT, bool NORM, bool XCOH>
+__device__ __forceinline__ void load_acts(GemvBatch<FMT, NORM> &B, __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr,
+                                          int r, int lane) {
+  constexpr int CK = (FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16;
   const uint32_t xo = (lane * 4 < kBatch * CK) ? (uint32_t)(r * CK + lane * 4) * 4u : 0x80000000u;
-  B.x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0));
+  B.x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, XCOH ? kAuxSc1 : 0));
   if constexpr (NORM) B.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, xo, 0, 0));
+}
+template <int FMT, bool NORM, bool XCOH>
+__device__ __forceinline__ void load_batch(GemvBatch<FMT, NORM> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                           __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int r, int c0, int g0,
+                                           int gshift, int lane) {
+  load_weights<FMT, NORM>(B, wr, sr, r, c0, g0, gshift, lane);
+  load_acts<FMT, NORM, XCOH>(B, xr, gr, r, lane);
 }
 
 // Stage a batch's activations in the wave's LDS slot, then accumulate its runs into acc (INT4:
@@ -377,8 +445,15 @@ __device__ __forceinline__ void argmax_tiles(const GemvArgs &a, int tile, int ti
 //     one is computed;
 //   * split-K partials travel through device-coherent memory and the last wave of a tile adds
 //     them in a fixed order, then runs the epilogue.
-template <int FMT, bool NORM, int EPI>
+// SYNC selects the unit's role in the fused attention kernel: kSyncNone (standalone),
+// kSyncProducer (the qkv GEMV: device-coherent output stores, then a count for the KV head of
+// its rows), kSyncConsumer (the o GEMV: weights requested, then a wait on the producers of its
+// k-range, then device-coherent activation loads).
+constexpr int kSyncNone = 0, kSyncProducer = 1, kSyncConsumer = 2;
+
+template <int FMT, bool NORM, int EPI, int SYNC = kSyncNone>
 __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> (&sm)[2], int lane) {
+  constexpr bool XCOH = SYNC == kSyncConsumer;
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;  // k per 16-byte run
   const int ks = a.ks, K = a.K, N = a.N;
@@ -406,7 +481,7 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
   // last run the loads read zeros.
   float acc = 0.f;
   GemvBatch<FMT, NORM> A, B;
-  load_batch<FMT, NORM>(A, wr, sr, xr, gr, 0, c0, g0, gshift, lane);
+  load_weights<FMT, NORM>(A, wr, sr, 0, c0, g0, gshift, lane);
   // The epilogue's inputs (sums of squares, bias, residual, INT8 row scale) are fetched now, so
   // the wave that finishes a tile does not wait on memory for them.
   const int n = tile * kTile + lane;
@@ -419,12 +494,20 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
     if (a.residual) pre_res = a.residual[n];  // (y may alias it: only this tile's epilogue writes y[n])
   }
   if constexpr (FMT == QDEC_W_Q8_ROW) pre_scale = reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
+  unsigned e = 0;
+  if constexpr (SYNC != kSyncNone) e = __builtin_amdgcn_readfirstlane(*a.epoch);
+  if constexpr (SYNC == kSyncConsumer) {
+    // the producers of activations k = c0 CK .. c1 CK - 1 (the weights above are already on
+    // their way)
+    if (!poll_flags(a.wait_flags, (c0 * CK) / a.wait_div, (c1 * CK - 1) / a.wait_div, e, a.err, lane)) return;
+  }
+  load_acts<FMT, NORM, XCOH>(A, xr, gr, 0, lane);
   const int nb = (nrun + kBatch - 1) / kBatch;
   for (int b = 0; b < nb; b += 2) {
-    load_batch<FMT, NORM>(B, wr, sr, xr, gr, (b + 1) * kBatch, c0, g0, gshift, lane);
+    load_batch<FMT, NORM, XCOH>(B, wr, sr, xr, gr, (b + 1) * kBatch, c0, g0, gshift, lane);
     compute_batch<FMT, NORM>(acc, A, sm[0], lane);
     if (b + 1 >= nb) break;
-    load_batch<FMT, NORM>(A, wr, sr, xr, gr, (b + 2) * kBatch, c0, g0, gshift, lane);
+    load_batch<FMT, NORM, XCOH>(A, wr, sr, xr, gr, (b + 2) * kBatch, c0, g0, gshift, lane);
     compute_batch<FMT, NORM>(acc, B, sm[1], lane);
   }
   if constexpr (Q4) acc *= 16777216.0f;  // 2^24, exact
@@ -468,7 +551,14 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
     if (valid) {
       if (a.bias) v += pre_bias;
       if (a.residual) v += pre_res;
-      a.y[n] = v;
+      st_f<SYNC == kSyncProducer>(a.y + n, v);
+    }
+    if constexpr (SYNC == kSyncProducer) {
+      // qkv: count this tile for the KV head its rows belong to (tiles never straddle heads)
+      drain_stores();
+      const int row0 = tile * kTile, qd = a.Hq * a.hd, kd = a.Hkv * a.hd;
+      const int j = row0 < qd ? (row0 / a.hd) / (a.Hq / a.Hkv) : (row0 < qd + kd ? (row0 - qd) / a.hd : (row0 - qd - kd) / a.hd);
+      if (lane == 0) (void)__hip_atomic_fetch_add(a.done + j * kLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (EPI == EPI_STORE && a.ssq_out) {
       const float sq = wave_sum(valid ? v * v : 0.f);

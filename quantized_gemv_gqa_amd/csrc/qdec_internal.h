@@ -49,6 +49,16 @@ struct GemvArgs {
   float *cand;
   int32_t *token, *pos, *token_log, *step_count;
   int log_len;
+  // Step-synchronised units of the fused layer kernels (null/0 otherwise).  *epoch is the step
+  // number e (>= 1).  A consumer unit waits until wait_flags[f] >= e for every f covering its
+  // k-range (f = k / wait_div).  A producer unit, after its device-coherent output stores, adds 1
+  // to done[KV head of its rows * kLine] (the qkv GEMV, whose Hq, Hkv, hd give the head layout).
+  const unsigned *epoch;
+  const unsigned *wait_flags;
+  int wait_div;
+  unsigned *done;
+  int Hq, Hkv, hd;
+  unsigned *err;  // set on a wait that times out
 };
 // Device atomics to one cache line serialize (about 13 ns each on MI355X), so every arrival
 // counter sits on a 128-byte line of its own.
@@ -65,6 +75,9 @@ struct GemvPlan {
   int tiles, nch, ks, cps, units, blocks;
 };
 GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split);
+// Copy the plan into the arguments a kernel reads (k-splits, runs per split, INT4 group as a
+// shift): every launch path calls it once, after the arguments are filled.
+void gemv_apply_plan(GemvArgs &a, const GemvPlan &p, int wfmt);
 size_t gemv_workspace_bytes(int wfmt, int N, int K, bool argmax = false);
 void gemv_bind_workspace(GemvArgs &a, const GemvPlan &p, void *ws);
 hipError_t launch_gemv(int wfmt, const GemvArgs &a, const GemvPlan &p, hipStream_t st);
@@ -96,6 +109,15 @@ struct AttnArgs {
   float *ws;               // [splits][Hq][D + 2] partials
   unsigned *counters;      // arrival counter of KV head j at [j * kLine], zero between launches
   float *out;              // [Hq][D]
+  // Step-synchronised form (fused layer kernel; null otherwise): wait until
+  // wait_cnt[j * kLine] >= *epoch * wait_per_step (the qkv tiles of KV head j are stored), read qkv
+  // with device-coherent loads, store out device-coherently and set done[j] = *epoch when the
+  // merge of KV head j is complete.
+  const unsigned *epoch;
+  const unsigned *wait_cnt;
+  unsigned wait_per_step;
+  unsigned *done;
+  unsigned *err;
 };
 constexpr int kMaxMergeSplits = 256;
 constexpr size_t kAttnCounterBytes = 64 * 128;  // one line per KV head, up to 64 KV heads
@@ -106,6 +128,19 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
 hipError_t launch_kv_append(const float *k, const float *v, void *k_pool, void *v_pool, int kv_fmt,
                             const int32_t *page_table, int n_pages, const int32_t *pos, int Hkv,
                             int D, hipStream_t st);
+
+// ---------------------------------------------------------------------------------- fused layer
+// The attention half of a decoder layer as one launch (see layer.hip): qkv GEMV, attention and
+// o GEMV as workgroup roles.  GEMV units are unit = block * waves + wave within their role's
+// block range.
+struct LayerArgs {
+  GemvArgs qkv, o;
+  AttnArgs at;
+  int nb_qkv, nb_o;  // blocks per GEMV role
+};
+bool layer_fusion_supported(int G, int D);
+int attn_layer_waves();
+hipError_t launch_attn_layer(const LayerArgs &a, int wfmt, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- small ops
 // Per-head post-processing of a fused qkv vector: optional per-head RMSNorm of q and k, RoPE of
@@ -129,9 +164,11 @@ hipError_t launch_rmsnorm_rope(const float *x, const float *gamma, float *y, int
 hipError_t launch_swiglu(const float *g, const float *u, float *m, int n, hipStream_t st);
 // h = bf16 -> fp32 row E[*token] (E null: h is given), ssq[t] = sum of h^2 over rows 64t..64t+63.
 // With rope_cs != null it also writes the RoPE table of *pos: rope_cs[2i], rope_cs[2i+1] =
-// cos, sin of pos * base^(-2i/D) in fp64, i < D/2.
+// cos, sin of pos * base^(-2i/D) in fp64, i < D/2.  With epoch != null it advances the step
+// number *epoch by one (the fused layer kernels' flag target).
 hipError_t launch_embed(const uint16_t *E, const int32_t *token, int H, int V, float *h, float *ssq,
-                        const int32_t *pos, float rope_base, int D, double *rope_cs, hipStream_t st);
+                        const int32_t *pos, float rope_base, int D, double *rope_cs, unsigned *epoch,
+                        hipStream_t st);
 // argmax over logits; writes *token, token_log[*step_count] (if log), advances *pos and
 // *step_count.  With logits == null it only advances *pos.
 hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int32_t *pos,

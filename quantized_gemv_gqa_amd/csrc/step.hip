@@ -27,12 +27,19 @@ struct qdec_step {
   // workspace carve-up
   float *qkv = nullptr, *attn = nullptr, *mlp = nullptr, *ssq = nullptr, *attn_ws = nullptr;
   double *rope_cs = nullptr;  // this step's RoPE (cos, sin) table, written by the embed kernel
+  // fused attention kernel (three launches per layer)
+  bool layer_ok = false;
+  float *hB = nullptr, *ssqB = nullptr;  // second residual buffer and its per-tile sums of squares
+  void *gemv_ws2 = nullptr;              // GEMV workspace of the roles that run beside the first
+  unsigned *lsync = nullptr;             // [0]: step number; then per layer: qkv counts, attention flags
+  size_t lsync_layer_words = 0;
   void *gemv_ws = nullptr;
   qdec::GemvPlan p_qkv, p_o, p_gu, p_down, p_lm;
   int ssq_n = 0;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-  hipStream_t graph_stream = nullptr;
+  hipGraph_t graph[2] = {nullptr, nullptr};      // [per-op]: captured step
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  hipStream_t graph_stream[2] = {nullptr, nullptr};
+  int graph_kernels[2] = {0, 0};
   int n_kernels = 0;
   // persistent step
   bool fused_ok = false;
@@ -47,7 +54,7 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, fused_layers, err, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, fused_layers, err, total;
   // persistent step
   size_t hB, xa, xb, ssqA, ssqB, sync, gu_flag, tile_cnt, cand, sub_cand, part[5];
   size_t part_bytes[5];
@@ -105,6 +112,10 @@ SkPhase plan_sk(int tiles, int nch, int waves) {
   }
 }
 
+// Per layer: the qkv tile counts (one 128-byte line per KV head) and the attention-done flags
+// (one line).
+size_t lsync_layer_words(int Hkv) { return (size_t)Hkv * kLine + kLine; }
+
 Layout layout_of(const qdec_config &c) {
   Layout L{};
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
@@ -122,14 +133,16 @@ Layout layout_of(const qdec_config &c) {
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, c.inter));
   if (c.vocab > 0) g = std::max(g, gemv_workspace_bytes(c.wfmt, c.vocab, c.hidden, true));
   L.gemv_ws = off; off += align256(g);
+  L.gemv_ws2 = off; off += align256(g);
+  L.lsync = off; off += align256((32 + (size_t)c.n_layers * lsync_layer_words(c.n_kv_heads)) * 4);
   L.err = off; off += 256;
   // persistent step: activations, sync lines, per-phase split state
   L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
   L.hB = off; off += align256((size_t)c.hidden * 4);
   L.xa = off; off += align256((size_t)c.hidden * 4);
   L.xb = off; off += align256((size_t)c.hidden * 4);
-  L.ssqA = off; off += 256;
-  L.ssqB = off; off += 256;
+  L.ssqA = off; off += align256(std::max<size_t>(256, (size_t)((c.hidden + 63) / 64) * 4));
+  L.ssqB = off; off += align256(std::max<size_t>(256, (size_t)((c.hidden + 63) / 64) * 4));
   L.sync = off; off += (size_t)sync_lines(c).total * 128;
   const int ck = (c.wfmt == QDEC_W_Q4_G_ZP8) ? 32 : 16;
   const int Ns[5] = {nqkv, c.hidden, 2 * c.inter, c.hidden, std::max(c.vocab, 1)};
@@ -216,19 +229,113 @@ GemvArgs gemv_args(const qdec_step *h, const void *W, const void *S, const float
     ++n;                                                   \
   } while (0)
 
-// Enqueue one whole step; returns the number of kernels launched through `count`.
-qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count) {
+AttnArgs step_attn_args(const qdec_step *h, int l) {
+  const qdec_config &c = h->cfg;
+  const qdec_state &s = h->state;
+  const qdec_layer_weights &w = h->layers[l];
+  AttnArgs at{};
+  at.qkv = h->qkv;
+  at.g_q = c.has_qk_norm ? w.g_q : nullptr;
+  at.g_k = c.has_qk_norm ? w.g_k : nullptr;
+  at.eps = c.rms_eps;
+  at.rope_cs = h->rope_cs;
+  at.k_pool = h->kpools[l];
+  at.v_pool = h->vpools[l];
+  at.kv_fmt = c.kv_fmt;
+  at.page_table = s.page_table;
+  at.n_pages = c.n_pages;
+  at.pos = s.pos;
+  at.Hq = c.n_heads;
+  at.Hkv = c.n_kv_heads;
+  at.D = c.head_dim;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  at.splits = c.num_splits;
+  at.counters = reinterpret_cast<unsigned *>(h->attn_ws);
+  at.ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
+  at.out = h->attn;
+  return at;
+}
+
+// One layer as the attention kernel (qkv GEMV, attention, o GEMV), then the gate/up and down
+// GEMVs.  Residual stream: hA = state.hidden (read by qkv and o's residual, written by down), hB
+// (written by o, read by gate/up and down's residual), each with its own sums of squares.
+hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
+  const qdec_config &c = h->cfg;
+  const qdec_state &s = h->state;
+  const qdec_layer_weights &w = h->layers[l];
+  const int H = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.inter, G = Hq / Hkv;
+  const int qd = Hq * D, nqkv = (Hq + 2 * Hkv) * D;
+  unsigned *const epoch = h->lsync;
+  unsigned *const ls = h->lsync + 32 + (size_t)l * h->lsync_layer_words;
+  unsigned *const qkv_cnt = ls;                            // [Hkv lines]
+  unsigned *const attn_done = ls + (size_t)Hkv * kLine;    // [Hkv] in one line
+  float *const hA = s.hidden;
+  LayerArgs la{};
+  la.qkv = gemv_args(h, w.w_qkv, w.s_qkv, hA, h->qkv, nqkv, H, h->p_qkv);
+  la.qkv.gamma = w.g_attn;
+  la.qkv.bias = c.has_qkv_bias ? w.b_qkv : nullptr;
+  la.qkv.epoch = epoch;
+  la.qkv.done = qkv_cnt;
+  la.qkv.Hq = Hq;
+  la.qkv.Hkv = Hkv;
+  la.qkv.hd = D;
+  la.qkv.err = h->err;
+  la.at = step_attn_args(h, l);
+  la.at.epoch = epoch;
+  la.at.wait_cnt = qkv_cnt;
+  la.at.wait_per_step = (unsigned)((G + 2) * (D / kTile));
+  la.at.done = attn_done;
+  la.at.err = h->err;
+  la.o = gemv_args(h, w.w_o, w.s_o, h->attn, h->hB, H, qd, h->p_o);
+  gemv_bind_workspace(la.o, h->p_o, h->gemv_ws2);
+  la.o.residual = hA;
+  la.o.ssq_out = h->ssqB;
+  la.o.epoch = epoch;
+  la.o.wait_flags = attn_done;
+  la.o.wait_div = G * D;  // attention outputs per KV head
+  la.o.err = h->err;
+  gemv_apply_plan(la.qkv, h->p_qkv, c.wfmt);
+  gemv_apply_plan(la.o, h->p_o, c.wfmt);
+  const int aw = attn_layer_waves();
+  la.nb_qkv = (h->p_qkv.units + aw - 1) / aw;
+  la.nb_o = (h->p_o.units + aw - 1) / aw;
+  hipError_t e = launch_attn_layer(la, c.wfmt, st);
+  if (e != hipSuccess) return e;
+  // the MLP block as two plain launches: its gate/up tiles all finish together, so a down GEMV
+  // in the same launch could only wait for them
+  GemvArgs g = gemv_args(h, w.w_gu, w.s_gu, h->hB, h->mlp, 2 * I, H, h->p_gu);
+  g.gamma = w.g_ffn;
+  g.ssq = h->ssqB;
+  g.epi = EPI_SWIGLU;
+  e = launch_gemv(c.wfmt, g, h->p_gu, st);
+  if (e != hipSuccess) return e;
+  GemvArgs d = gemv_args(h, w.w_down, w.s_down, h->mlp, hA, H, I, h->p_down);
+  d.residual = h->hB;
+  d.ssq_out = h->ssq;
+  return launch_gemv(c.wfmt, d, h->p_down, st);
+}
+
+// Enqueue one whole step; returns the number of kernels launched through `count`.  Unless
+// per_op is set (or the model's shape has no fused layer kernels), each layer is two launches.
+qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count, bool per_op) {
   const qdec_config &c = h->cfg;
   const qdec_state &s = h->state;
   const int H = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.inter;
   const int qd = Hq * D, nqkv = (Hq + 2 * Hkv) * D;
   const int wf = c.wfmt;
   int n = 0;
+  const bool fuse = h->layer_ok && !per_op;
   QDEC_CK(launch_embed(h->model.embed, s.token, H, c.vocab, s.hidden, h->ssq, s.pos, c.rope_base, D, h->rope_cs,
-                       st));
+                       fuse ? h->lsync : nullptr, st));
   if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace, H, st));
   for (int l = 0; l < c.n_layers; ++l) {
     const qdec_layer_weights &w = h->layers[l];
+    if (fuse) {
+      QDEC_CK(enqueue_layer(h, l, st));
+      n += 2;  // three launches
+      if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace + (size_t)(l + 1) * H, H, st));
+      continue;
+    }
     // attention block
     GemvArgs a = gemv_args(h, w.w_qkv, w.s_qkv, s.hidden, h->qkv, nqkv, H, h->p_qkv);
     a.gamma = w.g_attn;
@@ -445,6 +552,12 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   if (lm) h->p_lm = gemv_plan(cfg->wfmt, cfg->vocab, cfg->hidden, true);
   h->err = reinterpret_cast<unsigned *>(ws + L.err);
   const int G = cfg->n_heads / cfg->n_kv_heads;
+  h->gemv_ws2 = ws + L.gemv_ws2;
+  h->hB = reinterpret_cast<float *>(ws + L.hB);
+  h->ssqB = reinterpret_cast<float *>(ws + L.ssqB);
+  h->lsync = reinterpret_cast<unsigned *>(ws + L.lsync);
+  h->lsync_layer_words = lsync_layer_words(cfg->n_kv_heads);
+  h->layer_ok = layer_fusion_supported(G, cfg->head_dim) && cfg->n_kv_heads <= kLine;
   if (lm && m->embed && cfg->hidden % 64 == 0 && cfg->hidden <= 4096 &&
       fused_supported(cfg->wfmt, G, cfg->head_dim, cfg->kv_fmt)) {
     qdec_status r2 = setup_fused(h, L, G);
@@ -460,8 +573,11 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
 qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
   QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_decode_step: null handle");
   hipStream_t st = (hipStream_t)stream;
-  if (mode == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels);
-  if (mode == QDEC_STEP_FUSED) {
+  const bool per_op = (mode & QDEC_STEP_PER_OP) != 0;
+  const int base = mode & ~QDEC_STEP_PER_OP;
+  if (base == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels, per_op);
+  if (base == QDEC_STEP_FUSED) {
+    QDEC_REQUIRE(!per_op, QDEC_EINVAL, "qdec_decode_step: QDEC_STEP_PER_OP does not apply to the fused step");
     QDEC_REQUIRE(h->fused_ok, QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step is not available for this model");
     const int G = h->cfg.n_heads / h->cfg.n_kv_heads;
     hipError_t e = launch_fused(h->fa, h->cfg.wfmt, G, h->fused_blocks, st);
@@ -472,8 +588,9 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
     h->n_kernels = 1;
     return QDEC_OK;
   }
-  QDEC_REQUIRE(mode == QDEC_STEP_GRAPH, QDEC_EINVAL, "qdec_decode_step: unknown mode %d", mode);
-  if (!h->exec) {
+  QDEC_REQUIRE(base == QDEC_STEP_GRAPH, QDEC_EINVAL, "qdec_decode_step: unknown mode %d", mode);
+  const int v = per_op ? 1 : 0;
+  if (!h->exec[v]) {
     QDEC_REQUIRE(st != nullptr, QDEC_ESTATE,
                  "qdec_decode_step: graph capture needs a non-default stream");
     hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
@@ -481,7 +598,8 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
       set_error("hipStreamBeginCapture: %s", hipGetErrorString(e));
       return QDEC_EHIP;
     }
-    qdec_status r = enqueue_step(h, st, &h->n_kernels);
+    int nk = 0;
+    qdec_status r = enqueue_step(h, st, &nk, per_op);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(st, &g);
     if (r != QDEC_OK) {
@@ -492,22 +610,24 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
       set_error("hipStreamEndCapture: %s", hipGetErrorString(e));
       return QDEC_EHIP;
     }
-    e = hipGraphInstantiate(&h->exec, g, nullptr, nullptr, 0);
+    e = hipGraphInstantiate(&h->exec[v], g, nullptr, nullptr, 0);
     if (e != hipSuccess) {
       (void)hipGraphDestroy(g);
       set_error("hipGraphInstantiate: %s", hipGetErrorString(e));
       return QDEC_EHIP;
     }
-    h->graph = g;
-    h->graph_stream = st;
+    h->graph[v] = g;
+    h->graph_stream[v] = st;
+    h->graph_kernels[v] = nk;
   }
-  QDEC_REQUIRE(st == h->graph_stream, QDEC_ESTATE,
+  QDEC_REQUIRE(st == h->graph_stream[v], QDEC_ESTATE,
                "qdec_decode_step: graph was captured on another stream");
-  hipError_t e = hipGraphLaunch(h->exec, st);
+  hipError_t e = hipGraphLaunch(h->exec[v], st);
   if (e != hipSuccess) {
     set_error("hipGraphLaunch: %s", hipGetErrorString(e));
     return QDEC_EHIP;
   }
+  h->n_kernels = h->graph_kernels[v];
   return QDEC_OK;
 }
 
@@ -547,8 +667,10 @@ qdec_status qdec_step_read_error(qdec_step *h, int *flag) {
 
 void qdec_step_destroy(qdec_step *h) {
   if (!h) return;
-  if (h->exec) (void)hipGraphExecDestroy(h->exec);
-  if (h->graph) (void)hipGraphDestroy(h->graph);
+  for (int v = 0; v < 2; ++v) {
+    if (h->exec[v]) (void)hipGraphExecDestroy(h->exec[v]);
+    if (h->graph[v]) (void)hipGraphDestroy(h->graph[v]);
+  }
   delete h;
 }
 

@@ -101,15 +101,19 @@ def test_truncated_model_steps(name, n_layers):
         sync()
 
 
+MODES = (q.STEP_EAGER, q.STEP_GRAPH, q.STEP_EAGER | q.STEP_PER_OP, q.STEP_GRAPH | q.STEP_PER_OP)
+
+
 def test_graph_replay_equals_eager_bitwise():
-    """Same kernels either way: graph replays must reproduce eager launches bit for bit, across a
-    page boundary (positions 15 -> 16 -> 17), with pos and token read from device memory."""
+    """Same device code either way: graph replays and the two-launch layer kernels must reproduce
+    per-op eager launches bit for bit, across a page boundary (positions 15 -> 16 -> 17), with pos
+    and token read from device memory."""
     wl = synth.WORKLOADS["qwen2.5-7b-q4"]
     model = synth.make_model(wl, n_layers=2)
     kv = synth.make_kv(wl, 64, n_layers=2, ctx=15)
     dm = q.upload_model(model)
     outs = {}
-    for mode in (q.STEP_EAGER, q.STEP_GRAPH):
+    for mode in MODES:
         dk = q.upload_kv(kv, wl.kv_fmt)
         st = q.DecodeStep(dm, dk, pos0=15, token0=model["token"], trace=True, log_len=8, num_splits=3)
         res = []
@@ -118,17 +122,45 @@ def test_graph_replay_equals_eager_bitwise():
                 st.step(mode)
                 sync()
                 res.append((host(st.logits).copy(), host(st.trace).copy(), int(host(st.token)[0])))
+        assert st.read_error() == 0, mode
         outs[mode] = (res, host(st.token_log).copy(), int(host(st.pos)[0]), [host(t).copy() for t in dk["k"]])
         st.close()
-    (re, le, pe, ke), (rg, lg, pg, kg) = outs[q.STEP_EAGER], outs[q.STEP_GRAPH]
-    assert pe == pg == 19
-    assert np.array_equal(le, lg) and list(le[:4]) == [r[2] for r in re]
-    for a, b in zip(re, rg):
-        assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
-        assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
-        assert a[2] == b[2]
-    for a, b in zip(ke, kg):
-        assert np.array_equal(a, b)
+    re, le, pe, ke = outs[q.STEP_EAGER | q.STEP_PER_OP]
+    assert pe == 19 and list(le[:4]) == [r[2] for r in re]
+    for mode in MODES:
+        rg, lg, pg, kg = outs[mode]
+        assert pg == pe and np.array_equal(le, lg), mode
+        for a, b in zip(re, rg):
+            assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32)), mode
+            assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32)), mode
+            assert a[2] == b[2], mode
+        for a, b in zip(ke, kg):
+            assert np.array_equal(a, b), mode
+
+
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-q8", "qwen3-8b-q8"])
+def test_layer_kernels_equal_per_op_bitwise(name):
+    """The other fused-layer shapes (6 and 4 q heads per KV head, int8 weights, q/k norm) against
+    per-op launches, bit for bit, and the step's error word stays clear."""
+    wl = synth.WORKLOADS[name]
+    model = synth.make_model(wl, n_layers=2)
+    kv = synth.make_kv(wl, 40, n_layers=2, ctx=30)
+    dm = q.upload_model(model)
+    outs = {}
+    for mode in (q.STEP_GRAPH, q.STEP_GRAPH | q.STEP_PER_OP):
+        dk = q.upload_kv(kv, wl.kv_fmt)
+        st = q.DecodeStep(dm, dk, pos0=30, token0=model["token"], trace=True, num_splits=2)
+        res = []
+        with torch.cuda.stream(torch.cuda.Stream()):
+            for _ in range(3):
+                st.step(mode)
+                sync()
+                res.append((host(st.logits).copy().view(np.uint32), host(st.trace).copy().view(np.uint32)))
+        assert st.read_error() == 0
+        outs[mode] = res
+        st.close()
+    for a, b in zip(outs[q.STEP_GRAPH], outs[q.STEP_GRAPH | q.STEP_PER_OP]):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_step_errors_are_reported():

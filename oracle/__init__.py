@@ -75,6 +75,8 @@ def lib(path: str | None = None):
         L.orc_bf16_to_f32.argtypes = [U16]; L.orc_bf16_to_f32.restype = F
         L.orc_dequant_row.argtypes = [I, _P, _P, I, I64, I, _P]; L.orc_dequant_row.restype = None
         L.orc_gemv.argtypes = [I, _P, _P, I, _P, _P, _P, _P, I, I, I]; L.orc_gemv.restype = None
+        L.orc_quantize_act_i8.argtypes = [_P, I, I, _P, _P]; L.orc_quantize_act_i8.restype = None
+        L.orc_gemv_a8.argtypes = [I, _P, _P, I, _P, _P, _P, _P, _P, I, I, I]; L.orc_gemv_a8.restype = None
         L.orc_rmsnorm.argtypes = [_P, _P, _P, I, I, D]; L.orc_rmsnorm.restype = None
         L.orc_rope.argtypes = [_P, I, I, I, D]; L.orc_rope.restype = None
         L.orc_swiglu.argtypes = [_P, _P, _P, I]; L.orc_swiglu.restype = None
@@ -138,6 +140,31 @@ def gemv(wfmt, W, S, x, bias=None, residual=None, group=64, nthreads=0) -> np.nd
     r = None if residual is None else np.ascontiguousarray(residual, np.float32)
     lib().orc_gemv(_fmt(wfmt), _p(W), _p(S), group, _p(x), _p(b), _p(r), _p(y), N, K,
                    nthreads or int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1)
+    return y
+
+
+def quantize_act_i8(x, group=64):
+    """INT8 activations with one scale per group (Path A); returns (q int8 [K], s float32 [K/group])."""
+    x = np.ascontiguousarray(x, np.float32)
+    K = x.shape[0]
+    assert K % group == 0
+    q = np.empty(K, np.int8)
+    s = np.empty(K // group, np.float32)
+    lib().orc_quantize_act_i8(_p(x), K, group, _p(q), _p(s))
+    return q, s
+
+
+def gemv_a8(wfmt, W, S, q, sx, bias=None, residual=None, group=64, nthreads=0) -> np.ndarray:
+    """GEMV with INT8 activations (q, per-group sx from quantize_act_i8)."""
+    W = np.ascontiguousarray(W); S = np.ascontiguousarray(S)
+    q = np.ascontiguousarray(q, np.int8); sx = np.ascontiguousarray(sx, np.float32)
+    N = W.shape[0]
+    K = q.shape[0]
+    y = np.empty(N, np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    r = None if residual is None else np.ascontiguousarray(residual, np.float32)
+    lib().orc_gemv_a8(_fmt(wfmt), _p(W), _p(S), group, _p(q), _p(sx), _p(b), _p(r), _p(y), N, K,
+                      nthreads or int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1)
     return y
 
 

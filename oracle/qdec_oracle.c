@@ -17,6 +17,7 @@
  *        8 (INT8 per-output-row dequant in the GEMV).
  *  [PA]  "Chapter 2 Systems Foundations for LLMs": "PagedAttention - Virtual Memory for KV
  *        Caches" (page table from logical token block to physical block).
+ *  [H100] also "Challenge 3" (Path A: INT8 activations with a per-group scale and dp4a).
  *  [NQ]  "Naive CUDA Kernel Qwen engine, part 1" (eduardoqian): sections RMSNorm, Rope,
  *        SwiGLU, Sampler; the GGUF tensor list of a Qwen2 block.
  *
@@ -28,6 +29,7 @@
  *  - SwiGLU: SiLU (beta = 1) on the gate projection, the up projection linear.
  *  - Residual wiring: pre-norm, h += o_proj(attn(...)), h += down(swiglu(...)).
  *  - Greedy tie-break: smallest index.
+ *  - INT8 activations: symmetric per group, s = max|x|/127, round half to even in binary32.
  */
 #include "qdec_oracle.h"
 
@@ -123,6 +125,76 @@ void orc_gemv(int fmt, const void *W, const void *S, int group, const float *x, 
       y[n] = (float)acc;
     }
     free(w);
+  }
+}
+
+/* ---------------------------------------------------------------- INT8 activations (Path A)
+ *
+ * [H100 "Challenge 3", Path A; RT section 7, "Bug #3"]: before the GEMV the activations are
+ * quantised to INT8 with one scale per group of consecutive k, the dot product of the integer
+ * weight levels with the INT8 activations is taken in integers, and the group scales undo the
+ * quantisation on the integer sum.  The pages do not fix the scale or the rounding; the reading:
+ * symmetric per group of `group` k, s = max|x| / 127, q = round-half-even(x * (127 / max|x|)),
+ * every operation in binary32 (so the integer decision is the one the GPU takes), q in
+ * [-127, 127]; a group of zeros has s = 0 and q = 0.  Inputs are finite.
+ */
+void orc_quantize_act_i8(const float *x, int K, int group, int8_t *q, float *sx) {
+  for (int g = 0; g < K / group; ++g) {
+    const float *xg = x + (int64_t)g * group;
+    int8_t *qg = q + (int64_t)g * group;
+    float amax = 0.0f;
+    for (int i = 0; i < group; ++i) {
+      const float a = fabsf(xg[i]);
+      if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+      sx[g] = 0.0f;
+      memset(qg, 0, (size_t)group);
+      continue;
+    }
+    const float inv = 127.0f / amax; /* binary32 division, correctly rounded */
+    sx[g] = amax / 127.0f;
+    for (int i = 0; i < group; ++i) {
+      const float t = xg[i] * inv;   /* binary32 product */
+      float r = rintf(t);            /* nearest, ties to even */
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      qg[i] = (int8_t)r;
+    }
+  }
+}
+
+/* y[n] = sum over groups g of (weight scale) * sx[g] * sum_{k in g} level[n][k] * q[k] (+ bias)
+ * (+ residual): integer sums are exact (int64), the scaling is fp64, rounded once to fp32.
+ * INT8 weights: level = the int8 code, one scale per row (applied per group).  INT4 weights:
+ * level = nibble - 8 and the fp16 scale of the weight group; the activation groups are the
+ * weight groups. */
+void orc_gemv_a8(int fmt, const void *W, const void *S, int group, const int8_t *q, const float *sx,
+                 const float *bias, const float *residual, float *y, int N, int K, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int n = 0; n < N; ++n) {
+    double acc = 0.0;
+    for (int g = 0; g < K / group; ++g) {
+      int64_t isum = 0;
+      double ws;
+      if (fmt == ORC_W_Q8) {
+        const int8_t *w = (const int8_t *)W + (int64_t)n * K;
+        for (int k = g * group; k < (g + 1) * group; ++k) isum += (int64_t)w[k] * q[k];
+        ws = (double)((const float *)S)[n];
+      } else {
+        const uint8_t *b = (const uint8_t *)W + (int64_t)n * (K / 2);
+        for (int k = g * group; k < (g + 1) * group; ++k) {
+          const int nib = (k % 2 == 0) ? (b[k / 2] & 0x0F) : (b[k / 2] >> 4);
+          isum += (int64_t)(nib - 8) * q[k];
+        }
+        ws = (double)orc_f16_to_f32(((const uint16_t *)S)[(int64_t)n * (K / group) + g]);
+      }
+      acc += ws * (double)sx[g] * (double)isum;
+    }
+    if (bias != NULL) acc += (double)bias[n];
+    if (residual != NULL) acc += (double)residual[n];
+    y[n] = (float)acc;
   }
 }
 

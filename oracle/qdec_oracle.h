@@ -32,6 +32,12 @@ void orc_dequant_row(int fmt, const void *W, const void *S, int group, int64_t r
 void orc_gemv(int fmt, const void *W, const void *S, int group, const float *x, const float *bias,
               const float *residual, float *y, int N, int K, int nthreads);
 
+/* INT8 activations: q[k] in [-127, 127], one binary32 scale per group of `group` k */
+void orc_quantize_act_i8(const float *x, int K, int group, int8_t *q, float *sx);
+/* y[n] = fp32( sum_g wscale * sx[g] * sum_{k in g} level[n][k] q[k]  (+ bias) (+ residual) ) */
+void orc_gemv_a8(int fmt, const void *W, const void *S, int group, const int8_t *q, const float *sx,
+                 const float *bias, const float *residual, float *y, int N, int K, int nthreads);
+
 /* per row of `dim`: y = gamma * x / sqrt(mean(x^2) + eps)  (gamma may be NULL: all ones) */
 void orc_rmsnorm(const float *x, const float *gamma, float *y, int rows, int dim, double eps);
 

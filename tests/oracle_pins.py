@@ -148,6 +148,85 @@ def check_gemv_bruteforce():
         assert np.allclose(y0, dequant(wfmt, W, Sc, grp) @ x.astype(np.float64), rtol=1e-6, atol=1e-6)
 
 
+# ----------------------------------------------------------------------------- INT8 activations
+def check_act_i8_by_hand():
+    """Per-group symmetric INT8 activations, worked by hand: with max|x| = 127 the inverse scale
+    is exactly 1, so q is x rounded to nearest with ties to even (62.5 -> 62, 1.5 -> 2,
+    -2.5 -> -2, -0.5 -> 0); with max|x| = 1 the inverse scale is 127 and 0.5 -> 63.5 -> 64."""
+    x = np.array([127, 62.5, -0.5, 1.5, -2.5, 0, 3.25, -126.75,
+                  0.5, -1.0, 0.25, 0.125, 0, 0, 0, 0], np.float32)
+    qv, sx = O.quantize_act_i8(x, group=8)
+    assert list(qv[:8]) == [127, 62, 0, 2, -2, 0, 3, -127], list(qv[:8])
+    assert list(qv[8:12]) == [64, -127, 32, 16] and list(qv[12:]) == [0] * 4
+    assert sx[0] == np.float32(1.0) and sx[1] == np.float32(1.0) / np.float32(127.0)
+    # a group of zeros has scale 0 and codes 0
+    q0, s0 = O.quantize_act_i8(np.zeros(64, np.float32))
+    assert not q0.any() and s0[0] == 0.0
+
+
+def check_act_i8_invariants():
+    """For every nonzero group: the largest |q| is 127, q is the binary32 product x * (127/amax)
+    rounded to nearest-even, and |x - q*s| <= s/2 up to the rounding of the scale."""
+    r = _rng(11)
+    x = (r.standard_normal(64 * 7) * r.uniform(0.01, 30.0, 64 * 7)).astype(np.float32)
+    x[64:128] = 0.0
+    qv, sx = O.quantize_act_i8(x)
+    for g in range(7):
+        xg, qg = x[g * 64:(g + 1) * 64].astype(np.float64), qv[g * 64:(g + 1) * 64].astype(np.int64)
+        if g == 1:
+            assert sx[g] == 0 and not qg.any()
+            continue
+        amax = np.abs(xg).max()
+        assert np.abs(qg).max() == 127
+        assert sx[g] == np.float32(amax) / np.float32(127)
+        t = (x[g * 64:(g + 1) * 64] * (np.float32(127) / np.float32(amax))).astype(np.float32)
+        assert np.array_equal(qg, np.clip(np.rint(t), -127, 127).astype(np.int64))
+        assert np.all(np.abs(xg - qg * float(sx[g])) <= 0.5 * float(sx[g]) * (1 + 1e-5))
+
+
+def check_gemv_a8_against_dequantized_activations():
+    """The INT8-activation GEMV is the real GEMV on the dequantised activations q[k] * s[k // group]:
+    checked against numpy dequant + fp64 matmul, both formats, with bias and residual; and when
+    x holds integers with max |x| = 127 per group, quantisation is the identity (q = x, s = 1), so the
+    result equals the exact rational value of the fp-activation GEMV."""
+    from np_decoder import dequant
+    r = _rng(12)
+    for wfmt, grp in (("q8", 64), ("q4", 64), ("q4", 32)):
+        N, K = 37, 256
+        if wfmt == "q8":
+            W = r.integers(-127, 128, (N, K)).astype(np.int8)
+            Sc = ((0.02 / 127) * r.uniform(0.5, 1.5, N)).astype(np.float32)
+        else:
+            W = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
+            Sc = r.uniform(0.005, 0.02, (N, K // grp)).astype(np.float16).view(np.uint16)
+        x = r.standard_normal(K).astype(np.float32)
+        qv, sx = O.quantize_act_i8(x, group=grp)
+        b = (0.02 * r.standard_normal(N)).astype(np.float32)
+        res = r.standard_normal(N).astype(np.float32)
+        xh = qv.astype(np.float64) * np.repeat(sx.astype(np.float64), grp)
+        Wd = dequant(wfmt, W, Sc, grp)
+        y = O.gemv_a8(wfmt, W, Sc, qv, sx, bias=b, residual=res, group=grp)
+        assert np.allclose(y, Wd @ xh + b + res, rtol=1e-6, atol=1e-6), wfmt
+        y0 = O.gemv_a8(wfmt, W, Sc, qv, sx, group=grp)
+        assert np.allclose(y0, Wd @ xh, rtol=1e-6, atol=1e-7), wfmt
+        # the quantisation error of the activations bounds the distance to the fp-activation GEMV
+        yf = O.gemv(wfmt, W, Sc, x, group=grp)
+        bound = np.abs(Wd) @ np.repeat(sx.astype(np.float64), grp) * 0.5
+        assert np.all(np.abs(y0.astype(np.float64) - yf) <= bound * (1 + 1e-4) + 1e-6), wfmt
+        # integer activations, 127 in every group: exact
+        xi = r.integers(-126, 127, K).astype(np.float32)
+        xi[::grp] = 127.0
+        qi, si = O.quantize_act_i8(xi, group=grp)
+        assert np.array_equal(qi.astype(np.float32), xi) and np.all(si == 1.0)
+        yi = O.gemv_a8(wfmt, W, Sc, qi, si, group=grp)
+        for n in range(0, N, 5):
+            if wfmt == "q8":  # row scale times an integer sum (the numpy dequant rounds w to fp32)
+                exact = Fraction(float(Sc[n])) * int((W[n].astype(np.int64) * xi.astype(np.int64)).sum())
+            else:  # fp16 scale times a small integer level is exact in fp64
+                exact = sum((Fraction(float(v)) for v in Wd[n] * xi.astype(np.float64)), Fraction(0))
+            assert yi[n] == np.float32(float(exact)), (wfmt, n)
+
+
 # ----------------------------------------------------------------------------- RMSNorm
 def check_rmsnorm_closed_forms():
     r = _rng(5)
@@ -377,6 +456,7 @@ def check_decode_against_numpy(steps: int = 3):
 ALL_CHECKS = [
     check_f16_decode_exhaustive, check_bf16_round_nearest_even, check_int4_codes_by_hand,
     check_int8_onehot, check_gemv_ones_closed_form, check_gemv_bruteforce,
+    check_act_i8_by_hand, check_act_i8_invariants, check_gemv_a8_against_dequantized_activations,
     check_rmsnorm_closed_forms, check_rope_invariants, check_rope_textbook_cases,
     check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
     check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,

@@ -50,6 +50,17 @@ MUTANTS = [
     ("step_embed_row", [("head->embed[(int64_t)token * H + i]",
                          "head->embed[(int64_t)token * H + (H - 1 - i)]")]),
     ("argmax_last_tie", [("v[i] > v[best]", "v[i] >= v[best]")]),
+    ("a8_round_trunc", [("float r = rintf(t);", "float r = truncf(t);")]),
+    ("a8_round_half_away", [("float r = rintf(t);", "float r = roundf(t);")]),
+    ("a8_signed_amax", [("const float a = fabsf(xg[i]);", "const float a = xg[i];")]),
+    ("a8_scale_128", [("sx[g] = amax / 127.0f;", "sx[g] = amax / 128.0f;")]),
+    ("a8_first_group_scale", [("acc += ws * (double)sx[g] * (double)isum;",
+                               "acc += ws * (double)sx[0] * (double)isum;")]),
+    ("a8_zero_point", [("isum += (int64_t)(nib - 8) * q[k];", "isum += (int64_t)(nib - 7) * q[k];")]),
+    ("a8_nibble_order", [("(k % 2 == 0) ? (b[k / 2] & 0x0F) : (b[k / 2] >> 4);",
+                          "(k % 2 == 0) ? (b[k / 2] >> 4) : (b[k / 2] & 0x0F);")]),
+    ("a8_drop_residual", [("if (residual != NULL) acc += (double)residual[n];", "")]),
+    ("a8_drop_bias", [("if (bias != NULL) acc += (double)bias[n];", "")]),
 ]
 
 

@@ -81,6 +81,72 @@ def dominant_kernel_bytes(wl) -> int:
     return N * K + N * 4
 
 
+def gemv_ab(wl, reps: int = 50):
+    """A/B of the two GEMV activation paths at the workload's GEMV shapes: fp32 activations
+    (qdec_gemv_*) against INT8 activations (qdec_quantize_act_i8 + qdec_gemv_*_a8).  Each shape
+    streams copies of its weights totalling >= 1 GiB in rotation, so every launch reads HBM; the
+    averages come from one HIP event pair around `reps` back-to-back launches on the launch stream."""
+    import quantized_gemv_gqa_amd as q
+    dev = "cuda:0"
+    H, I, D = wl.hidden, wl.inter, wl.head_dim
+    shapes = [("qkv", (wl.n_heads + 2 * wl.n_kv_heads) * D, H), ("o", H, wl.n_heads * D), ("gate_up", 2 * I, H),
+              ("down", H, I)]
+    if wl.has_lm_head:
+        shapes.append(("lm_head", wl.vocab, H))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    stream = torch.cuda.Stream()
+    rows = []
+    for name, N, K in shapes:
+        wf = q.W_Q4 if wl.wfmt == "q4" else q.W_Q8
+        wbytes = q.lib().qdec_packed_weight_bytes(wf, N, K)
+        sbytes = q.lib().qdec_packed_scale_bytes(wf, N, K, wl.group)
+        copies = max(2, -(-(1 << 30) // (wbytes + sbytes)))
+        Ws, Ss = [], []
+        for _ in range(copies):  # any bytes are valid codes; scales of the synthetic model's range
+            Ws.append(torch.randint(0, 256, (wbytes,), dtype=torch.uint8, device=dev, generator=gen))
+            if wl.wfmt == "q4":
+                Ss.append((torch.rand(sbytes // 2, device=dev, generator=gen) * 0.015 + 0.005).half().view(torch.int16))
+            else:
+                Ss.append(torch.rand(sbytes // 4, device=dev, generator=gen) * (0.02 / 127))
+        x = torch.randn(K, device=dev, generator=gen)
+        y = torch.empty(N, device=dev)
+        qa = torch.empty(K, dtype=torch.int8, device=dev)
+        sx = torch.empty(K // wl.group, device=dev)
+        ws = q.gemv_workspace(wl.wfmt, N, K, dev)
+        calls = {
+            "fp32_act": lambda i: q.gemv(wl.wfmt, Ws[i % copies], Ss[i % copies], x, N, y=y, workspace=ws,
+                                         group=wl.group, stream=stream),
+            "int8_act_gemv": lambda i: q.gemv_a8(wl.wfmt, Ws[i % copies], Ss[i % copies], qa, sx, N, y=y,
+                                                 workspace=ws, group=wl.group, stream=stream),
+            "quantize": lambda i: q.quantize_act_i8(x, wl.group, q=qa, sx=sx, stream=stream),
+        }
+        us = {}
+        with torch.cuda.stream(stream):
+            for key, fn in calls.items():
+                for i in range(3):
+                    fn(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(reps):
+                    fn(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us[key] = e0.elapsed_time(e1) * 1e3 / reps
+        wsb = wbytes * N // (((N + 63) // 64) * 64) + sbytes * N // (((N + 63) // 64) * 64)  # unpadded
+        fp_bytes = wsb + 4 * K + 4 * N
+        a8_bytes = wsb + K + 4 * (K // wl.group) + 4 * N
+        rows.append({"gemv": name, "N": N, "K": K, "us_fp32_act": us["fp32_act"], "us_int8_act_gemv": us["int8_act_gemv"],
+                     "us_quantize": us["quantize"], "us_int8_act_total": us["int8_act_gemv"] + us["quantize"],
+                     "gbps_fp32_act": fp_bytes / (us["fp32_act"] * 1e-6) / 1e9,
+                     "gbps_int8_act_gemv": a8_bytes / (us["int8_act_gemv"] * 1e-6) / 1e9,
+                     "speedup_gemv_only": us["fp32_act"] / us["int8_act_gemv"],
+                     "speedup_with_quantize": us["fp32_act"] / (us["int8_act_gemv"] + us["quantize"])})
+        del Ws, Ss
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +157,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=512,
                     help="size of one plain device copy run after the timed region (counter calibration)")
+    ap.add_argument("--gemv-ab", action="store_true",
+                    help="instead of the decode step: A/B of fp32- vs INT8-activation GEMVs at the workload's shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the decode step on a single MI355X; "
@@ -101,6 +169,10 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.gemv_ab:
+        torch.cuda.set_device(0)
+        print(json.dumps({"workload": wl.name, "weights": wl.wfmt, "group": wl.group, "gemv_ab": gemv_ab(wl)}))
+        return
     K, W = args.steps, args.warmup
     max_ctx = wl.ctx + W + K + 16
     t0 = time.time()

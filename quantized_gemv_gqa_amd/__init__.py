@@ -118,6 +118,11 @@ def lib():
         L.qdec_gemv_workspace_bytes.argtypes = [_I, _I, _I]; L.qdec_gemv_workspace_bytes.restype = Z
         L.qdec_gemv_q8.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _P, Z, _P]; L.qdec_gemv_q8.restype = S
         L.qdec_gemv_q4.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P, Z, _P]; L.qdec_gemv_q4.restype = S
+        L.qdec_quantize_act_i8.argtypes = [_P, _I, _I, _P, _P, _P]; L.qdec_quantize_act_i8.restype = S
+        L.qdec_gemv_q8_a8.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _P, Z, _P]
+        L.qdec_gemv_q8_a8.restype = S
+        L.qdec_gemv_q4_a8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, Z, _P]
+        L.qdec_gemv_q4_a8.restype = S
         L.qdec_rmsnorm_rope.argtypes = [_P, _P, _P, _I, _I, F, F, _P, _P]; L.qdec_rmsnorm_rope.restype = S
         L.qdec_swiglu.argtypes = [_P, _P, _P, _I, _P]; L.qdec_swiglu.restype = S
         L.qdec_argmax.argtypes = [_P, _I, _P, _P]; L.qdec_argmax.restype = S
@@ -145,6 +150,7 @@ def lib():
 EXPORTED = [
     "qdec_last_error", "qdec_version", "qdec_packed_weight_bytes", "qdec_packed_scale_bytes",
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
+    "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
     "qdec_step_kernel_count", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
@@ -220,6 +226,34 @@ def gemv(wfmt: str, Wp, Sp, x, N: int, bias=None, residual=None, y=None, workspa
         st = lib().qdec_gemv_q4(_ptr(Wp), _ptr(Sp), group, _ptr(x), _ptr(bias), _ptr(residual), _ptr(y),
                                 N, K, ws, wsb, _stream(stream))
     _check(st, "qdec_gemv_" + wfmt)
+    return y
+
+
+def quantize_act_i8(x, group: int = 64, q=None, sx=None, stream=None):
+    """INT8 activations with one fp32 scale per group of `group` k (Path A)."""
+    K = x.numel()
+    if q is None:
+        q = torch.empty(K, dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty(K // group, dtype=torch.float32, device=x.device)
+    _check(lib().qdec_quantize_act_i8(_ptr(x), K, group, _ptr(q), _ptr(sx), _stream(stream)), "qdec_quantize_act_i8")
+    return q, sx
+
+
+def gemv_a8(wfmt: str, Wp, Sp, q, sx, N: int, bias=None, residual=None, y=None, workspace=None,
+            group: int = 64, stream=None):
+    """GEMV on INT8 activations (q, sx from quantize_act_i8 with the same group)."""
+    K = q.numel()
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=q.device)
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    if wfmt == "q8":
+        st = lib().qdec_gemv_q8_a8(_ptr(Wp), _ptr(Sp), _ptr(q), _ptr(sx), group, _ptr(bias), _ptr(residual),
+                                   _ptr(y), N, K, ws, wsb, _stream(stream))
+    else:
+        st = lib().qdec_gemv_q4_a8(_ptr(Wp), _ptr(Sp), group, _ptr(q), _ptr(sx), _ptr(bias), _ptr(residual),
+                                   _ptr(y), N, K, ws, wsb, _stream(stream))
+    _check(st, "qdec_gemv_%s_a8" % wfmt)
     return y
 
 

@@ -142,6 +142,55 @@ qdec_status qdec_gemv_q4(const void *Wp, const uint16_t *Sp, int group, const fl
                      workspace_bytes, stream, "qdec_gemv_q4");
 }
 
+static bool pow2_group(int group) { return group >= 32 && group <= 4096 && (group & (group - 1)) == 0; }
+
+qdec_status qdec_quantize_act_i8(const float *x, int K, int group, int8_t *q, float *sx, void *stream) {
+  const char *nm = "qdec_quantize_act_i8";
+  QDEC_REQUIRE(x && q && sx, QDEC_EINVAL, "%s: null pointer", nm);
+  QDEC_REQUIRE(pow2_group(group), QDEC_EUNSUPPORTED, "%s: group must be 32 times a power of two (got %d)", nm, group);
+  QDEC_REQUIRE(K >= group && K % group == 0, QDEC_EINVAL, "%s: K must be a positive multiple of group (K=%d group=%d)",
+               nm, K, group);
+  const char *xb = reinterpret_cast<const char *>(x), *qb = reinterpret_cast<const char *>(q);
+  QDEC_REQUIRE(!(qb < xb + (size_t)K * 4 && xb < qb + K), QDEC_EINVAL, "%s: q must not overlap x", nm);
+  if (launch_quantize_act_i8(x, K, group, q, sx, (hipStream_t)stream) != hipSuccess) return check_launch(nm);
+  return QDEC_OK;
+}
+
+static qdec_status gemv_a8_common(int wfmt, const void *Wp, const void *Sp, int group, const int8_t *q,
+                                  const float *sx, const float *bias, const float *residual, float *y, int N,
+                                  int K, void *ws, size_t ws_bytes, void *stream, const char *name) {
+  QDEC_REQUIRE(Wp && Sp && q && sx && y, QDEC_EINVAL, "%s: null pointer", name);
+  QDEC_REQUIRE(N >= 1 && K >= 1, QDEC_EINVAL, "%s: N and K must be >= 1 (N=%d K=%d)", name, N, K);
+  QDEC_REQUIRE(pow2_group(group), QDEC_EUNSUPPORTED, "%s: group must be 32 times a power of two (got %d)", name,
+               group);
+  QDEC_REQUIRE(K % group == 0, QDEC_EINVAL, "%s: K must be a multiple of group (K=%d group=%d)", name, K, group);
+  QDEC_REQUIRE(aligned(Wp, 16) && aligned(q, 16) && aligned(sx, 4) && aligned(y, 4), QDEC_EINVAL,
+               "%s: packed weights and q must be 16-byte aligned", name);
+  if (ws) {
+    QDEC_REQUIRE(aligned(ws, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", name);
+    QDEC_REQUIRE(ws_bytes >= gemv_workspace_bytes(wfmt, N, K), QDEC_EINVAL, "%s: workspace too small (%zu < %zu bytes)",
+                 name, ws_bytes, gemv_workspace_bytes(wfmt, N, K));
+  }
+  if (launch_gemv_a8(wfmt, reinterpret_cast<const uint8_t *>(Wp), Sp, q, sx, group, bias, residual, y, N, K, ws,
+                     (hipStream_t)stream) != hipSuccess)
+    return check_launch(name);
+  return QDEC_OK;
+}
+
+qdec_status qdec_gemv_q8_a8(const void *Wp, const float *Sp, const int8_t *q, const float *sx, int group,
+                            const float *bias, const float *residual, float *y, int N, int K, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return gemv_a8_common(QDEC_W_Q8_ROW, Wp, Sp, group, q, sx, bias, residual, y, N, K, workspace, workspace_bytes,
+                        stream, "qdec_gemv_q8_a8");
+}
+
+qdec_status qdec_gemv_q4_a8(const void *Wp, const uint16_t *Sp, int group, const int8_t *q, const float *sx,
+                            const float *bias, const float *residual, float *y, int N, int K, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  return gemv_a8_common(QDEC_W_Q4_G_ZP8, Wp, Sp, group, q, sx, bias, residual, y, N, K, workspace, workspace_bytes,
+                        stream, "qdec_gemv_q4_a8");
+}
+
 qdec_status qdec_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
                               float eps, float rope_base, const int32_t *pos, void *stream) {
   QDEC_REQUIRE(x && y, QDEC_EINVAL, "qdec_rmsnorm_rope: null pointer");

@@ -371,6 +371,39 @@ __device__ __forceinline__ void compute_batch(float &acc, const GemvBatch<FMT, N
   __builtin_amdgcn_wave_barrier();  // the batch after next overwrites this slot
 }
 
+// Split-K hand-off between waves that may sit on different XCDs: partials travel as sc1
+// stores/loads (no L2 write-back or invalidate needed); a wave counts its arrival only after its
+// partial store is acknowledged, so the wave completing the count finds every partial.  Returns
+// false on every wave but the last of the tile; the last gets the tile's sum in acc, added in
+// split order (sc1 buffer loads, not atomics, so they pipeline), and resets the counter.
+__device__ __forceinline__ bool splitk_combine(float &acc, float *part, unsigned *counters, int tile, int ks, int ksi,
+                                               int lane) {
+  float *pp = part + (size_t)tile * ks * kTile + lane;
+  __hip_atomic_store(pp + (size_t)ksi * kTile, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  drain_stores();
+  unsigned *ctr = counters + tile * kLine;
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (unsigned)(ks - 1)) return false;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const __amdgpu_buffer_rsrc_t pr = rsrc(part + (size_t)tile * ks * kTile, (uint32_t)ks * kTile * 4);
+  acc = 0.f;
+  int i = 0;
+  for (; i + 8 <= ks; i += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, (i + j) * kTile * 4, kAuxSc1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += t[j];
+  }
+  for (; i < ks; ++i)
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, i * kTile * 4, kAuxSc1));
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // Greedy token over the tiles of an lm-head GEMV: every tile posts its (max, row) candidate; the
 // last tile of each group (tile mod kArgGroups) reduces its group, the last group reduces the
 // groups, writes the token and advances the step scalars.  Two levels, because same-line
@@ -512,36 +545,7 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
   }
   if constexpr (Q4) acc *= 16777216.0f;  // 2^24, exact
 
-  if (ks > 1) {
-    // Split-K hand-off between waves that may sit on different XCDs: partials travel as sc1
-    // stores/loads (no L2 write-back or invalidate needed); a wave counts its arrival only after
-    // its partial store is acknowledged, so the wave completing the count finds every partial.
-    float *pp = a.part + (size_t)tile * ks * kTile + lane;
-    __hip_atomic_store(pp + (size_t)ksi * kTile, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    drain_stores();
-    unsigned *ctr = a.counters + tile * kLine;
-    unsigned prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (unsigned)(ks - 1)) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // sc1 buffer loads (not atomics, so they pipeline), summed in a fixed order so the result
-    // does not depend on which wave arrived last
-    const __amdgpu_buffer_rsrc_t pr = rsrc(a.part + (size_t)tile * ks * kTile, (uint32_t)ks * kTile * 4);
-    acc = 0.f;
-    int i = 0;
-    for (; i + 8 <= ks; i += 8) {
-      float t[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        t[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, (i + j) * kTile * 4, kAuxSc1));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += t[j];
-    }
-    for (; i < ks; ++i)
-      acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, i * kTile * 4, kAuxSc1));
-    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (ks > 1 && !splitk_combine(acc, a.part, a.counters, tile, ks, ksi, lane)) return;
 
   // ------------------------------------------------------------------ epilogue (one tile)
   float v = acc;

@@ -82,6 +82,11 @@ size_t gemv_workspace_bytes(int wfmt, int N, int K, bool argmax = false);
 void gemv_bind_workspace(GemvArgs &a, const GemvPlan &p, void *ws);
 hipError_t launch_gemv(int wfmt, const GemvArgs &a, const GemvPlan &p, hipStream_t st);
 
+// INT8 activations (gemv_a8.hip): per-group quantisation, and the GEMV on packed weights.
+hipError_t launch_quantize_act_i8(const float *x, int K, int group, int8_t *q, float *sx, hipStream_t st);
+hipError_t launch_gemv_a8(int wfmt, const uint8_t *W, const void *S, const int8_t *q, const float *sx, int group,
+                          const float *bias, const float *residual, float *y, int N, int K, void *ws, hipStream_t st);
+
 hipError_t launch_pack_q8(const int8_t *W, const float *S, int N, int K, uint8_t *Wp, float *Sp,
                           hipStream_t st);
 hipError_t launch_pack_q4(const uint8_t *W, const uint16_t *S, int N, int K, int group, uint8_t *Wp,

@@ -82,6 +82,26 @@ def test_gemv_rejects_bad_arguments(L):
     assert st == q.QDEC_EINVAL and "workspace too small" in _err(L)
 
 
+def test_int8_activation_calls_reject_bad_arguments(L):
+    assert L.qdec_quantize_act_i8(None, 128, 64, FAKE, FAKE, None) == q.QDEC_EINVAL
+    st = L.qdec_quantize_act_i8(FAKE, 128, 48, FAKE + 4096, FAKE + 8192, None)
+    assert st == q.QDEC_EUNSUPPORTED and "group" in _err(L)
+    st = L.qdec_quantize_act_i8(FAKE, 96, 64, FAKE + 4096, FAKE + 8192, None)
+    assert st == q.QDEC_EINVAL and "multiple of group" in _err(L)
+    st = L.qdec_quantize_act_i8(FAKE, 128, 64, FAKE + 256, FAKE + 8192, None)
+    assert st == q.QDEC_EINVAL and "overlap" in _err(L)
+    st = L.qdec_gemv_q8_a8(FAKE, FAKE, None, FAKE, 64, None, None, FAKE, 10, 128, None, 0, None)
+    assert st == q.QDEC_EINVAL and "null" in _err(L)
+    st = L.qdec_gemv_q8_a8(FAKE, FAKE, FAKE, FAKE, 16, None, None, FAKE, 10, 128, None, 0, None)
+    assert st == q.QDEC_EUNSUPPORTED and "group" in _err(L)
+    st = L.qdec_gemv_q4_a8(FAKE, FAKE, 64, FAKE, FAKE, None, None, FAKE, 10, 96, None, 0, None)
+    assert st == q.QDEC_EINVAL and "multiple of group" in _err(L)
+    st = L.qdec_gemv_q4_a8(FAKE, FAKE, 64, FAKE + 4, FAKE, None, None, FAKE, 10, 128, None, 0, None)
+    assert st == q.QDEC_EINVAL and "aligned" in _err(L)
+    st = L.qdec_gemv_q4_a8(FAKE, FAKE, 64, FAKE, FAKE, None, None, FAKE, 10, 128, FAKE, 16, None)
+    assert st == q.QDEC_EINVAL and "workspace too small" in _err(L)
+
+
 def test_pack_rejects_bad_arguments(L):
     assert L.qdec_pack_q8(None, FAKE, 4, 16, FAKE, FAKE, None) == q.QDEC_EINVAL
     assert L.qdec_pack_q8(FAKE, FAKE, 4, 24, FAKE, FAKE, None) == q.QDEC_EINVAL

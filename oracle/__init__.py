@@ -85,6 +85,10 @@ def lib(path: str | None = None):
         L.orc_attention.argtypes = [_P, _P, _P, I, _P, I, I, I, I, I, D, _P, _P]
         L.orc_attention.restype = None
         L.orc_argmax.argtypes = [_P, I]; L.orc_argmax.restype = I
+        U64 = ctypes.c_uint64
+        L.orc_philox4x64_10.argtypes = [_P, _P, _P]; L.orc_philox4x64_10.restype = None
+        L.orc_sample_uniform.argtypes = [U64, I64, I64]; L.orc_sample_uniform.restype = D
+        L.orc_sample.argtypes = [_P, I, D, I, D, U64, I64]; L.orc_sample.restype = I
         L.orc_decode_step.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Layer),
                                       ctypes.POINTER(_Head), _P, I, I, _P, _P, _P, I]
         L.orc_decode_step.restype = I
@@ -209,6 +213,24 @@ def attention(q, k_pool, v_pool, kv_fmt, page_table, T, page_size=16, scale=None
     lib().orc_attention(_p(q), _p(k_pool), _p(v_pool), _kvfmt(kv_fmt), _p(pt), page_size, int(T),
                         Hq, Hkv, D, float(sc), _p(out), _p(pr))
     return (out, pr) if probs else out
+
+
+def philox4x64_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, np.uint64)
+    k = np.ascontiguousarray(key, np.uint64)
+    out = np.empty(4, np.uint64)
+    lib().orc_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sample_uniform(seed: int, step: int, i: int) -> float:
+    return float(lib().orc_sample_uniform(seed, step, i))
+
+
+def sample(logits, temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0, step: int = 0) -> int:
+    """Temperature / top-k / top-p sampling with a Gumbel-max draw keyed by (seed, step)."""
+    v = np.ascontiguousarray(logits, np.float32)
+    return int(lib().orc_sample(_p(v), v.size, temperature, top_k, top_p, seed, step))
 
 
 def argmax(v) -> int:

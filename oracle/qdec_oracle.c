@@ -30,6 +30,7 @@
  *  - Residual wiring: pre-norm, h += o_proj(attn(...)), h += down(swiglu(...)).
  *  - Greedy tie-break: smallest index.
  *  - INT8 activations: symmetric per group, s = max|x|/127, round half to even in binary32.
+ *  - Sampling: temperature, then top-k, then top-p, then a Gumbel-max draw keyed by Philox.
  */
 #include "qdec_oracle.h"
 
@@ -318,6 +319,107 @@ int orc_argmax(const float *v, int n) {
   for (int i = 0; i < n; ++i)
     if (v[i] == v[i] && (best < 0 || v[i] > v[best])) best = i;
   return best;
+}
+
+/* ---------------------------------------------------------------- sampling
+ *
+ * [FQ "Local benchmark": the chat flags --temperature, --top-p, --top-k, --seed and the Qwen3
+ * recommended 0.6 / 0.95 / 20; FQ "Optimization study" stage 5 (greedy on the GPU, sampling
+ * still copied the logits out); NQ "Sampler" (greedy takes the largest, top-k draws at random
+ * among the k most probable tokens).]  The pages fix neither the order of the filters nor the
+ * random source.  The reading:
+ *   - temperature <= 0: greedy (orc_argmax);
+ *   - z_i = l_i / T in fp64;
+ *   - top-k (0 < k < V): the k largest logits, equal logits ordered by smaller index first;
+ *   - top-p (p < 1): within that set in the same order, the shortest prefix whose softmax mass
+ *     (fp64, exp(z - z_max) summed in that order) reaches p of the set's total;
+ *   - the draw: Gumbel-max over the kept set, token = argmax of fp32(z_i + g_i) with
+ *     g_i = -ln(-ln u_i), smallest index on equal keys.  u_i is uniform in (0, 1): the 64-bit
+ *     word (i mod 4) of Philox4x64-10 with key (seed, 0) and counter (floor(i / 4), step, 0, 0),
+ *     as ((word >> 11) + 0.5) * 2^-53.  Gumbel-max draws token i with probability
+ *     exp(z_i) / sum over the kept set of exp(z_j).
+ * Logits are finite. */
+
+/* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+ * SC'11): ten rounds of two 64x64 -> 128-bit multiplications with the published multipliers
+ * and Weyl key increments. */
+void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+  uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    const unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * c0;
+    const unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * c2;
+    const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B97F4A7C15ull;
+    k1 += 0xBB67AE8584CAA73Bull;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+double orc_sample_uniform(uint64_t seed, int64_t step, int64_t i) {
+  const uint64_t ctr[4] = {(uint64_t)i >> 2, (uint64_t)step, 0, 0}, key[2] = {seed, 0};
+  uint64_t w[4];
+  orc_philox4x64_10(ctr, key, w);
+  return ((double)(w[i & 3] >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+}
+
+typedef struct {
+  float l;
+  int i;
+} orc_li;
+
+static int orc_li_desc(const void *a, const void *b) {
+  const orc_li *x = (const orc_li *)a, *y = (const orc_li *)b;
+  if (x->l != y->l) return x->l > y->l ? -1 : 1;
+  return x->i - y->i;
+}
+
+int orc_sample(const float *logits, int V, double temperature, int top_k, double top_p, uint64_t seed,
+               int64_t step) {
+  if (!(temperature > 0.0)) return orc_argmax(logits, V);
+  const int filt_k = top_k > 0 && top_k < V;
+  const int filt_p = top_p < 1.0;
+  int n = V;
+  orc_li *ord = NULL;
+  if (filt_k || filt_p) {
+    ord = (orc_li *)malloc(sizeof(orc_li) * (size_t)V);
+    for (int i = 0; i < V; ++i) {
+      ord[i].l = logits[i];
+      ord[i].i = i;
+    }
+    qsort(ord, (size_t)V, sizeof(orc_li), orc_li_desc);
+    if (filt_k) n = top_k;
+    if (filt_p) {
+      const double zmax = (double)ord[0].l / temperature;
+      double tot = 0.0;
+      for (int j = 0; j < n; ++j) tot += exp((double)ord[j].l / temperature - zmax);
+      double cum = 0.0;
+      for (int j = 0; j < n; ++j) {
+        cum += exp((double)ord[j].l / temperature - zmax);
+        if (cum >= top_p * tot) {
+          n = j + 1;
+          break;
+        }
+      }
+    }
+  }
+  float best = 0.0f;
+  int best_i = -1;
+  for (int j = 0; j < n; ++j) {
+    const int i = ord ? ord[j].i : j;
+    const double g = -log(-log(orc_sample_uniform(seed, step, i)));
+    const float key = (float)((double)logits[i] / temperature + g);
+    if (best_i < 0 || key > best || (key == best && i < best_i)) {
+      best = key;
+      best_i = i;
+    }
+  }
+  free(ord);
+  return best_i;
 }
 
 /* ---------------------------------------------------------------- one decode step */

@@ -61,6 +61,13 @@ void orc_attention(const float *q, const void *k_pool, const void *v_pool, int k
 /* smallest index among the maxima */
 int orc_argmax(const float *v, int n);
 
+/* Philox4x64-10; the uniform (0, 1) draw of token i at a step; temperature / top-k / top-p
+   sampling with a Gumbel-max draw (greedy when temperature <= 0) */
+void orc_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
+double orc_sample_uniform(uint64_t seed, int64_t step, int64_t i);
+int orc_sample(const float *logits, int V, double temperature, int top_k, double top_p, uint64_t seed,
+               int64_t step);
+
 typedef struct {
   int n_layers, hidden, n_heads, n_kv_heads, head_dim, inter, vocab;
   int wfmt, group, kv_fmt, page_size;

@@ -227,6 +227,116 @@ def check_gemv_a8_against_dequantized_activations():
             assert yi[n] == np.float32(float(exact)), (wfmt, n)
 
 
+# ----------------------------------------------------------------------------- sampling
+def _np_philox_words(ctr, key):
+    """Philox4x64-10 words of one counter from numpy's generator (it advances the counter before
+    each block, so it is started one below)."""
+    c = (ctr[0] | (ctr[1] << 64) | (ctr[2] << 128) | (ctr[3] << 192)) - 1
+    bg = np.random.Philox(key=key[0] | (key[1] << 64), counter=c % (1 << 256))
+    return bg.random_raw(4)
+
+
+def check_philox_against_numpy():
+    """Philox4x64-10 equals numpy's implementation; the all-zero case is the published known-answer
+    vector of the Random123 distribution."""
+    assert [int(v) for v in O.philox4x64_10([0, 0, 0, 0], [0, 0])] == [
+        0x16554D9ECA36314C, 0xDB20FE9D672D0FDC, 0xD7E772CEE186176B, 0x7E68B68AEC7BA23B]
+    r = _rng(21)
+    for _ in range(12):
+        ctr = [int(v) for v in r.integers(0, 2 ** 63, 4, dtype=np.int64)]
+        ctr[0] |= 1
+        key = [int(v) for v in r.integers(0, 2 ** 63, 2, dtype=np.int64)]
+        assert np.array_equal(O.philox4x64_10(ctr, key), _np_philox_words(ctr, key))
+
+
+def check_sample_uniform_against_numpy():
+    """u of token i at a step: word i mod 4 of the block (i // 4, step, 0, 0) keyed (seed, 0), as
+    ((word >> 11) + 0.5) 2^-53."""
+    for seed, step in ((0, 0), (7, 1), (2 ** 40 + 3, 12345)):
+        for i in (0, 1, 2, 3, 4, 7, 150001):
+            w = int(_np_philox_words([i // 4, step, 0, 0], [seed, 0])[i % 4])
+            assert O.sample_uniform(seed, step, i) == ((w >> 11) + 0.5) * 2.0 ** -53
+            assert 0.0 < O.sample_uniform(seed, step, i) < 1.0
+
+
+def _np_sample(lg, T, k, p, seed, step):
+    """Independent reading of the sampler: stable sort, cumulative mass, Gumbel keys from numpy's
+    Philox and Python's libm log."""
+    lg = np.asarray(lg, np.float32)
+    if T <= 0:
+        return int(np.argmax(lg))
+    V = lg.size
+    order = np.argsort(-lg.astype(np.float64), kind="stable")
+    keep = order
+    if 0 < k < V:
+        keep = keep[:k]
+    if p < 1.0:
+        z = lg[keep].astype(np.float64) / T
+        e = np.exp(z - z[0])
+        cum = np.cumsum(e)  # (summed in the same order as the oracle's loop)
+        tot = e.sum()
+        n = int(np.argmax(cum >= p * tot)) + 1
+        keep = keep[:n]
+    best, bi = None, None
+    for i in sorted(int(v) for v in keep):
+        w = int(_np_philox_words([i // 4, step, 0, 0], [seed, 0])[i % 4])
+        u = ((w >> 11) + 0.5) * 2.0 ** -53
+        key = np.float32(float(lg[i]) / T - math.log(-math.log(u)))
+        if best is None or key > best:
+            best, bi = key, i
+    return bi
+
+
+def check_sample_against_numpy_reading():
+    r = _rng(22)
+    lg = (2.0 * r.standard_normal(300)).astype(np.float32)
+    lg[[5, 77]] = lg.max()  # a tie at the top
+    for T, k, p in ((1.0, 0, 1.0), (0.6, 20, 0.95), (0.7, 0, 0.5), (1.3, 50, 1.0), (0.0, 20, 0.9), (2.0, 300, 0.99)):
+        for step in (0, 1, 9):
+            assert O.sample(lg, T, k, p, seed=11, step=step) == _np_sample(lg, T, k, p, 11, step), (T, k, p, step)
+
+
+def check_sample_special_cases():
+    """Greedy limits: temperature 0, top-k 1 and a vanishing top-p all give the argmax; top-k >= V
+    keeps everything; with equal logits top-k keeps the smallest indices, and a top-p mass that
+    lands exactly on a prefix boundary stops there."""
+    r = _rng(23)
+    lg = r.standard_normal(1000).astype(np.float32)
+    am = int(np.argmax(lg))
+    for step in range(5):
+        assert O.sample(lg, 0.0, seed=1, step=step) == am
+        assert O.sample(lg, 0.8, top_k=1, seed=1, step=step) == am
+        assert O.sample(lg, 0.8, top_p=1e-12, seed=1, step=step) == am
+        assert O.sample(lg, 0.8, top_k=1000, seed=1, step=step) == O.sample(lg, 0.8, seed=1, step=step)
+    eq = np.zeros(8, np.float32)
+    got_k = {O.sample(eq, 1.0, top_k=3, seed=5, step=s) for s in range(200)}
+    assert got_k == {0, 1, 2}
+    got_p = {O.sample(eq, 1.0, top_p=0.5, seed=5, step=s) for s in range(200)}  # mass 4/8 reached at 4
+    assert got_p == {0, 1, 2, 3}
+
+
+def _chi2(counts, probs, n):
+    exp = np.asarray(probs) * n
+    return float(((np.asarray(counts) - exp) ** 2 / exp).sum())
+
+
+def check_sample_frequencies():
+    """Gumbel-max draws follow the softmax of l / T over the kept set (chi-square, 20000 steps,
+    a bound a correct sampler exceeds with probability below 1e-6)."""
+    lg = np.array([1.0, 2.0, 0.5, 2.0, -1.0, 0.0], np.float32)
+    n = 20000
+    for T, k, keep in ((1.0, 0, [0, 1, 2, 3, 4, 5]), (0.5, 3, [0, 1, 3])):
+        z = lg[keep].astype(np.float64) / T
+        pr = np.exp(z - z.max())
+        pr /= pr.sum()
+        cnt = np.zeros(len(keep))
+        for step in range(n):
+            t = O.sample(lg, T, top_k=k, seed=99, step=step)
+            assert t in keep, (T, k, t)
+            cnt[keep.index(t)] += 1
+        assert _chi2(cnt, pr, n) < 40.0, (T, k, cnt, pr * n)
+
+
 # ----------------------------------------------------------------------------- RMSNorm
 def check_rmsnorm_closed_forms():
     r = _rng(5)
@@ -457,6 +567,8 @@ ALL_CHECKS = [
     check_f16_decode_exhaustive, check_bf16_round_nearest_even, check_int4_codes_by_hand,
     check_int8_onehot, check_gemv_ones_closed_form, check_gemv_bruteforce,
     check_act_i8_by_hand, check_act_i8_invariants, check_gemv_a8_against_dequantized_activations,
+    check_philox_against_numpy, check_sample_uniform_against_numpy, check_sample_against_numpy_reading,
+    check_sample_special_cases, check_sample_frequencies,
     check_rmsnorm_closed_forms, check_rope_invariants, check_rope_textbook_cases,
     check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
     check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,

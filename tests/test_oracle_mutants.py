@@ -61,6 +61,17 @@ MUTANTS = [
                           "(k % 2 == 0) ? (b[k / 2] >> 4) : (b[k / 2] & 0x0F);")]),
     ("a8_drop_residual", [("if (residual != NULL) acc += (double)residual[n];", "")]),
     ("a8_drop_bias", [("if (bias != NULL) acc += (double)bias[n];", "")]),
+    ("philox_multiplier", [("0xCA5A826395121157ull", "0xCA5A826395121155ull")]),
+    ("philox_nine_rounds", [("for (int r = 0; r < 10; ++r) {\n    const unsigned __int128",
+                             "for (int r = 0; r < 9; ++r) {\n    const unsigned __int128")]),
+    ("uniform_word", [("return ((double)(w[i & 3] >> 11)", "return ((double)(w[0] >> 11)")]),
+    ("uniform_counter_order", [("{(uint64_t)i >> 2, (uint64_t)step, 0, 0}", "{(uint64_t)step, (uint64_t)i >> 2, 0, 0}")]),
+    ("sample_temperature_mul", [("(float)((double)logits[i] / temperature + g)", "(float)((double)logits[i] * temperature + g)")]),
+    ("sample_gumbel_sign", [("const double g = -log(-log(", "const double g = log(-log(")]),
+    ("sample_topp_strict", [("if (cum >= top_p * tot) {", "if (cum > top_p * tot) {")]),
+    ("sample_topk_tie_order", [("  return x->i - y->i;", "  return y->i - x->i;")]),
+    ("sample_greedy_threshold", [("if (!(temperature > 0.0)) return orc_argmax", "if (!(temperature > 1.0)) return orc_argmax")]),
+    ("sample_topk_off_by_one", [("if (filt_k) n = top_k;", "if (filt_k) n = top_k + 1;")]),
 ]
 
 

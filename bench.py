@@ -174,6 +174,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=512,
                     help="size of one plain device copy run after the timed region (counter calibration)")
+    ap.add_argument("--sampling", default="",
+                    help="T,top_k,top_p: sample each token on the GPU (seed 1234) instead of greedy argmax")
     ap.add_argument("--gemv-ab", action="store_true",
                     help="instead of the decode step: A/B of fp32- vs INT8-activation GEMVs at the workload's shapes")
     args = ap.parse_args()
@@ -204,6 +206,11 @@ def main():
 
     stream = torch.cuda.Stream()
     st = q.DecodeStep(dm, dk, pos0=wl.ctx, token0=model.get("token", 0), log_len=W + K, device=dev)
+    sampling = None
+    if args.sampling:
+        T_s, k_s, p_s = args.sampling.split(",")
+        sampling = {"temperature": float(T_s), "top_k": int(k_s), "top_p": float(p_s), "seed": 1234}
+        st.set_sampling(sampling["temperature"], sampling["top_k"], sampling["top_p"], sampling["seed"])
     with torch.cuda.stream(stream):
         for _ in range(W):
             st.step(q.STEP_GRAPH)
@@ -276,7 +283,7 @@ def main():
                    "head_dim": wl.head_dim, "inter": wl.inter, "vocab": wl.vocab, "weights": "int4 g%d zp8 fp16 scales" % wl.group,
                    "kv": "paged bf16, 16-token pages, shuffled", "context": wl.ctx, "batch": 1,
                    "submission": "hipGraph replay per token", "kernels_per_step": st.kernel_count,
-                   "num_splits": st.cfg.num_splits},
+                   "num_splits": st.cfg.num_splits, "next_token": sampling or "greedy"},
         "step_bytes": bytes_timed / K,
         "step_gbps": gbps_step,
         "step_frac_of_peak": gbps_step / HBM_PEAK_GBPS,

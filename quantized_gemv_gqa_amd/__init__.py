@@ -123,6 +123,8 @@ def lib():
         L.qdec_gemv_q8_a8.restype = S
         L.qdec_gemv_q4_a8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, Z, _P]
         L.qdec_gemv_q4_a8.restype = S
+        L.qdec_sample_workspace_bytes.argtypes = []; L.qdec_sample_workspace_bytes.restype = Z
+        L.qdec_sample.argtypes = [_P, _I, F, _I, F, ctypes.c_uint64, _P, _P, _P, Z, _P]; L.qdec_sample.restype = S
         L.qdec_rmsnorm_rope.argtypes = [_P, _P, _P, _I, _I, F, F, _P, _P]; L.qdec_rmsnorm_rope.restype = S
         L.qdec_swiglu.argtypes = [_P, _P, _P, _I, _P]; L.qdec_swiglu.restype = S
         L.qdec_argmax.argtypes = [_P, _I, _P, _P]; L.qdec_argmax.restype = S
@@ -136,6 +138,7 @@ def lib():
                                        ctypes.POINTER(QdecState), ctypes.POINTER(_P)]
         L.qdec_step_create.restype = S
         L.qdec_decode_step.argtypes = [_P, _I, _P]; L.qdec_decode_step.restype = S
+        L.qdec_step_set_sampling.argtypes = [_P, F, _I, F, ctypes.c_uint64]; L.qdec_step_set_sampling.restype = S
         L.qdec_step_kernel_count.argtypes = [_P]; L.qdec_step_kernel_count.restype = _I
         L.qdec_step_destroy.argtypes = [_P]; L.qdec_step_destroy.restype = None
         L.qdec_step_fused_supported.argtypes = [_P]; L.qdec_step_fused_supported.restype = _I
@@ -150,10 +153,10 @@ def lib():
 EXPORTED = [
     "qdec_last_error", "qdec_version", "qdec_packed_weight_bytes", "qdec_packed_scale_bytes",
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
-    "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8",
+    "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8", "qdec_sample_workspace_bytes", "qdec_sample",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
-    "qdec_step_kernel_count", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
+    "qdec_step_kernel_count", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
     "qdec_step_phase_times", "qdec_step_wave_times", "qdec_step_fused_waves",
 ]
 
@@ -255,6 +258,23 @@ def gemv_a8(wfmt: str, Wp, Sp, q, sx, N: int, bias=None, residual=None, y=None, 
                                    _ptr(y), N, K, ws, wsb, _stream(stream))
     _check(st, "qdec_gemv_%s_a8" % wfmt)
     return y
+
+
+def sample_workspace(device="cuda"):
+    return torch.empty(lib().qdec_sample_workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def sample(logits, temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0, step=None,
+           token=None, workspace=None, stream=None):
+    """Next token from device logits (temperature / top-k / top-p, Gumbel-max draw keyed by
+    (seed, *step)); returns the device int32 token tensor."""
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=logits.device)
+    if workspace is None:
+        workspace = sample_workspace(logits.device)
+    _check(lib().qdec_sample(_ptr(logits), logits.numel(), temperature, top_k, top_p, seed, _ptr(step), _ptr(token),
+                             _ptr(workspace), workspace.numel(), _stream(stream)), "qdec_sample")
+    return token
 
 
 def rmsnorm_rope(x, gamma=None, eps: float = 1e-6, rope_base: float = 0.0, pos=None, out=None, stream=None):
@@ -439,6 +459,11 @@ class DecodeStep:
 
     def step(self, mode: int = STEP_EAGER, stream=None):
         _check(lib().qdec_decode_step(self.handle, mode, _stream(stream)), "qdec_decode_step")
+
+    def set_sampling(self, temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0):
+        """Sample later tokens (temperature / top-k / top-p, draw counter = step_count) instead of
+        taking the greedy argmax; temperature <= 0 goes back to greedy.  Drops captured graphs."""
+        _check(lib().qdec_step_set_sampling(self.handle, temperature, top_k, top_p, seed), "qdec_step_set_sampling")
 
     @property
     def kernel_count(self) -> int:

@@ -191,6 +191,31 @@ qdec_status qdec_gemv_q4_a8(const void *Wp, const uint16_t *Sp, int group, const
                         stream, "qdec_gemv_q4_a8");
 }
 
+size_t qdec_sample_workspace_bytes(void) { return sample_workspace_bytes(); }
+
+qdec_status qdec_sample(const float *logits, int V, float temperature, int top_k, float top_p, uint64_t seed,
+                        const int32_t *step, int32_t *token, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *nm = "qdec_sample";
+  QDEC_REQUIRE(logits && token && workspace, QDEC_EINVAL, "%s: null pointer", nm);
+  QDEC_REQUIRE(V >= 1, QDEC_EINVAL, "%s: V must be >= 1 (V=%d)", nm, V);
+  QDEC_REQUIRE(!std::isnan(temperature), QDEC_EINVAL, "%s: temperature is NaN", nm);
+  QDEC_REQUIRE(top_p > 0.f && top_p <= 1.f, QDEC_EINVAL, "%s: top_p must be in (0, 1] (got %g)", nm, (double)top_p);
+  QDEC_REQUIRE(top_k >= 0, QDEC_EINVAL, "%s: top_k must be >= 0 (got %d)", nm, top_k);
+  if (temperature > 0.f) {
+    QDEC_REQUIRE(top_k <= kSampleMaxTopK || top_k >= V, QDEC_EUNSUPPORTED, "%s: top_k above %d is not supported (got %d)",
+                 nm, kSampleMaxTopK, top_k);
+    QDEC_REQUIRE(top_p >= 1.f || (top_k >= 1 && top_k <= kSampleMaxTopK), QDEC_EUNSUPPORTED,
+                 "%s: top_p < 1 needs 1 <= top_k <= %d (got top_k=%d)", nm, kSampleMaxTopK, top_k);
+  }
+  QDEC_REQUIRE(aligned(workspace, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", nm);
+  QDEC_REQUIRE(workspace_bytes >= sample_workspace_bytes(), QDEC_EINVAL, "%s: workspace too small (%zu < %zu bytes)",
+               nm, workspace_bytes, sample_workspace_bytes());
+  if (launch_sample(logits, V, temperature, top_k, top_p, seed, step, token, nullptr, nullptr, nullptr, 0, workspace,
+                    (hipStream_t)stream) != hipSuccess)
+    return check_launch(nm);
+  return QDEC_OK;
+}
+
 qdec_status qdec_rmsnorm_rope(const float *x, const float *gamma, float *y, int rows, int dim,
                               float eps, float rope_base, const int32_t *pos, void *stream) {
   QDEC_REQUIRE(x && y, QDEC_EINVAL, "qdec_rmsnorm_rope: null pointer");

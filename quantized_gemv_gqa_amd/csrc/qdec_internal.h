@@ -87,6 +87,13 @@ hipError_t launch_quantize_act_i8(const float *x, int K, int group, int8_t *q, f
 hipError_t launch_gemv_a8(int wfmt, const uint8_t *W, const void *S, const int8_t *q, const float *sx, int group,
                           const float *bias, const float *residual, float *y, int N, int K, void *ws, hipStream_t st);
 
+// Sampling (sample.hip): temperature / top-k / top-p with a Philox-keyed Gumbel-max draw.
+constexpr int kSampleMaxTopK = 256;
+size_t sample_workspace_bytes();
+hipError_t launch_sample(const float *logits, int V, float temperature, int top_k, float top_p, uint64_t seed,
+                         const int32_t *step, int32_t *token, int32_t *token_log, int32_t *step_count, int32_t *pos,
+                         int log_len, void *ws, hipStream_t st);
+
 hipError_t launch_pack_q8(const int8_t *W, const float *S, int N, int K, uint8_t *Wp, float *Sp,
                           hipStream_t st);
 hipError_t launch_pack_q4(const uint8_t *W, const uint16_t *S, int N, int K, int group, uint8_t *Wp,

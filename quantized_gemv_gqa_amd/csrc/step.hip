@@ -41,6 +41,11 @@ struct qdec_step {
   hipStream_t graph_stream[2] = {nullptr, nullptr};
   int graph_kernels[2] = {0, 0};
   int n_kernels = 0;
+  // sampling of the next token (temperature > 0) instead of the greedy argmax
+  float temperature = 0.f, top_p = 1.f;
+  int top_k = 0;
+  uint64_t seed = 0;
+  void *sample_ws = nullptr;
   // persistent step
   bool fused_ok = false;
   int fused_blocks = 0;
@@ -54,7 +59,7 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, fused_layers, err, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, fused_layers, err, sample_ws, total;
   // persistent step
   size_t hB, xa, xb, ssqA, ssqB, sync, gu_flag, tile_cnt, cand, sub_cand, part[5];
   size_t part_bytes[5];
@@ -136,6 +141,7 @@ Layout layout_of(const qdec_config &c) {
   L.gemv_ws2 = off; off += align256(g);
   L.lsync = off; off += align256((32 + (size_t)c.n_layers * lsync_layer_words(c.n_kv_heads)) * 4);
   L.err = off; off += 256;
+  L.sample_ws = off; off += align256(sample_workspace_bytes());
   // persistent step: activations, sync lines, per-phase split state
   L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
   L.hB = off; off += align256((size_t)c.hidden * 4);
@@ -378,7 +384,17 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count, bool per_op) 
     QDEC_CK(launch_gemv(wf, d, h->p_down, st));
     if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace + (size_t)(l + 1) * H, H, st));
   }
-  if (h->model.w_lm) {
+  if (h->model.w_lm && h->temperature > 0.f) {
+    // lm head storing the logits, then the sampler (draw counter: the step count), which writes
+    // the token and advances the step scalars
+    GemvArgs a = gemv_args(h, h->model.w_lm, h->model.s_lm, s.hidden, s.logits, c.vocab, H, h->p_lm);
+    a.gamma = h->model.g_out;
+    a.epi = EPI_STORE;
+    QDEC_CK(launch_gemv(wf, a, h->p_lm, st));
+    QDEC_CK(launch_sample(s.logits, c.vocab, h->temperature, h->top_k, h->top_p, h->seed, s.step_count, s.token,
+                          s.token_log, s.step_count, s.pos, s.log_len, h->sample_ws, st));
+    ++n;  // (two launches)
+  } else if (h->model.w_lm) {
     // lm head with the greedy argmax, token write and position advance fused in its epilogue
     GemvArgs a = gemv_args(h, h->model.w_lm, h->model.s_lm, s.hidden, s.logits, c.vocab, H, h->p_lm);
     a.gamma = h->model.g_out;
@@ -542,6 +558,7 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   h->attn_ws = reinterpret_cast<float *>(ws + L.attn_ws);
   h->rope_cs = reinterpret_cast<double *>(ws + L.rope_cs);
   h->gemv_ws = ws + L.gemv_ws;
+  h->sample_ws = ws + L.sample_ws;
   h->ssq_n = (cfg->hidden + 63) / 64;
   const int qd = cfg->n_heads * cfg->head_dim;
   const int nqkv = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
@@ -578,6 +595,7 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
   if (base == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels, per_op);
   if (base == QDEC_STEP_FUSED) {
     QDEC_REQUIRE(!per_op, QDEC_EINVAL, "qdec_decode_step: QDEC_STEP_PER_OP does not apply to the fused step");
+    QDEC_REQUIRE(!(h->temperature > 0.f), QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step decodes greedily only");
     QDEC_REQUIRE(h->fused_ok, QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step is not available for this model");
     const int G = h->cfg.n_heads / h->cfg.n_kv_heads;
     hipError_t e = launch_fused(h->fa, h->cfg.wfmt, G, h->fused_blocks, st);
@@ -632,6 +650,35 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
 }
 
 int qdec_step_kernel_count(const qdec_step *h) { return h ? h->n_kernels : 0; }
+
+qdec_status qdec_step_set_sampling(qdec_step *h, float temperature, int top_k, float top_p, uint64_t seed) {
+  const char *nm = "qdec_step_set_sampling";
+  QDEC_REQUIRE(h, QDEC_EINVAL, "%s: null handle", nm);
+  QDEC_REQUIRE(!std::isnan(temperature), QDEC_EINVAL, "%s: temperature is NaN", nm);
+  QDEC_REQUIRE(top_p > 0.f && top_p <= 1.f, QDEC_EINVAL, "%s: top_p must be in (0, 1] (got %g)", nm, (double)top_p);
+  QDEC_REQUIRE(top_k >= 0, QDEC_EINVAL, "%s: top_k must be >= 0", nm);
+  if (temperature > 0.f) {
+    QDEC_REQUIRE(h->model.w_lm && h->state.step_count, QDEC_EINVAL, "%s: sampling needs an lm head and step_count", nm);
+    const int V = h->cfg.vocab;
+    QDEC_REQUIRE(top_k <= kSampleMaxTopK || top_k >= V, QDEC_EUNSUPPORTED, "%s: top_k above %d is not supported", nm,
+                 kSampleMaxTopK);
+    QDEC_REQUIRE(top_p >= 1.f || (top_k >= 1 && top_k <= kSampleMaxTopK), QDEC_EUNSUPPORTED,
+                 "%s: top_p < 1 needs 1 <= top_k <= %d", nm, kSampleMaxTopK);
+  }
+  h->temperature = temperature > 0.f ? temperature : 0.f;
+  h->top_k = top_k;
+  h->top_p = top_p;
+  h->seed = seed;
+  // captured graphs hold the old launch list: drop them (the next GRAPH call captures again)
+  for (int v = 0; v < 2; ++v) {
+    if (h->exec[v]) (void)hipGraphExecDestroy(h->exec[v]);
+    if (h->graph[v]) (void)hipGraphDestroy(h->graph[v]);
+    h->exec[v] = nullptr;
+    h->graph[v] = nullptr;
+    h->graph_stream[v] = nullptr;
+  }
+  return QDEC_OK;
+}
 
 int qdec_step_fused_supported(const qdec_step *h) { return h && h->fused_ok ? 1 : 0; }
 

@@ -102,6 +102,29 @@ def test_int8_activation_calls_reject_bad_arguments(L):
     assert st == q.QDEC_EINVAL and "workspace too small" in _err(L)
 
 
+def test_sample_rejects_bad_arguments(L):
+    WS = L.qdec_sample_workspace_bytes()
+    assert WS > 0
+    ok = dict(logits=FAKE, V=1000, temperature=0.7, top_k=20, top_p=0.9, seed=1, step=None, token=FAKE + 8192,
+              workspace=FAKE, workspace_bytes=WS, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.qdec_sample(*a.values())
+    assert call(logits=None) == q.QDEC_EINVAL
+    assert call(V=0) == q.QDEC_EINVAL
+    assert call(temperature=float("nan")) == q.QDEC_EINVAL
+    assert call(top_p=0.0) == q.QDEC_EINVAL and "top_p" in _err(L)
+    assert call(top_p=1.5) == q.QDEC_EINVAL
+    assert call(top_k=-1) == q.QDEC_EINVAL
+    assert call(top_k=0) == q.QDEC_EUNSUPPORTED and "top_p < 1" in _err(L)
+    assert call(top_k=300) == q.QDEC_EUNSUPPORTED
+    assert call(top_k=300, top_p=1.0) == q.QDEC_EUNSUPPORTED
+    assert call(workspace=FAKE + 16) == q.QDEC_EINVAL
+    assert call(workspace_bytes=WS - 1) == q.QDEC_EINVAL and "too small" in _err(L)
+
+
 def test_pack_rejects_bad_arguments(L):
     assert L.qdec_pack_q8(None, FAKE, 4, 16, FAKE, FAKE, None) == q.QDEC_EINVAL
     assert L.qdec_pack_q8(FAKE, FAKE, 4, 24, FAKE, FAKE, None) == q.QDEC_EINVAL

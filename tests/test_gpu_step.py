@@ -222,3 +222,34 @@ def test_fused_step_agrees_with_eager_across_page_boundary():
     for a, b in zip(ke + ve, kf + vf):  # the appended rows agree to bf16 rounding of near-equal inputs
         diff = np.abs(a.view(np.int16).astype(np.int32) - b.view(np.int16).astype(np.int32))
         assert diff.max() <= 2
+
+
+def test_step_sampling_matches_sampler_on_its_logits():
+    """Sampling inside the step: the logits meet the logits bar against the oracle, and the token
+    is exactly the sampler's draw (oracle) from those logits at draw counter = step count; graph
+    replays draw fresh numbers; greedy comes back when the temperature is set to 0."""
+    wl = synth.WORKLOADS["qwen2.5-7b-q4"]
+    p = Pair(wl, n_layers=2, trace=False, log_len=8)
+    T32, p32 = float(np.float32(0.7)), float(np.float32(0.9))
+    p.gpu.set_sampling(0.7, 40, 0.9, seed=5)
+    tok = p.model["token"]
+    toks = []
+    with torch.cuda.stream(torch.cuda.Stream()):
+        for s, mode in enumerate((q.STEP_EAGER, q.STEP_GRAPH, q.STEP_GRAPH, q.STEP_GRAPH)):
+            p.gpu.step(mode)
+            sync()
+            ref = p.oracle_step(p.pos0 + s, tok)
+            lg = host(p.gpu.logits)
+            assert float(np.abs(lg - ref["logits"]).max()) <= LOGIT_TOL
+            gtok = int(host(p.gpu.token)[0])
+            assert gtok == oracle.sample(lg, T32, 40, p32, seed=5, step=s), s
+            toks.append(gtok)
+            tok = gtok
+        with pytest.raises(q.QdecError):
+            p.gpu.step(q.STEP_FUSED)  # greedy only
+        p.gpu.set_sampling(0.0)
+        p.gpu.step(q.STEP_GRAPH)
+        sync()
+        assert int(host(p.gpu.token)[0]) == int(np.argmax(host(p.gpu.logits)))
+    assert host(p.gpu.token_log)[:4].tolist() == toks
+    assert int(host(p.gpu.step_count)[0]) == 5 and int(host(p.gpu.pos)[0]) == p.pos0 + 5

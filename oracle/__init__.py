@@ -85,6 +85,8 @@ def lib(path: str | None = None):
         L.orc_attention.argtypes = [_P, _P, _P, I, _P, I, I, I, I, I, D, _P, _P]
         L.orc_attention.restype = None
         L.orc_argmax.argtypes = [_P, I]; L.orc_argmax.restype = I
+        L.orc_decode_batch.argtypes = [_P, _P, _P, I, _P, I, _P, _P, _P, _P, _P, I]
+        L.orc_decode_batch.restype = None
         U64 = ctypes.c_uint64
         L.orc_philox4x64_10.argtypes = [_P, _P, _P]; L.orc_philox4x64_10.restype = None
         L.orc_sample_uniform.argtypes = [U64, I64, I64]; L.orc_sample_uniform.restype = D
@@ -275,6 +277,20 @@ class OracleDecoder:
             hd.w_lm, hd.s_lm = _p(model["w_lm"]), _p(model["s_lm"])
         self.head = hd
         self.h = np.zeros(wl.hidden, np.float32) if wl.has_lm_head else model["h0"].copy()
+
+    def step_batch(self, block_tables, pos, tokens, h):
+        """Batched step: row b of block_tables [B][max_blocks], pos[b] (< 0: idle), tokens[b], residual
+        streams h [B][H] (updated in place).  Returns (next tokens [B], logits [B][V])."""
+        bt = np.ascontiguousarray(block_tables, np.int32)
+        B, mb = bt.shape
+        ps = np.ascontiguousarray(pos, np.int32)
+        tk = np.ascontiguousarray(tokens, np.int32)
+        assert h.dtype == np.float32 and h.flags.c_contiguous and h.shape == (B, self.wl.hidden)
+        lg = np.zeros((B, self.wl.vocab), np.float32)
+        nxt = np.full(B, -1, np.int32)
+        lib().orc_decode_batch(ctypes.byref(self.cfg), self.layers, ctypes.byref(self.head), B, _p(bt), mb, _p(ps),
+                               _p(tk), _p(h), _p(lg), _p(nxt), self.nthreads)
+        return nxt, lg
 
     def step(self, pos: int, token: int = 0, trace: bool = False, logits: bool = True):
         wl = self.wl

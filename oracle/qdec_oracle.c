@@ -486,3 +486,22 @@ int orc_decode_step(const orc_config *c, const orc_layer *layers, const orc_head
   free(a); free(q); free(k); free(v); free(att); free(g); free(u); free(m);
   return next;
 }
+
+/* ---------------------------------------------------------------- batched decode
+ * [Systems "PagedAttention - Virtual Memory for KV Caches", "Continuous Batching", "Request
+ * Lifecycle" (decode: one new token per running sequence per step, all running sequences batched
+ * together; each sequence's block table maps its logical blocks to physical blocks of one shared
+ * pool, allocated on demand).]  Sequences in a batch do not interact: the batched step is the
+ * single-sequence step applied to every running slot with that slot's block table, position and
+ * token.  A slot with pos < 0 is idle and left untouched. */
+void orc_decode_batch(const orc_config *c, const orc_layer *layers, const orc_head *head, int B,
+                      const int32_t *block_tables, int max_blocks, const int32_t *pos, const int32_t *tokens,
+                      float *h, float *logits, int32_t *next, int nthreads) {
+  for (int b = 0; b < B; ++b) {
+    if (pos[b] < 0) continue;
+    next[b] = orc_decode_step(c, layers, head, block_tables + (int64_t)b * max_blocks, pos[b], tokens[b],
+                              h + (int64_t)b * c->hidden, NULL,
+                              logits ? logits + (int64_t)b * c->vocab : NULL, nthreads);
+  }
+}
+

@@ -99,6 +99,13 @@ int orc_decode_step(const orc_config *cfg, const orc_layer *layers, const orc_he
                     const int32_t *page_table, int pos, int token, float *h, float *trace,
                     float *logits, int nthreads);
 
+/* Batched decode: the single-sequence step for every slot b with pos[b] >= 0, with block table
+   row b ([B][max_blocks]), token tokens[b] and residual stream h[b] ([B][H]); logits [B][V] or
+   NULL; next[b] gets the greedy token (idle slots untouched). */
+void orc_decode_batch(const orc_config *c, const orc_layer *layers, const orc_head *head, int B,
+                      const int32_t *block_tables, int max_blocks, const int32_t *pos, const int32_t *tokens,
+                      float *h, float *logits, int32_t *next, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -287,3 +287,41 @@ def make_kv(wl: Workload, max_ctx: int, seed: int | None = None, n_layers: int |
                                seed, stream_id(name, l), 1.0)
             lst.append(a)
     return {"page_table": pt, "k": kp, "v": vp, "max_ctx": max_ctx, "ctx": ctx}
+
+
+def make_kv_batch(wl: Workload, ctxs, max_blocks: int, seed: int | None = None, n_layers: int | None = None,
+                  spare_pages: int = 0) -> dict:
+    """Shared per-layer K/V pools for a batch of sequences with their own block tables.
+
+    Sequence b holds ctxs[b] prior tokens (N(0,1) values, a different draw per sequence) in the
+    blocks its table row maps; the pool's physical pages are dealt to the sequences through a seeded
+    permutation, each sequence getting max_blocks of them (row b, unused rows entries -1 past
+    `spare_pages` pages left free for on-demand allocation).  Returns the block tables
+    [B][max_blocks], the pools, and the free page list.
+    """
+    seed = wl.seed if seed is None else seed
+    L = wl.n_layers if n_layers is None else n_layers
+    B = len(ctxs)
+    need = [-(-(c + 1) // wl.page_size) for c in ctxs]  # blocks holding the context and the next token
+    assert all(n <= max_blocks for n in need)
+    P = sum(need) + spare_pages
+    perm = permutation(P, seed, stream_id("pages"))
+    tables = np.full((B, max_blocks), -1, np.int32)
+    o = 0
+    for b in range(B):
+        tables[b, :need[b]] = perm[o:o + need[b]]
+        o += need[b]
+    free = [int(v) for v in perm[o:]]
+    dt = np.float32 if wl.kv_fmt == "f32" else np.uint16
+    fmt = 1 if wl.kv_fmt == "f32" else 2
+    shape = (P, wl.n_kv_heads, wl.page_size, wl.head_dim)
+    kp, vp = [], []
+    for l in range(L):
+        for name, lst in (("k_cache", kp), ("v_cache", vp)):
+            a = np.zeros(shape, dt)
+            for b in range(B):
+                row = np.ascontiguousarray(tables[b])
+                _L().synth_fill_kv(_p(a), fmt, _p(row), wl.page_size, int(ctxs[b]), wl.n_kv_heads, wl.head_dim,
+                                   seed + 7919 * (b + 1), stream_id(name, l), 1.0)
+            lst.append(a)
+    return {"block_tables": tables, "k": kp, "v": vp, "free_pages": free, "ctxs": list(ctxs)}

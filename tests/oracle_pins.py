@@ -563,6 +563,49 @@ def check_decode_against_numpy(steps: int = 3):
             tok = b["token"]
 
 
+def check_decode_batch_against_numpy():
+    """Batched step: every running slot equals the independent numpy decoder of that sequence alone
+    (its own block table into the shared pool, its own position and token); an idle slot is left
+    untouched; a block allocated on demand when a sequence crosses a page boundary is used."""
+    wl = S.tiny("q4", shuffled_pages=True)
+    m = S.make_model(wl)
+    ctxs = [15, 20, 9]
+    kv = S.make_kv_batch(wl, ctxs, max_blocks=4, spare_pages=3)
+    tables = kv["block_tables"].copy()
+    free = list(kv["free_pages"])
+    od = O.OracleDecoder(m, {"page_table": tables[0], "k": kv["k"], "v": kv["v"]})
+    nds = []
+    for b, c in enumerate(ctxs):
+        one = {"page_table": tables[b], "ctx": c, "k": kv["k"], "v": kv["v"]}
+        kl, vl = logical_kv(one, wl, wl.n_layers)
+        nds.append(NumpyDecoder(m, kl, vl))
+    toks = np.array([m["token"], 3, 11], np.int32)
+    pos = np.array(ctxs, np.int32)
+    h = np.zeros((3, wl.hidden), np.float32)
+    for step in range(3):
+        active = [True, step != 1, True]  # slot 1 sits out the second step
+        ps = np.where(active, pos, -1).astype(np.int32)
+        for b in range(3):  # on-demand block for the token about to be written
+            if active[b] and tables[b, pos[b] // wl.page_size] < 0:
+                tables[b, pos[b] // wl.page_size] = free.pop()
+        h_idle = h[1].copy()
+        nxt, lg = od.step_batch(tables, ps, toks, h)
+        for b in range(3):
+            if not active[b]:
+                assert nxt[b] == -1 and np.array_equal(h[b], h_idle)
+                continue
+            ref = nds[b].step(int(pos[b]), int(toks[b]))
+            assert np.allclose(lg[b], ref["logits"], rtol=0, atol=1e-5 * np.abs(ref["logits"]).max()), (step, b)
+            hl = ref["trace"][-1]
+            assert np.all(np.abs(h[b] - hl) <= 1e-5 * np.abs(hl).max()), (step, b)
+            srt = np.sort(ref["logits"].astype(np.float64))
+            if srt[-1] - srt[-2] > 1e-5 * abs(srt[-1]):
+                assert nxt[b] == ref["token"], (step, b)
+            toks[b] = ref["token"]
+            pos[b] += 1
+    assert (tables >= 0).sum() == sum(-(-(c + 1) // wl.page_size) for c in ctxs) + 1  # slot 0 crossed a page
+
+
 ALL_CHECKS = [
     check_f16_decode_exhaustive, check_bf16_round_nearest_even, check_int4_codes_by_hand,
     check_int8_onehot, check_gemv_ones_closed_form, check_gemv_bruteforce,
@@ -572,5 +615,5 @@ ALL_CHECKS = [
     check_rmsnorm_closed_forms, check_rope_invariants, check_rope_textbook_cases,
     check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
     check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,
-    check_decode_zero_weights_identity, check_decode_against_numpy,
+    check_decode_zero_weights_identity, check_decode_against_numpy, check_decode_batch_against_numpy,
 ]

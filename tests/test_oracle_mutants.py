@@ -72,6 +72,9 @@ MUTANTS = [
     ("sample_topk_tie_order", [("  return x->i - y->i;", "  return y->i - x->i;")]),
     ("sample_greedy_threshold", [("if (!(temperature > 0.0)) return orc_argmax", "if (!(temperature > 1.0)) return orc_argmax")]),
     ("sample_topk_off_by_one", [("if (filt_k) n = top_k;", "if (filt_k) n = top_k + 1;")]),
+    ("batch_first_table", [("block_tables + (int64_t)b * max_blocks, pos[b]", "block_tables, pos[b]")]),
+    ("batch_shared_hidden", [("h + (int64_t)b * c->hidden, NULL,", "h, NULL,")]),
+    ("batch_shared_logits", [("logits ? logits + (int64_t)b * c->vocab : NULL", "logits")]),
 ]
 
 

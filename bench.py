@@ -164,6 +164,62 @@ def gemv_ab(wl, reps: int = 40, replays: int = 5):
     return rows
 
 
+def batch_bench(wl, B: int, K: int, W: int):
+    """Batched decode: B sequences of the workload's context, one token each per step, one hipGraph
+    replay per step over a shared paged KV pool with per-sequence block tables (blocks for the
+    timed positions mapped before the timed region).  Throughput counts all B tokens of a step."""
+    import quantized_gemv_gqa_amd as q
+    import synth
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    model = synth.make_model(wl)
+    ctxs = [wl.ctx] * B
+    max_blocks = -(-(wl.ctx + W + K + 1) // 16)
+    kv = synth.make_kv_batch(wl, ctxs, max_blocks, spare_pages=B * (max_blocks - (wl.ctx + 1 + 15) // 16))
+    gen_s = time.time() - t0
+    tables, free = kv["block_tables"].copy(), list(kv["free_pages"])
+    for b in range(B):  # map every block the run will write (the host's on-demand allocation, done ahead)
+        for blk in range(max_blocks):
+            if tables[b, blk] < 0:
+                tables[b, blk] = free.pop()
+    dm = q.upload_model(model, dev)
+    dt = torch.int16 if wl.kv_fmt == "bf16" else None
+    kp = [torch.from_numpy(a.view(np.int16) if dt is not None else a).to(dev) for a in kv["k"]]
+    vp = [torch.from_numpy(a.view(np.int16) if dt is not None else a).to(dev) for a in kv["v"]]
+    del kv
+    d_tables = torch.from_numpy(tables).to(dev)
+    d_pos = torch.full((B,), wl.ctx, dtype=torch.int32, device=dev)
+    d_tok = torch.full((B,), int(model.get("token", 0)), dtype=torch.int32, device=dev)
+    splits = q.batch_splits(B, wl.n_kv_heads, wl.ctx)
+    bd = q.BatchDecode(dm, kp, vp, d_tables, d_pos, d_tok, num_splits=splits, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(W):
+            bd.step(q.STEP_GRAPH)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            bd.step(q.STEP_GRAPH)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    assert int(d_pos.min().item()) == wl.ctx + W + K
+    # algorithmic bytes of a step: every weight once, each sequence's KV once
+    T0 = wl.ctx + W + 1
+    one = sum(step_bytes(wl, T0 + i) for i in range(K)) / K
+    kv_one = 2 * wl.n_layers * wl.n_kv_heads * wl.head_dim * (2 if wl.kv_fmt == "bf16" else 4) * (T0 + K / 2)
+    step_b = one + (B - 1) * kv_one
+    return {"metric": "batched decode tokens/s, Qwen2.5-7B-shape INT4, 1 GPU", "value": B * K / (ms * K * 1e-3),
+            "unit": "tokens/s", "batch": B, "steps": K, "warmup": W, "ms_per_step": ms, "higher_is_better": True,
+            "data": "synthetic", "dtype": "f32",
+            "config": {"workload": wl.name, "sequences": B, "context_each": wl.ctx, "kv": "one shared paged bf16 pool, "
+                       "per-sequence block tables", "submission": "hipGraph replay per step",
+                       "kernels_per_step": bd.kernel_count, "num_splits": splits},
+            "step_bytes": step_b, "step_gbps": step_b / (ms * 1e-3) / 1e9, "gen_s": gen_s}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +232,8 @@ def main():
                     help="size of one plain device copy run after the timed region (counter calibration)")
     ap.add_argument("--sampling", default="",
                     help="T,top_k,top_p: sample each token on the GPU (seed 1234) instead of greedy argmax")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="instead of the batch-1 step: batched decode of this many sequences (1..8)")
     ap.add_argument("--gemv-ab", action="store_true",
                     help="instead of the decode step: A/B of fp32- vs INT8-activation GEMVs at the workload's shapes")
     args = ap.parse_args()
@@ -188,6 +246,9 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.batch:
+        print(json.dumps(batch_bench(wl, args.batch, args.steps, args.warmup)))
+        return
     if args.gemv_ab:
         torch.cuda.set_device(0)
         print(json.dumps({"workload": wl.name, "weights": wl.wfmt, "group": wl.group, "gemv_ab": gemv_ab(wl)}))

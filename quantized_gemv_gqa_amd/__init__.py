@@ -90,6 +90,12 @@ class QdecModel(ctypes.Structure):
                 ("w_lm", _P), ("s_lm", _P)]
 
 
+class QdecBatchState(ctypes.Structure):
+    _fields_ = [("k_pools", ctypes.POINTER(_P)), ("v_pools", ctypes.POINTER(_P)), ("block_tables", _P),
+                ("max_batch", _I), ("max_blocks", _I), ("pos", _P), ("tokens", _P), ("hidden", _P), ("logits", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class QdecState(ctypes.Structure):
     _fields_ = [("k_pools", ctypes.POINTER(_P)), ("v_pools", ctypes.POINTER(_P)),
                 ("page_table", _P), ("pos", _P), ("token", _P), ("hidden", _P), ("logits", _P),
@@ -123,6 +129,17 @@ def lib():
         L.qdec_gemv_q8_a8.restype = S
         L.qdec_gemv_q4_a8.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P, Z, _P]
         L.qdec_gemv_q4_a8.restype = S
+        L.qdec_gemm_workspace_bytes.argtypes = [_I, _I, _I, _I]; L.qdec_gemm_workspace_bytes.restype = Z
+        L.qdec_gemm_q8.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, Z, _P]; L.qdec_gemm_q8.restype = S
+        L.qdec_gemm_q4.argtypes = [_P, _P, _I, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, Z, _P]; L.qdec_gemm_q4.restype = S
+        L.qdec_batch_workspace_bytes.argtypes = [ctypes.POINTER(QdecConfig), _I]
+        L.qdec_batch_workspace_bytes.restype = Z
+        L.qdec_batch_create.argtypes = [ctypes.POINTER(QdecConfig), ctypes.POINTER(QdecModel),
+                                        ctypes.POINTER(QdecBatchState), ctypes.POINTER(_P)]
+        L.qdec_batch_create.restype = S
+        L.qdec_batch_decode_step.argtypes = [_P, _I, _P]; L.qdec_batch_decode_step.restype = S
+        L.qdec_batch_kernel_count.argtypes = [_P]; L.qdec_batch_kernel_count.restype = _I
+        L.qdec_batch_destroy.argtypes = [_P]; L.qdec_batch_destroy.restype = None
         L.qdec_sample_workspace_bytes.argtypes = []; L.qdec_sample_workspace_bytes.restype = Z
         L.qdec_sample.argtypes = [_P, _I, F, _I, F, ctypes.c_uint64, _P, _P, _P, Z, _P]; L.qdec_sample.restype = S
         L.qdec_rmsnorm_rope.argtypes = [_P, _P, _P, _I, _I, F, F, _P, _P]; L.qdec_rmsnorm_rope.restype = S
@@ -154,6 +171,8 @@ EXPORTED = [
     "qdec_last_error", "qdec_version", "qdec_packed_weight_bytes", "qdec_packed_scale_bytes",
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
     "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8", "qdec_sample_workspace_bytes", "qdec_sample",
+    "qdec_gemm_workspace_bytes", "qdec_gemm_q8", "qdec_gemm_q4", "qdec_batch_workspace_bytes", "qdec_batch_create",
+    "qdec_batch_decode_step", "qdec_batch_kernel_count", "qdec_batch_destroy",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
     "qdec_step_kernel_count", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
@@ -258,6 +277,28 @@ def gemv_a8(wfmt: str, Wp, Sp, q, sx, N: int, bias=None, residual=None, y=None, 
                                    _ptr(y), N, K, ws, wsb, _stream(stream))
     _check(st, "qdec_gemv_%s_a8" % wfmt)
     return y
+
+
+def gemm(wfmt: str, Wp, Sp, X, N: int, bias=None, residual=None, Y=None, workspace=None, group: int = 64,
+         stream=None):
+    """Skinny GEMM: Y [nb][N] = W X[b] for the rows of X [nb][K] (nb <= 8)."""
+    nb, K = X.shape
+    if Y is None:
+        Y = torch.empty((nb, N), dtype=torch.float32, device=X.device)
+    ws, wsb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel())
+    if wfmt == "q8":
+        st = lib().qdec_gemm_q8(_ptr(Wp), _ptr(Sp), _ptr(X), K, nb, _ptr(bias), _ptr(residual), _ptr(Y), Y.shape[1], N,
+                                K, ws, wsb, _stream(stream))
+    else:
+        st = lib().qdec_gemm_q4(_ptr(Wp), _ptr(Sp), group, _ptr(X), K, nb, _ptr(bias), _ptr(residual), _ptr(Y),
+                                Y.shape[1], N, K, ws, wsb, _stream(stream))
+    _check(st, "qdec_gemm_" + wfmt)
+    return Y
+
+
+def gemm_workspace(wfmt: str, N: int, K: int, nb: int, device="cuda"):
+    nbytes = lib().qdec_gemm_workspace_bytes(W_Q8 if wfmt == "q8" else W_Q4, N, K, nb)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def sample_workspace(device="cuda"):
@@ -392,7 +433,91 @@ def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 1) -> int:
     return int(max(1, min(s, 64)))
 
 
-# ----------------------------------------------------------------------------- decode step
+# ----------------------------------------------------------------------------- decode steps
+def batch_splits(batch: int, n_kv_heads: int, ctx: int) -> int:
+    """Attention splits for a batch: the batch-1 choice, capped so that batch * KV heads * splits
+    stays near 512 workgroups (two per compute unit; each unit is latency-bound, so more of them
+    only queue)."""
+    return int(max(1, min(default_splits(n_kv_heads, ctx), 512 // max(1, batch * n_kv_heads))))
+
+
+class BatchDecode:
+    """Batched decode of up to 8 sequences over one shared paged KV pool (libqdec batch handle).
+
+    The caller keeps `block_tables` ([max_batch][max_blocks] int32, device), `pos` and `tokens`
+    ([max_batch] int32, device) up to date between steps: a slot with pos < 0 is idle, and the block
+    of the position about to be written must be mapped before the step."""
+
+    def __init__(self, dev_model: dict, k_pools, v_pools, block_tables, pos, tokens, num_splits: int = 8,
+                 device="cuda"):
+        """num_splits: attention splits per (sequence, KV head); batch_splits() gives a choice that
+        keeps about two attention workgroups per compute unit."""
+        wl = dev_model["workload"]
+        self.wl = wl
+        L = len(dev_model["layers"])
+        B, mb = block_tables.shape
+        c = QdecConfig()
+        c.n_layers, c.hidden, c.n_heads, c.n_kv_heads = L, wl.hidden, wl.n_heads, wl.n_kv_heads
+        c.head_dim, c.inter, c.vocab = wl.head_dim, wl.inter, wl.vocab
+        c.wfmt, c.group = (W_Q8 if wl.wfmt == "q8" else W_Q4), wl.group
+        c.kv_fmt, c.page_size = (KV_F32 if wl.kv_fmt == "f32" else KV_BF16), PAGE
+        c.n_pages = k_pools[0].shape[0]
+        c.has_qkv_bias, c.has_qk_norm = int(wl.qkv_bias), int(wl.qk_norm)
+        c.num_splits = num_splits
+        c.rms_eps, c.rope_base = wl.eps, wl.rope_base
+        self.cfg = c
+        self.block_tables, self.pos, self.tokens = block_tables, pos, tokens
+        self._keep = [dev_model, k_pools, v_pools]
+        self.layer_arr = (QdecLayerWeights * L)()
+        for i, d in enumerate(dev_model["layers"]):
+            lw = self.layer_arr[i]
+            for n in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gu", "s_gu", "w_down", "s_down", "g_attn", "g_ffn"):
+                setattr(lw, n, _ptr(d[n]))
+            for n in ("b_qkv", "g_q", "g_k"):
+                setattr(lw, n, _ptr(d.get(n)))
+        m = QdecModel()
+        m.layers = self.layer_arr
+        m.embed, m.g_out = _ptr(dev_model["embed"]), _ptr(dev_model["g_out"])
+        m.w_lm, m.s_lm = _ptr(dev_model["w_lm"]), _ptr(dev_model["s_lm"])
+        self.model = m
+        self.hidden = torch.zeros((B, wl.hidden), dtype=torch.float32, device=device)
+        self.logits = torch.zeros((B, wl.vocab), dtype=torch.float32, device=device)
+        nbytes = lib().qdec_batch_workspace_bytes(ctypes.byref(c), B)
+        if nbytes == 0:
+            raise QdecError(QDEC_EINVAL, "qdec_batch_workspace_bytes")
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.kp = (_P * L)(*[_ptr(t) for t in k_pools[:L]])
+        self.vp = (_P * L)(*[_ptr(t) for t in v_pools[:L]])
+        s = QdecBatchState()
+        s.k_pools, s.v_pools = self.kp, self.vp
+        s.block_tables, s.max_batch, s.max_blocks = _ptr(block_tables), B, mb
+        s.pos, s.tokens, s.hidden, s.logits = _ptr(pos), _ptr(tokens), _ptr(self.hidden), _ptr(self.logits)
+        s.workspace, s.workspace_bytes = _ptr(self.workspace), nbytes
+        self.state = s
+        h = _P()
+        _check(lib().qdec_batch_create(ctypes.byref(c), ctypes.byref(m), ctypes.byref(s), ctypes.byref(h)),
+               "qdec_batch_create")
+        self.handle = h
+
+    def step(self, mode: int = STEP_EAGER, stream=None):
+        _check(lib().qdec_batch_decode_step(self.handle, mode, _stream(stream)), "qdec_batch_decode_step")
+
+    @property
+    def kernel_count(self) -> int:
+        return lib().qdec_batch_kernel_count(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().qdec_batch_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 class DecodeStep:
     """Owns the device state of one decode stream and a libqdec step handle."""
 

@@ -6,7 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 
-#include "qdec_internal.h"
+#include "qdec_batch.h"
 
 namespace qdec {
 
@@ -189,6 +189,68 @@ qdec_status qdec_gemv_q4_a8(const void *Wp, const uint16_t *Sp, int group, const
                             size_t workspace_bytes, void *stream) {
   return gemv_a8_common(QDEC_W_Q4_G_ZP8, Wp, Sp, group, q, sx, bias, residual, y, N, K, workspace, workspace_bytes,
                         stream, "qdec_gemv_q4_a8");
+}
+
+size_t qdec_gemm_workspace_bytes(int wfmt, int N, int K, int nb) {
+  if (N < 1 || K < 1 || nb < 1 || nb > 8 || (wfmt != QDEC_W_Q8_ROW && wfmt != QDEC_W_Q4_G_ZP8)) return 0;
+  return gemm_b_workspace_bytes(wfmt, N, K, gemm_b_columns(nb));
+}
+
+static qdec_status gemm_common(int wfmt, const void *Wp, const void *Sp, int group, const float *X, int ldx, int nb,
+                               const float *bias, const float *residual, float *Y, int ldy, int N, int K, void *ws,
+                               size_t ws_bytes, void *stream, const char *name) {
+  QDEC_REQUIRE(Wp && Sp && X && Y, QDEC_EINVAL, "%s: null pointer", name);
+  QDEC_REQUIRE(N >= 1 && K >= 1 && nb >= 1 && nb <= 8, QDEC_EINVAL, "%s: need N, K >= 1 and nb in [1, 8] (N=%d K=%d nb=%d)",
+               name, N, K, nb);
+  if (wfmt == QDEC_W_Q8_ROW) {
+    QDEC_REQUIRE(K % 16 == 0, QDEC_EINVAL, "%s: K must be a multiple of 16 (K=%d)", name, K);
+  } else {
+    QDEC_REQUIRE(group >= 32 && group <= 4096 && (group & (group - 1)) == 0, QDEC_EUNSUPPORTED,
+                 "%s: group must be 32 times a power of two (got %d)", name, group);
+    QDEC_REQUIRE(K % group == 0, QDEC_EINVAL, "%s: K must be a multiple of group (K=%d group=%d)", name, K, group);
+  }
+  QDEC_REQUIRE(ldx >= K && ldx % 4 == 0 && ldy >= N, QDEC_EINVAL, "%s: need ldx >= K, ldx %% 4 == 0, ldy >= N", name);
+  QDEC_REQUIRE(aligned(Wp, 16) && aligned(X, 16) && aligned(Y, 4), QDEC_EINVAL,
+               "%s: packed weights and X must be 16-byte aligned", name);
+  const char *xb = reinterpret_cast<const char *>(X), *yb = reinterpret_cast<const char *>(Y);
+  const size_t xn = ((size_t)(nb - 1) * ldx + K) * 4, yn = ((size_t)(nb - 1) * ldy + N) * 4;
+  QDEC_REQUIRE(!(xb < yb + yn && yb < xb + xn), QDEC_EINVAL, "%s: X must not overlap Y", name);
+  if (ws) {
+    QDEC_REQUIRE(aligned(ws, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", name);
+    QDEC_REQUIRE(ws_bytes >= gemm_b_workspace_bytes(wfmt, N, K, gemm_b_columns(nb)), QDEC_EINVAL,
+                 "%s: workspace too small", name);
+  }
+  GemmBArgs a{};
+  a.W = reinterpret_cast<const uint8_t *>(Wp);
+  a.S = Sp;
+  a.X = X;
+  a.ldx = ldx;
+  a.bias = bias;
+  a.residual = residual;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.nb = nb;
+  a.nb_max = gemm_b_columns(nb);
+  a.epi = EPI_STORE;
+  if (launch_gemm_b(wfmt, a, ws, (hipStream_t)stream) != hipSuccess) return check_launch(name);
+  return QDEC_OK;
+}
+
+qdec_status qdec_gemm_q8(const void *Wp, const float *Sp, const float *X, int ldx, int nb, const float *bias,
+                         const float *residual, float *Y, int ldy, int N, int K, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return gemm_common(QDEC_W_Q8_ROW, Wp, Sp, 0, X, ldx, nb, bias, residual, Y, ldy, N, K, workspace, workspace_bytes,
+                     stream, "qdec_gemm_q8");
+}
+
+qdec_status qdec_gemm_q4(const void *Wp, const uint16_t *Sp, int group, const float *X, int ldx, int nb,
+                         const float *bias, const float *residual, float *Y, int ldy, int N, int K, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return gemm_common(QDEC_W_Q4_G_ZP8, Wp, Sp, group, X, ldx, nb, bias, residual, Y, ldy, N, K, workspace,
+                     workspace_bytes, stream, "qdec_gemm_q4");
 }
 
 size_t qdec_sample_workspace_bytes(void) { return sample_workspace_bytes(); }

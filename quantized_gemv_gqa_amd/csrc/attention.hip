@@ -23,6 +23,7 @@
 #include <cmath>
 
 #include "qdec_attention.h"
+#include "qdec_batch.h"
 
 namespace qdec {
 
@@ -34,6 +35,24 @@ template <int D, int G, int KVF, bool ROPE>
 __global__ void __launch_bounds__(attn::kAttnThreads) attn_split(AttnArgs a) {
   __shared__ attn::AttnSmem<D, G, ROPE> sm;
   attn::attn_unit<D, G, KVF, ROPE, false>(a, blockIdx.x, blockIdx.y, sm);
+}
+
+// grid (Hkv, splits, B): the step form of the unit for sequence b, its pointers offset by b
+template <int D, int G, int KVF>
+__global__ void __launch_bounds__(attn::kAttnThreads) attn_split_batch(const AttnBatch ab) {
+  __shared__ attn::AttnSmem<D, G, true> sm;
+  const int b = blockIdx.z;
+  const int t = ab.pos[b];
+  if (t < 0 || t >= ab.max_blocks * 16) return;  // idle slot, or past its block table: skipped
+  AttnArgs a = ab.a;
+  a.qkv = ab.qkv + (size_t)b * (a.Hq + 2 * a.Hkv) * D;
+  a.rope_cs = ab.rope_cs + (size_t)b * D;
+  a.pos = ab.pos + b;
+  a.page_table = ab.tables + (size_t)b * ab.max_blocks;
+  a.counters = reinterpret_cast<unsigned *>(ab.ws + (size_t)b * ab.ws_stride);
+  a.ws = reinterpret_cast<float *>(ab.ws + (size_t)b * ab.ws_stride + kAttnCounterBytes);
+  a.out = ab.out + (size_t)b * a.Hq * D;
+  attn::attn_unit<D, G, KVF, true, false>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 __global__ void kv_append(const float *__restrict__ k, const float *__restrict__ v, void *k_pool,
@@ -74,7 +93,32 @@ hipError_t launch_g(const AttnArgs &a, int G, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int KVF>
+hipError_t launch_batch_g(const AttnBatch &ab, int G, hipStream_t st) {
+  dim3 grid(ab.a.Hkv, ab.a.splits, ab.B);
+  constexpr int kT = attn::kAttnThreads;
+  switch (G) {
+#define QDEC_G(g)                                                                            \
+  case g:                                                                                    \
+    hipLaunchKernelGGL((attn_split_batch<D, g, KVF>), grid, dim3(kT), 0, st, ab);            \
+    break;
+    QDEC_G(1) QDEC_G(2) QDEC_G(3) QDEC_G(4) QDEC_G(5) QDEC_G(6) QDEC_G(7) QDEC_G(8)
+#undef QDEC_G
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attention_batch(const AttnBatch &ab, hipStream_t st) {
+  const int G = ab.a.Hq / ab.a.Hkv;
+  if (ab.a.D == 128)
+    return ab.a.kv_fmt == QDEC_KV_BF16 ? launch_batch_g<128, QDEC_KV_BF16>(ab, G, st)
+                                       : launch_batch_g<128, QDEC_KV_F32>(ab, G, st);
+  return ab.a.kv_fmt == QDEC_KV_BF16 ? launch_batch_g<64, QDEC_KV_BF16>(ab, G, st)
+                                     : launch_batch_g<64, QDEC_KV_F32>(ab, G, st);
+}
 
 // [per-KV-head arrival counters, one 128-byte line each, zero between launches]
 // [splits][Hq][D] partial outputs, then [splits][Hq][2] partial (max, sum)

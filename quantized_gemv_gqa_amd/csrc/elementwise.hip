@@ -13,7 +13,7 @@
 
 #include <climits>
 
-#include "qdec_internal.h"
+#include "qdec_batch.h"
 
 namespace qdec {
 
@@ -227,6 +227,146 @@ __global__ void __launch_bounds__(1024) argmax_finish_k(const float *__restrict_
   }
 }
 
+// ------------------------------------------------------------------ rows of the batched step
+// grid (ceil(H / 256), B): h[b] = E[tokens[b]] for running rows; block (0, b) also writes row b's
+// RoPE table (the same angles as embed_k)
+__global__ void __launch_bounds__(256) embed_rows_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ tokens,
+                                                    const int32_t *__restrict__ pos, int H, int V, float *h, float base,
+                                                    int D, double *__restrict__ cs) {
+  const int b = blockIdx.y;
+  const int t = pos[b];
+  if (t < 0) return;
+  if (blockIdx.x == 0) {
+    double *c = cs + (size_t)b * D;
+    for (int k = threadIdx.x; k < D / 2; k += 256) {
+      const double theta = pow((double)base, -2.0 * (double)k / (double)D);
+      double sn, co;
+      sincos((double)t * theta, &sn, &co);
+      c[2 * k] = co;
+      c[2 * k + 1] = sn;
+    }
+  }
+  int tok = tokens[b];
+  if (tok < 0 || tok >= V) tok = 0;  // documented precondition; never read outside the table
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < H) h[(size_t)b * H + i] = __builtin_bit_cast(float, (uint32_t)E[(size_t)tok * H + i] << 16);
+}
+
+// one workgroup of 1024 threads per row: y = gamma * x / sqrt(mean(x^2) + eps); rows of a
+// multiple of 4 values are read and written as float4, each element loaded once into registers
+__global__ void __launch_bounds__(1024) rmsnorm_rows_k(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                       float *__restrict__ y, int dim, float eps) {
+  __shared__ float part[16];
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)blockIdx.x * dim);
+  float4 *yr = reinterpret_cast<float4 *>(y + (size_t)blockIdx.x * dim);
+  const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+  const int n4 = dim / 4;
+  constexpr int kMaxPer = 4;  // float4 per thread held in registers (rows up to 16384 values)
+  float4 v[kMaxPer];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + 1024 * k;
+    v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += part[w];
+  const float r = rsqrtf(tot / (float)dim + eps);
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + 1024 * k;
+    if (i < n4) {
+      const float4 g = g4[i];
+      yr[i] = make_float4(g.x * (v[k].x * r), g.y * (v[k].y * r), g.z * (v[k].z * r), g.w * (v[k].w * r));
+    }
+  }
+}
+
+// (value, index) reduction of one workgroup of 1024 threads: larger value, then smaller index
+__device__ __forceinline__ void block_argmax_1024(float &bv, int &bi, float *sv, int *si) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    si[tid >> 6] = bi;
+  }
+  __syncthreads();
+  bv = sv[0];
+  bi = si[0];
+  for (int w = 1; w < 16; ++w) {
+    const int i2 = si[w];
+    const float v2 = sv[w];
+    if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+}
+
+constexpr int kArgChunks = 64;  // workgroups per row in the first argmax pass
+
+// grid (kArgChunks, B): candidate (value, index) of chunk c of row b
+__global__ void __launch_bounds__(1024) argmax_rows_part_k(const float *__restrict__ logits, int V,
+                                                           const int32_t *__restrict__ pos, float *cv, int *ci) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int b = blockIdx.y;
+  if (pos[b] < 0) return;
+  const int chunk = (V + kArgChunks - 1) / kArgChunks;
+  const int i0 = blockIdx.x * chunk, i1 = min(V, i0 + chunk);
+  const float *lg = logits + (size_t)b * V;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int i = i0 + (int)threadIdx.x; i < i1; i += 1024) {
+    const float v = lg[i];
+    if (v == v && (bi == INT_MAX || v > bv)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  block_argmax_1024(bv, bi, sv, si);
+  if (threadIdx.x == 0) {
+    cv[b * kArgChunks + blockIdx.x] = bv;
+    ci[b * kArgChunks + blockIdx.x] = bi;
+  }
+}
+
+// one wave per row: tokens[b] = smallest index of the largest logit over the chunk candidates,
+// pos[b] += 1
+__global__ void __launch_bounds__(64) argmax_rows_k(const float *__restrict__ cv, const int *__restrict__ ci,
+                                                    int32_t *tokens, int32_t *pos) {
+  const int b = blockIdx.x;
+  if (pos[b] < 0) return;
+  const int tid = threadIdx.x;
+  float bv = cv[b * kArgChunks + tid];
+  int bi = ci[b * kArgChunks + tid];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  if (tid == 0) {
+    tokens[b] = (bi == INT_MAX) ? 0 : bi;
+    pos[b] += 1;
+  }
+}
+
 __global__ void copy_k(const float *__restrict__ s, float *__restrict__ d, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) d[i] = s[i];
 }
@@ -265,6 +405,29 @@ hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int3
                                 hipStream_t st) {
   hipLaunchKernelGGL(argmax_finish_k, dim3(1), dim3(1024), 0, st, logits, n, token, pos, token_log,
                      step_count, log_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_rows(const uint16_t *E, const int32_t *tokens, const int32_t *pos, int B, int H, int V,
+                             float *h, float rope_base, int D, double *rope_cs, hipStream_t st) {
+  hipLaunchKernelGGL(embed_rows_k, dim3((H + 255) / 256, B), dim3(256), 0, st, E, tokens, pos, H, V, h, rope_base, D,
+                     rope_cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(const float *x, const float *gamma, float *y, int B, int dim, float eps, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_rows_k, dim3(B), dim3(1024), 0, st, x, gamma, y, dim, eps);
+  return hipGetLastError();
+}
+
+size_t argmax_rows_workspace_bytes(int B) { return (size_t)B * kArgChunks * 8; }
+
+hipError_t launch_argmax_rows(const float *logits, int B, int V, int32_t *tokens, int32_t *pos, void *ws,
+                              hipStream_t st) {
+  float *cv = reinterpret_cast<float *>(ws);
+  int *ci = reinterpret_cast<int *>(cv + (size_t)B * kArgChunks);
+  hipLaunchKernelGGL(argmax_rows_part_k, dim3(kArgChunks, B), dim3(1024), 0, st, logits, V, pos, cv, ci);
+  hipLaunchKernelGGL(argmax_rows_k, dim3(B), dim3(64), 0, st, cv, ci, tokens, pos);
   return hipGetLastError();
 }
 

@@ -125,6 +125,22 @@ def test_sample_rejects_bad_arguments(L):
     assert call(workspace_bytes=WS - 1) == q.QDEC_EINVAL and "too small" in _err(L)
 
 
+def test_batch_and_gemm_validation(L):
+    c = _cfg(n_pages=600)
+    assert L.qdec_batch_workspace_bytes(ctypes.byref(c), 8) > 0
+    assert L.qdec_batch_workspace_bytes(ctypes.byref(c), 9) == 0
+    assert L.qdec_batch_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert L.qdec_batch_create(None, None, None, None) == q.QDEC_EINVAL
+    assert L.qdec_gemm_workspace_bytes(q.W_Q4, 4608, 3584, 8) > L.qdec_gemm_workspace_bytes(q.W_Q4, 4608, 3584, 2)
+    assert L.qdec_gemm_workspace_bytes(q.W_Q4, 4608, 3584, 9) == 0
+    st = L.qdec_gemm_q4(FAKE, FAKE, 64, FAKE, 128, 9, None, None, FAKE + (1 << 20), 10, 10, 128, None, 0, None)
+    assert st == q.QDEC_EINVAL and "nb" in _err(L)
+    st = L.qdec_gemm_q4(FAKE, FAKE, 64, FAKE, 126, 2, None, None, FAKE + (1 << 20), 10, 10, 126, None, 0, None)
+    assert st == q.QDEC_EINVAL
+    st = L.qdec_gemm_q8(FAKE, FAKE, FAKE, 128, 2, None, None, FAKE + 256, 10, 10, 128, None, 0, None)
+    assert st == q.QDEC_EINVAL and "overlap" in _err(L)
+
+
 def test_pack_rejects_bad_arguments(L):
     assert L.qdec_pack_q8(None, FAKE, 4, 16, FAKE, FAKE, None) == q.QDEC_EINVAL
     assert L.qdec_pack_q8(FAKE, FAKE, 4, 24, FAKE, FAKE, None) == q.QDEC_EINVAL

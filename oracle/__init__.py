@@ -87,6 +87,7 @@ def lib(path: str | None = None):
         L.orc_argmax.argtypes = [_P, I]; L.orc_argmax.restype = I
         L.orc_decode_batch.argtypes = [_P, _P, _P, I, _P, I, _P, _P, _P, _P, _P, I]
         L.orc_decode_batch.restype = None
+        L.orc_prefill.argtypes = [_P, _P, _P, _P, I, _P, I, _P, _P, I]; L.orc_prefill.restype = I
         U64 = ctypes.c_uint64
         L.orc_philox4x64_10.argtypes = [_P, _P, _P]; L.orc_philox4x64_10.restype = None
         L.orc_sample_uniform.argtypes = [U64, I64, I64]; L.orc_sample_uniform.restype = D
@@ -277,6 +278,15 @@ class OracleDecoder:
             hd.w_lm, hd.s_lm = _p(model["w_lm"]), _p(model["s_lm"])
         self.head = hd
         self.h = np.zeros(wl.hidden, np.float32) if wl.has_lm_head else model["h0"].copy()
+
+    def prefill(self, pos0: int, tokens):
+        """Prompt tokens at positions pos0 .. pos0 + T - 1 (stores their KV); returns the last
+        position's greedy token, logits and residual stream."""
+        tk = np.ascontiguousarray(tokens, np.int32)
+        lg = np.empty(self.wl.vocab, np.float32)
+        nxt = lib().orc_prefill(ctypes.byref(self.cfg), self.layers, ctypes.byref(self.head), _p(self.page_table),
+                                int(pos0), _p(tk), tk.size, _p(self.h), _p(lg), self.nthreads)
+        return {"token": nxt, "logits": lg, "h": self.h.copy()}
 
     def step_batch(self, block_tables, pos, tokens, h):
         """Batched step: row b of block_tables [B][max_blocks], pos[b] (< 0: idle), tokens[b], residual

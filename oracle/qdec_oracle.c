@@ -505,3 +505,18 @@ void orc_decode_batch(const orc_config *c, const orc_layer *layers, const orc_he
   }
 }
 
+/* ---------------------------------------------------------------- prefill
+ * [RT section 6 and FQ "Local benchmark": prefill runs the whole prompt through the model, writing
+ * its KV, and the first token comes from the last position's logits.]  A causal decoder's prefill
+ * of tokens t_0 .. t_{T-1} at positions pos0 .. pos0 + T - 1 is, by definition, the single-token
+ * step applied to each position in order: position p attends to keys 0 .. p.  Returns the greedy
+ * token of the last position; h and logits are those of the last position. */
+int orc_prefill(const orc_config *c, const orc_layer *layers, const orc_head *head, const int32_t *page_table,
+                int pos0, const int32_t *tokens, int T, float *h, float *logits, int nthreads) {
+  int next = -1;
+  for (int t = 0; t < T; ++t)
+    next = orc_decode_step(c, layers, head, page_table, pos0 + t, tokens[t], h, NULL, t == T - 1 ? logits : NULL,
+                           nthreads);
+  return next;
+}
+

@@ -106,6 +106,11 @@ void orc_decode_batch(const orc_config *c, const orc_layer *layers, const orc_he
                       const int32_t *block_tables, int max_blocks, const int32_t *pos, const int32_t *tokens,
                       float *h, float *logits, int32_t *next, int nthreads);
 
+/* Prefill: the single-token step for tokens[t] at position pos0 + t, t = 0 .. T-1, in order;
+   h and logits (optional) are the last position's; returns its greedy token. */
+int orc_prefill(const orc_config *c, const orc_layer *layers, const orc_head *head, const int32_t *page_table,
+                int pos0, const int32_t *tokens, int T, float *h, float *logits, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

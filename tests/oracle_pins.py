@@ -20,7 +20,7 @@ import torch
 import oracle as O
 import synth as S
 
-from np_decoder import NumpyDecoder, logical_kv
+from np_decoder import NumpyDecoder, bf16_bits_to_f32, logical_kv
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -606,6 +606,37 @@ def check_decode_batch_against_numpy():
     assert (tables >= 0).sum() == sum(-(-(c + 1) // wl.page_size) for c in ctxs) + 1  # slot 0 crossed a page
 
 
+def check_prefill_against_numpy():
+    """Prefill of a 21-token prompt after 9 cached tokens (crossing a page boundary): the last
+    position's logits and the KV of every prompt position against the independent numpy decoder
+    stepping through the prompt."""
+    wl = S.tiny("q4", shuffled_pages=True)
+    m = S.make_model(wl)
+    ctx, T = 9, 21
+    kv = S.make_kv(wl, ctx + T + 4, ctx=ctx)
+    wl9 = replace(wl, ctx=ctx)
+    od = O.OracleDecoder(m, kv)
+    kl, vl = logical_kv(kv, wl9, wl.n_layers)
+    nd = NumpyDecoder(m, kl, vl)
+    toks = (np.arange(T) * 7 + 3) % wl.vocab
+    r = od.prefill(ctx, toks)
+    ref = None
+    for t in range(T):
+        ref = nd.step(ctx + t, int(toks[t]))
+    assert np.allclose(r["logits"], ref["logits"], rtol=0, atol=1e-5 * np.abs(ref["logits"]).max())
+    srt = np.sort(ref["logits"].astype(np.float64))
+    if srt[-1] - srt[-2] > 1e-5 * abs(srt[-1]):
+        assert r["token"] == ref["token"]
+    pt = kv["page_table"]
+    for l in range(wl.n_layers):
+        for t in range(ctx, ctx + T):
+            for pool, lst in ((od.k[l], nd.K[l]), (od.v[l], nd.V[l])):
+                got = pool[pt[t // wl.page_size], :, t % wl.page_size, :]
+                got = got.astype(np.float32) if wl.kv_fmt == "f32" else bf16_bits_to_f32(got)
+                want = np.asarray(lst[t], np.float32)
+                assert np.allclose(got, want, rtol=0, atol=1e-5 * max(1e-30, np.abs(want).max())), (l, t)
+
+
 ALL_CHECKS = [
     check_f16_decode_exhaustive, check_bf16_round_nearest_even, check_int4_codes_by_hand,
     check_int8_onehot, check_gemv_ones_closed_form, check_gemv_bruteforce,
@@ -616,4 +647,5 @@ ALL_CHECKS = [
     check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
     check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,
     check_decode_zero_weights_identity, check_decode_against_numpy, check_decode_batch_against_numpy,
+    check_prefill_against_numpy,
 ]

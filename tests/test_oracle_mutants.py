@@ -75,6 +75,8 @@ MUTANTS = [
     ("batch_first_table", [("block_tables + (int64_t)b * max_blocks, pos[b]", "block_tables, pos[b]")]),
     ("batch_shared_hidden", [("h + (int64_t)b * c->hidden, NULL,", "h, NULL,")]),
     ("batch_shared_logits", [("logits ? logits + (int64_t)b * c->vocab : NULL", "logits")]),
+    ("prefill_fixed_position", [("page_table, pos0 + t, tokens[t], h, NULL", "page_table, pos0, tokens[t], h, NULL")]),
+    ("prefill_first_logits", [("t == T - 1 ? logits : NULL", "t == 0 ? logits : NULL")]),
 ]
 
 

@@ -513,10 +513,13 @@ void orc_decode_batch(const orc_config *c, const orc_layer *layers, const orc_he
  * token of the last position; h and logits are those of the last position. */
 int orc_prefill(const orc_config *c, const orc_layer *layers, const orc_head *head, const int32_t *page_table,
                 int pos0, const int32_t *tokens, int T, float *h, float *logits, int nthreads) {
+  /* positions before the last need no logits: their steps skip the lm head */
+  orc_config body = *c;
+  body.has_lm_head = 0;
   int next = -1;
   for (int t = 0; t < T; ++t)
-    next = orc_decode_step(c, layers, head, page_table, pos0 + t, tokens[t], h, NULL, t == T - 1 ? logits : NULL,
-                           nthreads);
+    next = orc_decode_step(t == T - 1 ? c : &body, layers, head, page_table, pos0 + t, tokens[t], h, NULL,
+                           t == T - 1 ? logits : NULL, nthreads);
   return next;
 }
 

@@ -76,7 +76,8 @@ MUTANTS = [
     ("batch_shared_hidden", [("h + (int64_t)b * c->hidden, NULL,", "h, NULL,")]),
     ("batch_shared_logits", [("logits ? logits + (int64_t)b * c->vocab : NULL", "logits")]),
     ("prefill_fixed_position", [("page_table, pos0 + t, tokens[t], h, NULL", "page_table, pos0, tokens[t], h, NULL")]),
-    ("prefill_first_logits", [("t == T - 1 ? logits : NULL", "t == 0 ? logits : NULL")]),
+    ("prefill_first_logits", [("t == T - 1 ? logits : NULL", "t == 0 ? logits : NULL"),
+                              ("t == T - 1 ? c : &body", "t == 0 ? c : &body")]),
 ]
 
 

@@ -220,6 +220,56 @@ def batch_bench(wl, B: int, K: int, W: int):
             "step_bytes": step_b, "step_gbps": step_b / (ms * 1e-3) / 1e9, "gen_s": gen_s}
 
 
+def prefill_bench(wl, T: int, reps: int, warmup: int):
+    """Time to first token for a T-token prompt on an empty sequence: qdec_prefill on the step
+    handle (every layer's projections on the matrix cores, attention, KV stored, lm head and the
+    greedy first token), HIP events around each call on its stream; the position is reset to 0
+    between calls, outside the timed region."""
+    import quantized_gemv_gqa_amd as q
+    import synth
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    model = synth.make_model(wl)
+    kv = synth.make_kv(wl, T + 16, ctx=0)
+    gen_s = time.time() - t0
+    dm = q.upload_model(model, dev)
+    dk = q.upload_kv(kv, wl.kv_fmt, dev)
+    st = q.DecodeStep(dm, dk, pos0=0, token0=0, log_len=4, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    tokens = torch.randint(0, wl.vocab, (T,), dtype=torch.int32, device=dev, generator=gen)
+    stream = torch.cuda.Stream()
+    times = []
+    with torch.cuda.stream(stream):
+        for i in range(warmup + reps):
+            st.pos.zero_()
+            st.step_count.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st.prefill(tokens)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+    assert int(st.pos.item()) == T
+    ms = sum(times) / len(times)
+    H, I, D = wl.hidden, wl.inter, wl.head_dim
+    params = (wl.n_heads + 2 * wl.n_kv_heads) * D * H + H * wl.n_heads * D + 2 * I * H + H * I
+    gemm_flop = 2.0 * T * params * wl.n_layers
+    attn_flop = 2.0 * 2 * wl.n_layers * wl.n_heads * D * (T * (T + 1) / 2)
+    return {"metric": "prefill time to first token, Qwen2.5-7B-shape INT4, 1 GPU", "value": ms, "unit": "ms",
+            "higher_is_better": False, "prompt_tokens": T, "reps": reps, "warmup": warmup,
+            "prefill_tokens_per_s": T / (ms * 1e-3), "dtype": "f16 matrix inputs as fp16 pairs, f32 accumulation",
+            "data": "synthetic",
+            "config": {"workload": wl.name, "layers": wl.n_layers, "context_before": 0},
+            "roofline": {"bound": "mfma", "achieved": gemm_flop / (ms * 1e-3) / 1e12, "peak": 2500.0,
+                         "unit": "TFLOP/s", "frac": gemm_flop / (ms * 1e-3) / 1e12 / 2500.0,
+                         "note": "algorithmic GEMM flops (2 T x weights per layer) over the whole prefill time; "
+                                 "the pair split issues 3 (INT4) matrix products per fragment"},
+            "gemm_flop": gemm_flop, "attn_flop": attn_flop, "ms_each": times, "gen_s": gen_s}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +282,8 @@ def main():
                     help="size of one plain device copy run after the timed region (counter calibration)")
     ap.add_argument("--sampling", default="",
                     help="T,top_k,top_p: sample each token on the GPU (seed 1234) instead of greedy argmax")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="instead of the decode step: time to first token for a prompt of this many tokens")
     ap.add_argument("--batch", type=int, default=0,
                     help="instead of the batch-1 step: batched decode of this many sequences (1..8)")
     ap.add_argument("--gemv-ab", action="store_true",
@@ -246,6 +298,9 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.prefill:
+        print(json.dumps(prefill_bench(wl, args.prefill, max(1, min(args.steps, 10)), min(args.warmup, 2))))
+        return
     if args.batch:
         print(json.dumps(batch_bench(wl, args.batch, args.steps, args.warmup)))
         return

@@ -140,6 +140,11 @@ def lib():
         L.qdec_batch_decode_step.argtypes = [_P, _I, _P]; L.qdec_batch_decode_step.restype = S
         L.qdec_batch_kernel_count.argtypes = [_P]; L.qdec_batch_kernel_count.restype = _I
         L.qdec_batch_destroy.argtypes = [_P]; L.qdec_batch_destroy.restype = None
+        L.qdec_gemm_mfma.argtypes = [_I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _P, _I, _I, _I, _P]
+        L.qdec_gemm_mfma.restype = S
+        L.qdec_prefill_workspace_bytes.argtypes = [ctypes.POINTER(QdecConfig), _I]
+        L.qdec_prefill_workspace_bytes.restype = Z
+        L.qdec_prefill.argtypes = [_P, _P, _I, _P, Z, _P]; L.qdec_prefill.restype = S
         L.qdec_sample_workspace_bytes.argtypes = []; L.qdec_sample_workspace_bytes.restype = Z
         L.qdec_sample.argtypes = [_P, _I, F, _I, F, ctypes.c_uint64, _P, _P, _P, Z, _P]; L.qdec_sample.restype = S
         L.qdec_rmsnorm_rope.argtypes = [_P, _P, _P, _I, _I, F, F, _P, _P]; L.qdec_rmsnorm_rope.restype = S
@@ -172,7 +177,8 @@ EXPORTED = [
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
     "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8", "qdec_sample_workspace_bytes", "qdec_sample",
     "qdec_gemm_workspace_bytes", "qdec_gemm_q8", "qdec_gemm_q4", "qdec_batch_workspace_bytes", "qdec_batch_create",
-    "qdec_batch_decode_step", "qdec_batch_kernel_count", "qdec_batch_destroy",
+    "qdec_batch_decode_step", "qdec_batch_kernel_count", "qdec_batch_destroy", "qdec_prefill_workspace_bytes",
+    "qdec_prefill", "qdec_gemm_mfma",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
     "qdec_step_kernel_count", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
@@ -293,6 +299,17 @@ def gemm(wfmt: str, Wp, Sp, X, N: int, bias=None, residual=None, Y=None, workspa
         st = lib().qdec_gemm_q4(_ptr(Wp), _ptr(Sp), group, _ptr(X), K, nb, _ptr(bias), _ptr(residual), _ptr(Y),
                                 Y.shape[1], N, K, ws, wsb, _stream(stream))
     _check(st, "qdec_gemm_" + wfmt)
+    return Y
+
+
+def gemm_mfma(wfmt: str, Wp, Sp, X16, N: int, X16lo=None, bias=None, residual=None, Y=None, group: int = 64,
+              stream=None):
+    """Prefill GEMM: Y [M][N] = W X[m] for activations X = X16 + X16lo ([M][K] torch.float16 each)."""
+    M, K = X16.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X16.device)
+    _check(lib().qdec_gemm_mfma(W_Q8 if wfmt == "q8" else W_Q4, _ptr(Wp), _ptr(Sp), group, _ptr(X16), _ptr(X16lo), K, M,
+                                _ptr(bias), _ptr(residual), _ptr(Y), Y.shape[1], N, K, _stream(stream)), "qdec_gemm_mfma")
     return Y
 
 
@@ -584,6 +601,20 @@ class DecodeStep:
 
     def step(self, mode: int = STEP_EAGER, stream=None):
         _check(lib().qdec_decode_step(self.handle, mode, _stream(stream)), "qdec_decode_step")
+
+    def prefill(self, tokens, stream=None, workspace=None):
+        """Run the prompt `tokens` (int32 device tensor) at positions pos .. pos + n - 1: stores its
+        KV, sets token to the greedy next token and advances pos by n (libqdec qdec_prefill)."""
+        n = tokens.numel()
+        if workspace is None:
+            nbytes = lib().qdec_prefill_workspace_bytes(ctypes.byref(self.cfg), n)
+            if nbytes == 0:
+                raise QdecError(QDEC_EUNSUPPORTED, "qdec_prefill_workspace_bytes")
+            if getattr(self, "_pws", None) is None or self._pws.numel() < nbytes:
+                self._pws = torch.zeros(nbytes, dtype=torch.uint8, device=tokens.device)
+            workspace = self._pws
+        _check(lib().qdec_prefill(self.handle, _ptr(tokens), n, _ptr(workspace), workspace.numel(), _stream(stream)),
+               "qdec_prefill")
 
     def set_sampling(self, temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0):
         """Sample later tokens (temperature / top-k / top-p, draw counter = step_count) instead of

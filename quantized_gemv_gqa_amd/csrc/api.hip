@@ -253,6 +253,40 @@ qdec_status qdec_gemm_q4(const void *Wp, const uint16_t *Sp, int group, const fl
                      workspace_bytes, stream, "qdec_gemm_q4");
 }
 
+qdec_status qdec_gemm_mfma(int wfmt, const void *Wp, const void *Sp, int group, const uint16_t *X16, const uint16_t *X16lo,
+                           int ldx, int M, const float *bias, const float *residual, float *Y, int ldy, int N, int K,
+                           void *stream) {
+  const char *nm = "qdec_gemm_mfma";
+  QDEC_REQUIRE(Wp && Sp && X16 && Y, QDEC_EINVAL, "%s: null pointer", nm);
+  QDEC_REQUIRE(wfmt == QDEC_W_Q8_ROW || wfmt == QDEC_W_Q4_G_ZP8, QDEC_EUNSUPPORTED, "%s: unknown weight format %d", nm,
+               wfmt);
+  QDEC_REQUIRE(M >= 1 && N >= 1 && K >= 32 && K % 32 == 0, QDEC_EINVAL, "%s: need M, N >= 1 and K a multiple of 32 (K=%d)",
+               nm, K);
+  if (wfmt == QDEC_W_Q4_G_ZP8)
+    QDEC_REQUIRE(group >= 32 && group <= 4096 && (group & (group - 1)) == 0 && K % group == 0, QDEC_EUNSUPPORTED,
+                 "%s: group must be 32 times a power of two dividing K (got %d)", nm, group);
+  QDEC_REQUIRE(ldx >= K && ldx % 8 == 0 && ldy >= N, QDEC_EINVAL, "%s: need ldx >= K, ldx %% 8 == 0, ldy >= N", nm);
+  QDEC_REQUIRE(aligned(Wp, 16) && aligned(X16, 16) && aligned(X16lo, 16) && aligned(Y, 4), QDEC_EINVAL,
+               "%s: packed weights and X16 must be 16-byte aligned", nm);
+  GemmPArgs a{};
+  a.W = reinterpret_cast<const uint8_t *>(Wp);
+  a.S = Sp;
+  a.X = X16;
+  a.Xl = X16lo;
+  a.ldx = ldx;
+  a.bias = bias;
+  a.residual = residual;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.epi = EPI_STORE;
+  if (launch_gemm_p(wfmt, a, (hipStream_t)stream) != hipSuccess) return check_launch(nm);
+  return QDEC_OK;
+}
+
 size_t qdec_sample_workspace_bytes(void) { return sample_workspace_bytes(); }
 
 qdec_status qdec_sample(const float *logits, int V, float temperature, int top_k, float top_p, uint64_t seed,

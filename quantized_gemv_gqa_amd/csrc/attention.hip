@@ -55,6 +55,20 @@ __global__ void __launch_bounds__(attn::kAttnThreads) attn_split_batch(const Att
   attn::attn_unit<D, G, KVF, true, false>(a, blockIdx.x, blockIdx.y, sm);
 }
 
+// grid (Hkv, 1, T): query t of a prompt over keys 0 .. pos_rows[t] (one split)
+template <int D, int G, int KVF>
+__global__ void __launch_bounds__(attn::kAttnThreads) attn_split_rows(const AttnRows r) {
+  __shared__ attn::AttnSmem<D, G, false> sm;
+  const int t = blockIdx.z;
+  AttnArgs a = r.a;
+  a.q = r.q + (size_t)t * r.q_stride;
+  a.pos = r.pos_rows + t;
+  a.counters = reinterpret_cast<unsigned *>(r.ws + (size_t)t * r.ws_stride);
+  a.ws = reinterpret_cast<float *>(r.ws + (size_t)t * r.ws_stride + kAttnCounterBytes);
+  a.out = r.out + (size_t)t * a.Hq * D;
+  attn::attn_unit<D, G, KVF, false, false>(a, blockIdx.x, blockIdx.y, sm);
+}
+
 __global__ void kv_append(const float *__restrict__ k, const float *__restrict__ v, void *k_pool,
                           void *v_pool, int kv_fmt, const int32_t *__restrict__ page_table,
                           int n_pages, const int32_t *__restrict__ pos, int Hkv, int D) {
@@ -109,7 +123,30 @@ hipError_t launch_batch_g(const AttnBatch &ab, int G, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int KVF>
+hipError_t launch_rows_g(const AttnRows &r, int G, hipStream_t st) {
+  dim3 grid(r.a.Hkv, r.a.splits, r.T);
+  constexpr int kT = attn::kAttnThreads;
+  switch (G) {
+#define QDEC_G(g)                                                                            \
+  case g:                                                                                    \
+    hipLaunchKernelGGL((attn_split_rows<D, g, KVF>), grid, dim3(kT), 0, st, r);              \
+    break;
+    QDEC_G(1) QDEC_G(2) QDEC_G(3) QDEC_G(4) QDEC_G(5) QDEC_G(6) QDEC_G(7) QDEC_G(8)
+#undef QDEC_G
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_attention_rows(const AttnRows &r, hipStream_t st) {
+  const int G = r.a.Hq / r.a.Hkv;
+  if (r.a.D == 128)
+    return r.a.kv_fmt == QDEC_KV_BF16 ? launch_rows_g<128, QDEC_KV_BF16>(r, G, st) : launch_rows_g<128, QDEC_KV_F32>(r, G, st);
+  return r.a.kv_fmt == QDEC_KV_BF16 ? launch_rows_g<64, QDEC_KV_BF16>(r, G, st) : launch_rows_g<64, QDEC_KV_F32>(r, G, st);
+}
 
 hipError_t launch_attention_batch(const AttnBatch &ab, hipStream_t st) {
   const int G = ab.a.Hq / ab.a.Hkv;

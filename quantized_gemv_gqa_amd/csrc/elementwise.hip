@@ -367,6 +367,108 @@ __global__ void __launch_bounds__(64) argmax_rows_k(const float *__restrict__ cv
   }
 }
 
+// ------------------------------------------------------------------ prefill rows
+__global__ void prefill_positions_k(const int32_t *__restrict__ pos, int T, int32_t *__restrict__ rows) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < T) rows[t] = *pos + t;
+}
+
+__global__ void add_pos_k(int32_t *pos, int delta) {
+  if (threadIdx.x == 0) *pos += delta;
+}
+
+// grid (ceil(H / 256), T)
+__global__ void __launch_bounds__(256) embed_tokens_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ tokens,
+                                                      int H, int V, float *__restrict__ x) {
+  int tok = tokens[blockIdx.y];
+  if (tok < 0 || tok >= V) tok = 0;  // documented precondition; never read outside the table
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < H) x[(size_t)blockIdx.y * H + i] = __builtin_bit_cast(float, (uint32_t)E[(size_t)tok * H + i] << 16);
+}
+
+// fp32 -> fp16 pair: h = fp16(v) (nearest even), l = fp16(v - h); h + l carries 22 bits of v
+__device__ __forceinline__ void split_h(float v, uint32_t &h, uint32_t &l) {
+  const _Float16 hi = (_Float16)v;
+  h = __builtin_bit_cast(uint16_t, hi);
+  l = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)hi));
+}
+
+// as rmsnorm_rows_k, the output as an fp16 pair
+__global__ void __launch_bounds__(1024) rmsnorm_rows_h_k(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                         uint16_t *__restrict__ yh, uint16_t *__restrict__ yl, int dim,
+                                                         float eps) {
+  __shared__ float part[16];
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)blockIdx.x * dim);
+  uint2 *yrh = reinterpret_cast<uint2 *>(yh + (size_t)blockIdx.x * dim);
+  uint2 *yrl = reinterpret_cast<uint2 *>(yl + (size_t)blockIdx.x * dim);
+  const float4 *g4 = reinterpret_cast<const float4 *>(gamma);
+  const int n4 = dim / 4;
+  constexpr int kMaxPer = 4;
+  float4 v[kMaxPer];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + 1024 * k;
+    v[k] = i < n4 ? xr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += part[w];
+  const float r = rsqrtf(tot / (float)dim + eps);
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = threadIdx.x + 1024 * k;
+    if (i < n4) {
+      const float4 g = g4[i];
+      uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+      split_h(g.x * (v[k].x * r), h0, l0);
+      split_h(g.y * (v[k].y * r), h1, l1);
+      split_h(g.z * (v[k].z * r), h2, l2);
+      split_h(g.w * (v[k].w * r), h3, l3);
+      yrh[i] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      yrl[i] = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+  }
+}
+
+__global__ void to_half_k(const float *__restrict__ x, uint16_t *__restrict__ yh, uint16_t *__restrict__ yl, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t h, l;
+    split_h(x[i], h, l);
+    yh[i] = (uint16_t)h;
+    yl[i] = (uint16_t)l;
+  }
+}
+
+// grid (Hq + 2 Hkv, T): as qkv_post for token t at position pos_rows[t]
+__global__ void __launch_bounds__(64) qkv_post_rows_k(QkvRows r) {
+  __shared__ float buf[256];
+  const QkvPostArgs &a = r.a;
+  const int hh = blockIdx.x, row = blockIdx.y;
+  const int D = a.D;
+  const int t = r.pos_rows[row];
+  float *qkv = r.qkv + (size_t)row * (a.Hq + 2 * a.Hkv) * D;
+  float *x;
+  int kind, j;
+  if (hh < a.Hq) {
+    kind = 0; j = hh; x = qkv + (size_t)hh * D;
+  } else if (hh < a.Hq + a.Hkv) {
+    kind = 1; j = hh - a.Hq; x = qkv + (size_t)(a.Hq + j) * D;
+  } else {
+    kind = 2; j = hh - a.Hq - a.Hkv; x = qkv + (size_t)(a.Hq + a.Hkv + j) * D;
+  }
+  if (kind < 2) norm_rope_row(x, x, D, kind == 0 ? a.g_q : a.g_k, a.eps, a.rope_base, t, buf);
+  if (kind == 0 || !a.k_pool) return;
+  const int phys = a.page_table[t >> 4];
+  if (phys < 0 || phys >= a.n_pages) return;
+  void *pool = (kind == 1) ? a.k_pool : a.v_pool;
+  const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (t & 15)) * D;
+  for (int d = threadIdx.x; d < D; d += 64) store_kv(pool, a.kv_fmt, e0 + d, kind == 1 ? buf[d] : x[d]);
+}
+
 __global__ void copy_k(const float *__restrict__ s, float *__restrict__ d, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) d[i] = s[i];
 }
@@ -428,6 +530,39 @@ hipError_t launch_argmax_rows(const float *logits, int B, int V, int32_t *tokens
   int *ci = reinterpret_cast<int *>(cv + (size_t)B * kArgChunks);
   hipLaunchKernelGGL(argmax_rows_part_k, dim3(kArgChunks, B), dim3(1024), 0, st, logits, V, pos, cv, ci);
   hipLaunchKernelGGL(argmax_rows_k, dim3(B), dim3(64), 0, st, cv, ci, tokens, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_positions(const int32_t *pos, int T, int32_t *pos_rows, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_positions_k, dim3((T + 255) / 256), dim3(256), 0, st, pos, T, pos_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_pos(int32_t *pos, int delta, hipStream_t st) {
+  hipLaunchKernelGGL(add_pos_k, dim3(1), dim3(64), 0, st, pos, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_tokens(const uint16_t *E, const int32_t *tokens, int T, int H, int V, float *x, hipStream_t st) {
+  hipLaunchKernelGGL(embed_tokens_k, dim3((H + 255) / 256, T), dim3(256), 0, st, E, tokens, H, V, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows_h(const float *x, const float *gamma, uint16_t *yh, uint16_t *yl, int B, int dim,
+                                 float eps, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_rows_h_k, dim3(B), dim3(1024), 0, st, x, gamma, yh, yl, dim, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_half(const float *x, uint16_t *yh, uint16_t *yl, size_t n, hipStream_t st) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(to_half_k, dim3((unsigned)blocks), dim3(256), 0, st, x, yh, yl, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_post_rows(const QkvRows &r, hipStream_t st) {
+  hipLaunchKernelGGL(qkv_post_rows_k, dim3(r.a.Hq + 2 * r.a.Hkv, r.T), dim3(64), 0, st, r);
   return hipGetLastError();
 }
 

@@ -26,6 +26,68 @@ int gemm_b_columns(int batch);  // nb_max for a batch size (2, 4 or 8)
 size_t gemm_b_workspace_bytes(int wfmt, int N, int K, int nb_max);
 hipError_t launch_gemm_b(int wfmt, GemmBArgs a, void *ws, hipStream_t st);
 
+// Prefill GEMM on the matrix cores (gemm_p.hip): Y[m][n] = sum_k X[m][k] w[n][k] for m < M, with
+// activations given as fp16 pairs X = Xh + Xl ([M][ldx] each, ldx % 8 == 0; Xl null: Xh alone),
+// K % 32 == 0; fp32 output, + bias[n], + residual[m][n] (same layout as Y, may alias it), or the
+// SwiGLU of the gate/up row pairs with EPI_SWIGLU, written as an fp16 pair (Yh, Yl) [M][ldy]
+// (N / 2 outputs) when Yh is set.
+struct GemmPArgs {
+  const uint8_t *W;
+  const void *S;
+  const uint16_t *X, *Xl;  // fp16 bits: high and low parts
+  int ldx;
+  const float *bias, *residual;
+  float *Y;
+  uint16_t *Yh, *Yl;       // EPI_SWIGLU: fp16 pair output [M][ldy] instead of Y
+  int ldy;
+  int M, N, K, group;
+  int epi;
+  // k-split (EPI_STORE only): split z writes its fp32 partial to part[z][M][N], and a reduce
+  // launch adds the splits in order (deterministic) and applies scale, bias and residual
+  int ks;
+  float *part;
+};
+// k-splits a prefill GEMM uses (1 when its tiles already fill the GPU); part needs
+// ks * M * N floats
+int gemm_p_splits(int M, int N, int K, int epi);
+hipError_t launch_gemm_p(int wfmt, const GemmPArgs &a, hipStream_t st);
+
+// Prefill row kernels (elementwise.hip)
+// pos_rows[t] = *pos + t for t < T
+hipError_t launch_prefill_positions(const int32_t *pos, int T, int32_t *pos_rows, hipStream_t st);
+// *pos += delta
+hipError_t launch_add_pos(int32_t *pos, int delta, hipStream_t st);
+// x[t] = E[tokens[t]] (bf16 -> fp32), t < T
+hipError_t launch_embed_tokens(const uint16_t *E, const int32_t *tokens, int T, int H, int V, float *x, hipStream_t st);
+// fp16 pair rows: v = gamma * x[b] / sqrt(mean(x[b]^2) + eps) as yh = fp16(v), yl = fp16(v - yh);
+// and the same split of plain fp32 values
+hipError_t launch_rmsnorm_rows_h(const float *x, const float *gamma, uint16_t *yh, uint16_t *yl, int B, int dim,
+                                 float eps, hipStream_t st);
+hipError_t launch_to_half(const float *x, uint16_t *yh, uint16_t *yl, size_t n, hipStream_t st);
+// per token t and head: q/k RMSNorm (optional), RoPE at pos_rows[t], k and v stored into the pools
+// at the page of pos_rows[t]; qkv [T][(Hq + 2 Hkv) D] rewritten in place (q, k rotated)
+struct QkvRows {
+  QkvPostArgs a;            // per-sequence fields (qkv, pos unused)
+  float *qkv;
+  const int32_t *pos_rows;
+  int T;
+};
+hipError_t launch_qkv_post_rows(const QkvRows &r, hipStream_t st);
+
+// Prefill attention (attention.hip): query t of the prompt (rotated q at q + t * q_stride) over
+// keys 0 .. pos_rows[t] of the sequence's pages, one split; out [T][Hq D].
+struct AttnRows {
+  AttnArgs a;               // pools, page table, heads, scale (q, pos, ws, out per row below)
+  const float *q;
+  int q_stride;
+  const int32_t *pos_rows;
+  char *ws;
+  size_t ws_stride;
+  float *out;
+  int T;
+};
+hipError_t launch_attention_rows(const AttnRows &r, hipStream_t st);
+
 // Row kernels of the batched step (elementwise.hip).  A row b with pos[b] < 0 is idle.
 // h[b] = bf16 -> fp32 E[tokens[b]]; rope_cs[b] = the fp64 (cos, sin) table of pos[b] (D/2 pairs)
 hipError_t launch_embed_rows(const uint16_t *E, const int32_t *tokens, const int32_t *pos, int B, int H, int V,

@@ -16,7 +16,7 @@
 #include <vector>
 
 #include "qdec_fused.h"
-#include "qdec_internal.h"
+#include "qdec_batch.h"
 
 struct qdec_step {
   qdec_config cfg;
@@ -500,12 +500,202 @@ qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
   return QDEC_OK;
 }
 
+// ------------------------------------------------------------------ prefill
+struct PLayout {
+  size_t x32, a16, a16l, qkv, att, att16, att16l, mlp16, mlp16l, pos_rows, attn_ws, attn_stride, a_last, part, total;
+};
+
+PLayout playout(const qdec_config &c, int T) {
+  PLayout L{};
+  const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim, qd = c.n_heads * c.head_dim;
+  size_t o = 0;
+  L.x32 = o; o += align256((size_t)T * c.hidden * 4);
+  L.a16 = o; o += align256((size_t)T * c.hidden * 2);
+  L.a16l = o; o += align256((size_t)T * c.hidden * 2);
+  L.qkv = o; o += align256((size_t)T * nqkv * 4);
+  L.att = o; o += align256((size_t)T * qd * 4);
+  L.att16 = o; o += align256((size_t)T * qd * 2);
+  L.att16l = o; o += align256((size_t)T * qd * 2);
+  L.mlp16 = o; o += align256((size_t)T * c.inter * 2);
+  L.mlp16l = o; o += align256((size_t)T * c.inter * 2);
+  L.pos_rows = o; o += align256((size_t)T * 4);
+  L.attn_stride = align256(attn_workspace_bytes(c.n_heads, c.head_dim, 1));
+  L.attn_ws = o; o += (size_t)T * L.attn_stride;
+  L.a_last = o; o += align256((size_t)c.hidden * 4);
+  size_t pb = 0;  // k-split partials of the largest split GEMM
+  const int Ns[3] = {nqkv, c.hidden, c.hidden}, Ks[3] = {c.hidden, qd, c.inter};
+  for (int i = 0; i < 3; ++i)
+    pb = std::max(pb, (size_t)gemm_p_splits(T, Ns[i], Ks[i], EPI_STORE) * T * Ns[i] * 4);
+  L.part = o; o += align256(pb);
+  L.total = o;
+  return L;
+}
+
+qdec_status prefill_supported(const qdec_config &c) {
+  const int qd = c.n_heads * c.head_dim;
+  QDEC_REQUIRE(c.hidden % 32 == 0 && qd % 32 == 0 && c.inter % 32 == 0 && c.hidden <= 16384, QDEC_EUNSUPPORTED,
+               "qdec_prefill: hidden, n_heads*head_dim and inter must be multiples of 32 (hidden <= 16384)");
+  return QDEC_OK;
+}
+
+qdec_status enqueue_prefill(qdec_step *h, const int32_t *tokens, int T, char *ws, hipStream_t st) {
+  const qdec_config &c = h->cfg;
+  const qdec_state &s = h->state;
+  const int H = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim, I = c.inter, V = c.vocab;
+  const int nqkv = (Hq + 2 * Hkv) * D, qd = Hq * D;
+  const int wf = c.wfmt;
+  const PLayout L = playout(c, T);
+  float *x32 = reinterpret_cast<float *>(ws + L.x32);
+  uint16_t *a16 = reinterpret_cast<uint16_t *>(ws + L.a16);
+  uint16_t *a16l = reinterpret_cast<uint16_t *>(ws + L.a16l);
+  float *qkv = reinterpret_cast<float *>(ws + L.qkv);
+  float *att = reinterpret_cast<float *>(ws + L.att);
+  uint16_t *att16 = reinterpret_cast<uint16_t *>(ws + L.att16);
+  uint16_t *att16l = reinterpret_cast<uint16_t *>(ws + L.att16l);
+  uint16_t *mlp16 = reinterpret_cast<uint16_t *>(ws + L.mlp16);
+  uint16_t *mlp16l = reinterpret_cast<uint16_t *>(ws + L.mlp16l);
+  int32_t *pos_rows = reinterpret_cast<int32_t *>(ws + L.pos_rows);
+  float *a_last = reinterpret_cast<float *>(ws + L.a_last);
+  int n = 0;
+  QDEC_CK(launch_prefill_positions(s.pos, T, pos_rows, st));
+  QDEC_CK(launch_embed_tokens(h->model.embed, tokens, T, H, V, x32, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const qdec_layer_weights &w = h->layers[l];
+    QDEC_CK(launch_rmsnorm_rows_h(x32, w.g_attn, a16, a16l, T, H, c.rms_eps, st));
+    GemmPArgs g{};
+    g.W = reinterpret_cast<const uint8_t *>(w.w_qkv);
+    g.S = w.s_qkv;
+    g.X = a16;
+    g.Xl = a16l;
+    g.ldx = H;
+    g.bias = c.has_qkv_bias ? w.b_qkv : nullptr;
+    g.Y = qkv;
+    g.ldy = nqkv;
+    g.M = T;
+    g.N = nqkv;
+    g.K = H;
+    g.group = c.group;
+    g.epi = EPI_STORE;
+    g.part = reinterpret_cast<float *>(ws + L.part);
+    g.ks = gemm_p_splits(T, nqkv, H, EPI_STORE);
+    QDEC_CK(launch_gemm_p(wf, g, st));
+    QkvRows qr{};
+    qr.a.g_q = c.has_qk_norm ? w.g_q : nullptr;
+    qr.a.g_k = c.has_qk_norm ? w.g_k : nullptr;
+    qr.a.eps = c.rms_eps;
+    qr.a.rope_base = c.rope_base;
+    qr.a.Hq = Hq;
+    qr.a.Hkv = Hkv;
+    qr.a.D = D;
+    qr.a.k_pool = h->kpools[l];
+    qr.a.v_pool = h->vpools[l];
+    qr.a.kv_fmt = c.kv_fmt;
+    qr.a.page_table = s.page_table;
+    qr.a.n_pages = c.n_pages;
+    qr.qkv = qkv;
+    qr.pos_rows = pos_rows;
+    qr.T = T;
+    QDEC_CK(launch_qkv_post_rows(qr, st));
+    AttnRows ar{};
+    ar.a.k_pool = h->kpools[l];
+    ar.a.v_pool = h->vpools[l];
+    ar.a.kv_fmt = c.kv_fmt;
+    ar.a.page_table = s.page_table;
+    ar.a.n_pages = c.n_pages;
+    ar.a.Hq = Hq;
+    ar.a.Hkv = Hkv;
+    ar.a.D = D;
+    ar.a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    ar.a.splits = 1;
+    ar.q = qkv;
+    ar.q_stride = nqkv;
+    ar.pos_rows = pos_rows;
+    ar.ws = ws + L.attn_ws;
+    ar.ws_stride = L.attn_stride;
+    ar.out = att;
+    ar.T = T;
+    QDEC_CK(launch_attention_rows(ar, st));
+    QDEC_CK(launch_to_half(att, att16, att16l, (size_t)T * qd, st));
+    GemmPArgs o = g;
+    o.W = reinterpret_cast<const uint8_t *>(w.w_o);
+    o.S = w.s_o;
+    o.X = att16;
+    o.Xl = att16l;
+    o.ldx = qd;
+    o.bias = nullptr;
+    o.residual = x32;
+    o.Y = x32;
+    o.ldy = H;
+    o.N = H;
+    o.K = qd;
+    o.ks = gemm_p_splits(T, H, qd, EPI_STORE);
+    QDEC_CK(launch_gemm_p(wf, o, st));
+    QDEC_CK(launch_rmsnorm_rows_h(x32, w.g_ffn, a16, a16l, T, H, c.rms_eps, st));
+    GemmPArgs gu = g;
+    gu.W = reinterpret_cast<const uint8_t *>(w.w_gu);
+    gu.S = w.s_gu;
+    gu.bias = nullptr;
+    gu.Y = nullptr;
+    gu.Yh = mlp16;
+    gu.Yl = mlp16l;
+    gu.ldy = I;
+    gu.N = 2 * I;
+    gu.epi = EPI_SWIGLU;
+    gu.ks = 1;
+    QDEC_CK(launch_gemm_p(wf, gu, st));
+    GemmPArgs d = o;
+    d.W = reinterpret_cast<const uint8_t *>(w.w_down);
+    d.S = w.s_down;
+    d.X = mlp16;
+    d.Xl = mlp16l;
+    d.ldx = I;
+    d.K = I;
+    d.ks = gemm_p_splits(T, H, I, EPI_STORE);
+    QDEC_CK(launch_gemm_p(wf, d, st));
+  }
+  // the last token: hidden state, final RMSNorm, lm head with the greedy argmax (it advances the
+  // position by one, so the prompt's other tokens are added first) and the step bookkeeping
+  QDEC_CK(launch_copy(x32 + (size_t)(T - 1) * H, s.hidden, H, st));
+  QDEC_CK(launch_rmsnorm_rows(x32 + (size_t)(T - 1) * H, h->model.g_out, a_last, 1, H, c.rms_eps, st));
+  if (T > 1) QDEC_CK(launch_add_pos(s.pos, T - 1, st));
+  GemvArgs a = gemv_args(h, h->model.w_lm, h->model.s_lm, a_last, s.logits, V, H, h->p_lm);
+  a.epi = EPI_ARGMAX;
+  a.token = s.token;
+  a.pos = s.pos;
+  a.token_log = s.token_log;
+  a.step_count = s.step_count;
+  a.log_len = s.log_len;
+  QDEC_CK(launch_gemv(wf, a, h->p_lm, st));
+  (void)n;
+  return QDEC_OK;
+}
+
 }  // namespace
 }  // namespace qdec
 
 using namespace qdec;
 
 extern "C" {
+
+size_t qdec_prefill_workspace_bytes(const qdec_config *cfg, int max_tokens) {
+  if (validate(cfg) != QDEC_OK || max_tokens < 1 || prefill_supported(*cfg) != QDEC_OK) return 0;
+  return playout(*cfg, max_tokens).total;
+}
+
+qdec_status qdec_prefill(qdec_step *h, const int32_t *tokens, int n_tokens, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  const char *nm = "qdec_prefill";
+  QDEC_REQUIRE(h && tokens && workspace, QDEC_EINVAL, "%s: null argument", nm);
+  QDEC_REQUIRE(n_tokens >= 1, QDEC_EINVAL, "%s: n_tokens must be >= 1", nm);
+  QDEC_REQUIRE(h->model.embed && h->model.w_lm, QDEC_EINVAL, "%s: needs the embedding and the lm head", nm);
+  qdec_status r = prefill_supported(h->cfg);
+  if (r != QDEC_OK) return r;
+  QDEC_REQUIRE((reinterpret_cast<uintptr_t>(workspace) % 256) == 0, QDEC_EINVAL, "%s: workspace must be 256-byte aligned",
+               nm);
+  QDEC_REQUIRE(workspace_bytes >= playout(h->cfg, n_tokens).total, QDEC_EINVAL, "%s: workspace too small (%zu < %zu bytes)",
+               nm, workspace_bytes, playout(h->cfg, n_tokens).total);
+  return enqueue_prefill(h, tokens, n_tokens, reinterpret_cast<char *>(workspace), (hipStream_t)stream);
+}
 
 size_t qdec_step_workspace_bytes(const qdec_config *cfg) {
   if (validate(cfg) != QDEC_OK) return 0;

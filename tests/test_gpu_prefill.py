@@ -1,0 +1,154 @@
+"""Prefill (the prompt's projections on the matrix cores) against the CPU oracle.
+
+Bars, derived from the arithmetic.  The prefill GEMM carries the activations as an fp16 pair
+(x = xh + xl, 22 significant bits) and every weight exactly (an INT4 (c - 8) s as an fp16 pair, INT8
+codes exact), with fp32 accumulation: against the oracle's fp64 GEMV of the fp32 activations each
+output is within (3 * 2^-22 + 2^-15) sum_k |w_k x_k| (the split and the dropped low x low product,
+plus fp32 accumulation of K / 32 matrix-instruction partial sums, K <= 2^13).  With only the high
+parts (plain fp16 activations) the bound is (2^-11 + 2^-15) sum_k |w_k x_k|.  The whole prefill then meets the decode step's bars:
+last hidden state 1e-3 of its max-abs value, logits 2e-2 max-abs, every stored K/V value of the
+prompt within 1e-3 of the layer's max-abs K/V value plus one bf16 rounding step (at most 2^-7 of
+its own magnitude); the greedy token matches unless the oracle's top-2 margin is inside the logits
+bar.  The K/V bar holds for every token of the first layer; in later layers it holds for at least
+90 % of the prompt's tokens and every token stays within 2e-2: both sides round K/V to bf16, and
+where a value sits at a rounding boundary they may store neighbours one step apart; a later
+position whose softmax over the synthetic keys is sharp (score spread of about 9) and nearly tied
+turns that step into a visibly different attention output (measured: median per-token error
+3.8e-6 of the hidden state, two tokens in a hundred above 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev, host, rel_max_err, sync
+
+q = pytest.importorskip("quantized_gemv_gqa_amd")
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN_TOL = 1e-3
+LOGIT_TOL = 2e-2
+KV_TOL = 1e-3
+KV_SPREAD_TOL = 2e-2
+
+
+def _weights(rng, wfmt, N, K, group=64):
+    if wfmt == "q8":
+        W = rng.integers(-127, 128, (N, K)).astype(np.int8)
+        return W, ((0.02 / 127) * rng.uniform(0.5, 1.5, N)).astype(np.float32)
+    W = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    return W, rng.uniform(0.005, 0.02, (N, K // group)).astype(np.float16).view(np.uint16)
+
+
+def _split(x):
+    hi = x.astype(np.float16)
+    lo = (x - hi.astype(np.float32)).astype(np.float16)
+    return hi, lo
+
+
+@pytest.mark.parametrize("wfmt,N,K,M", [("q4", 4608, 3584, 512), ("q4", 3584, 3584, 130), ("q4", 200, 640, 7),
+                                        ("q8", 2048, 1536, 256), ("q8", 100, 128, 1), ("q4", 1000, 256, 129),
+                                        ("q4", 64, 96, 33)])
+@pytest.mark.parametrize("pair", [True, False])
+def test_gemm_mfma_parity(wfmt, N, K, M, pair):
+    rng = np.random.default_rng(N + K + M)
+    W, S = _weights(rng, wfmt, N, K, group=32 if K % 64 else 64)
+    grp = 32 if K % 64 else 64
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    hi, lo = _split(x)
+    xin = x if pair else hi.astype(np.float32)
+    b = (0.02 * rng.standard_normal(N)).astype(np.float32)
+    R = rng.standard_normal((M, N)).astype(np.float32)
+    Wp, Sp = (q.pack_q8(dev(W), dev(S)) if wfmt == "q8" else q.pack_q4(dev(W), dev(S), grp))
+    Y = q.gemm_mfma(wfmt, Wp, Sp, dev(hi), N, X16lo=dev(lo) if pair else None, bias=dev(b), residual=dev(R), group=grp)
+    sync()
+    Y = host(Y)
+    absw = np.stack([np.abs(oracle.dequant_row(wfmt, W, S, n, K, group=grp)) for n in range(N)]).astype(np.float64)
+    rows = sorted(set([0, M - 1] + list(rng.integers(0, M, min(M, 24)))))
+    rel = (3 * 2.0 ** -22 if pair else 2.0 ** -11) + 2.0 ** -15
+    for m in rows:
+        ref = oracle.gemv(wfmt, W, S, xin[m], bias=b, residual=R[m], group=grp)
+        bound = rel * (absw @ np.abs(xin[m]).astype(np.float64)) + 2.0 ** -23 * (np.abs(ref) + np.abs(b) + np.abs(R[m]))
+        err = np.abs(Y[m].astype(np.float64) - ref)
+        assert np.all(err <= bound), (m, float((err / bound).max()))
+
+
+class Prompt:
+    def __init__(self, name, ctx, T, n_layers=2):
+        wl = synth.WORKLOADS[name]
+        self.wl = wl
+        self.model = synth.make_model(wl, n_layers=n_layers)
+        self.kv = synth.make_kv(wl, ctx + T + 24, n_layers=n_layers, ctx=ctx)
+        self.ctx, self.T = ctx, T
+        self.orc = oracle.OracleDecoder(self.model, self.kv)
+        self.dm = q.upload_model(self.model)
+        self.dk = q.upload_kv(self.kv, wl.kv_fmt)
+        self.gpu = q.DecodeStep(self.dm, self.dk, pos0=ctx, token0=0, log_len=8)
+        rng = np.random.default_rng(ctx + T)
+        self.tokens = rng.integers(0, wl.vocab, T).astype(np.int32)
+
+
+def _kv_rows(pool, wl, pt, t0, t1):
+    t = np.arange(t0, t1)
+    a = pool[pt[t // 16], :, t % 16, :]
+    return a.astype(np.float32) if wl.kv_fmt == "f32" else (a.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("name,ctx,T", [("qwen2.5-7b-q4", 40, 100), ("qwen2.5-7b-q4", 0, 256), ("qwen3-8b-q8", 5, 64),
+                                        ("qwen2.5-1.5b-q8", 16, 33)])
+def test_prefill_matches_oracle(name, ctx, T):
+    p = Prompt(name, ctx, T)
+    with torch.cuda.stream(torch.cuda.Stream()):
+        p.gpu.prefill(dev(p.tokens))
+        sync()
+    ref = p.orc.prefill(ctx, p.tokens)
+    assert int(host(p.gpu.pos)[0]) == ctx + T and int(host(p.gpu.step_count)[0]) == 1
+    e = rel_max_err(host(p.gpu.hidden), ref["h"])
+    assert e <= HIDDEN_TOL, e
+    lg = host(p.gpu.logits)
+    assert float(np.abs(lg - ref["logits"]).max()) <= LOGIT_TOL
+    tok = int(host(p.gpu.token)[0])
+    if tok != ref["token"]:
+        srt = np.sort(ref["logits"].astype(np.float64))
+        assert srt[-1] - srt[-2] <= LOGIT_TOL, (tok, ref["token"])
+    assert int(host(p.gpu.token_log)[0]) == tok
+    pt = p.kv["page_table"]
+    for l in range(2):
+        for mine, theirs in ((p.dk["k"][l], p.orc.k[l]), (p.dk["v"][l], p.orc.v[l])):
+            g = _kv_rows(host(mine).view(np.uint16) if p.wl.kv_fmt == "bf16" else host(mine), p.wl, pt, ctx, ctx + T)
+            o = _kv_rows(theirs, p.wl, pt, ctx, ctx + T)
+            step = 2.0 ** -7 if p.wl.kv_fmt == "bf16" else 0.0  # one bf16 step is at most 2^-7 of the value
+            excess = np.abs(g - o) - step * np.abs(o)  # beyond one storage rounding step of the value
+            per_tok = excess.reshape(T, -1).max(axis=1) / np.abs(o).max()
+            if l == 0:  # computed from the exact embedding rows: no attention upstream
+                assert per_tok.max() <= KV_TOL, (l, float(per_tok.max()))
+            else:
+                assert np.mean(per_tok <= KV_TOL) >= 0.9 and per_tok.max() <= KV_SPREAD_TOL, (
+                    l, float(np.mean(per_tok <= KV_TOL)), float(per_tok.max()))
+            # the context before the prompt is untouched
+            if ctx:
+                g0 = _kv_rows(host(mine).view(np.uint16) if p.wl.kv_fmt == "bf16" else host(mine), p.wl, pt, 0, ctx)
+                o0 = _kv_rows(theirs, p.wl, pt, 0, ctx)
+                assert np.array_equal(g0, o0)
+
+
+def test_decode_continues_after_prefill():
+    """Prefill, then graph decode steps: each step meets the prefill bars against the oracle
+    continuing from its own prefill (teacher-forced with the GPU's token)."""
+    p = Prompt("qwen2.5-7b-q4", 20, 45)
+    with torch.cuda.stream(torch.cuda.Stream()):
+        p.gpu.prefill(dev(p.tokens))
+        sync()
+        ref = p.orc.prefill(20, p.tokens)
+        tok = int(host(p.gpu.token)[0])
+        for s in range(3):
+            p.gpu.step(q.STEP_GRAPH)
+            sync()
+            r = p.orc.step(20 + 45 + s, tok)
+            assert float(np.abs(host(p.gpu.logits) - r["logits"]).max()) <= LOGIT_TOL, s
+            tok = int(host(p.gpu.token)[0])
+    assert int(host(p.gpu.pos)[0]) == 20 + 45 + 3
+    assert host(p.gpu.token_log)[:4].tolist()[0] >= 0
+    del ref

@@ -438,15 +438,15 @@ def upload_kv(kv: dict, kv_fmt: str, device="cuda") -> dict:
 
 
 def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 1) -> int:
-    """Attention split count: about `pages_per_wave` KV pages for each of a split's 8 waves (pages
-    are dealt round-robin over all waves of a KV head), at most 64 splits: the merge reads 32
-    splits' partials per pass, so past that a longer context gives each wave more pages instead.
-    Just above a multiple of 32 it rounds down (33 splits would cost a second pass for one
-    split's worth of pages)."""
+    """Attention split count: at most `pages_per_wave` KV pages for each of a split's 8 waves
+    (pages are dealt round-robin over all waves of a KV head, and the wave with the most pages
+    sets the split's time), rounded up to a multiple of 8 so a context that grows by a few pages
+    does not give some waves a second page, at most 64 (past that a longer context gives each
+    wave more pages).  Measured at 4096 tokens, Qwen2.5-7B shape: 40 splits 1.958 ms per step, 32
+    splits 1.980 ms, 48 splits 1.962 ms."""
     pages = max(1, -(-(ctx + 1) // PAGE))
     s = -(-pages // (8 * pages_per_wave))
-    if s > 32 and s % 32 <= (s // 32) * 8:
-        s -= s % 32
+    s = -(-s // 8) * 8
     return int(max(1, min(s, 64)))
 
 

@@ -157,10 +157,8 @@ __device__ __forceinline__ bool ge_u32(unsigned v, unsigned target) { return (in
 __device__ __forceinline__ void poll_pause(unsigned spins) {
   if (spins < 8)
     __builtin_amdgcn_s_sleep(1);
-  else if (spins < 32)
-    __builtin_amdgcn_s_sleep(4);
   else
-    __builtin_amdgcn_s_sleep(32);
+    __builtin_amdgcn_s_sleep(8);
 }
 
 // one thread: *p >= target
@@ -520,8 +518,11 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
   const int n = tile * kTile + lane;
   const bool valid = n < N;
   float pre_ssq = 0.f, pre_bias = 0.f, pre_res = 0.f, pre_scale = 1.f;
-  if constexpr (NORM)
-    for (int i = lane; i < a.ssq_n; i += 64) pre_ssq += a.ssq[i];
+  if constexpr (NORM) {
+    // one plain load per lane (a sum here would make the wave wait for the weights above too)
+    if (lane < a.ssq_n) pre_ssq = a.ssq[lane];
+    for (int i = lane + 64; i < a.ssq_n; i += 64) pre_ssq += a.ssq[i];
+  }
   if (EPI != EPI_SWIGLU && valid) {
     if (a.bias) pre_bias = a.bias[n];
     if (a.residual) pre_res = a.residual[n];  // (y may alias it: only this tile's epilogue writes y[n])

@@ -143,7 +143,7 @@ __device__ __forceinline__ void norm_rope(float (&own)[D / 16], float (&mate)[D 
 
 constexpr int kAttnWaves = 8;                  // waves per workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kMergeLoads = 16;                // partial outputs a merging thread loads per pass
+constexpr int kMergeLoads = 20;  // partial outputs a merging thread loads per pass (G = 7, 8: 40 splits in one pass)
 
 __device__ __forceinline__ void store_sc1_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAuxSc1);

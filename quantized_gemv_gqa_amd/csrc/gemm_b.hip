@@ -13,9 +13,19 @@
 // fp32 once (v_cvt_f32_ubyte on masked bytes), then used by every column: one FMA per code and
 // column, with the zero point (INT4) and the byte bias (INT8) folded out as
 // sum_k (c_k - z) x_k = sum_k c_k x_k - z sum_k x_k, sum_k x_k staged per run and column.  The
-// columns' activation chunks are staged once per wave in LDS and read back as broadcasts.  fp32
-// matrix cores would not help: on gfx950 their fp32 rate equals the vector rate, and 16-bit inputs
-// would change the fp32 activations.
+// columns' activation chunks are staged once per wave in LDS and read back as broadcasts.
+//
+// INT4 with 4 or 8 columns runs on the matrix cores instead (v_mfma_f32_16x16x32_f16): one FMA per
+// code and column is VALU-bound there (8 columns: gate/up at about 1.4 TB/s).  Each lane keeps its
+// own row's codes as the A operand, as fp16 c - 8 (exact), for one 8-code word at a time; lane
+// group g = lane / 16 thus feeds rows 16 g .. 16 g + 15 of the 64-row tile into the instruction's
+// 16 rows.  The B operand is block-diagonal: lane (group g, column j) holds the activations of
+// batch column 4 bg + j % 4 only when j / 4 == g, so output column j gets exactly the products of
+// tile row i + 16 (j / 4) — each instruction computes four independent 16-row x 4-column blocks,
+// and the codes need no exchange between lanes.  Activations go in as fp16 pairs x = xh + xl
+// (22 significant bits; two instructions), products are exact in fp32, the run's sum is scaled
+// by the group scale in fp32.  A final LDS transpose returns to one row per lane for the shared
+// split-K combine and epilogues.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -146,54 +156,130 @@ __device__ __forceinline__ void b_compute(float (&acc)[NB], const BatchB<FMT, NB
   __builtin_amdgcn_wave_barrier();  // the batch after next overwrites this slot
 }
 
-template <int FMT, int NB, int EPI>
-__global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a) {
-  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
-  constexpr int CK = Q4 ? 32 : 16;
-  __shared__ StageB<CK, NB> stage_all[kWavesB][2];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kWavesB + wave;
-  const int ks = a.ks, K = a.K, N = a.N;
-  const int tiles = (N + kTile - 1) / kTile;
-  if (unit >= tiles * ks) return;  // whole wave
-  StageB<CK, NB>(&sm)[2] = stage_all[wave];
-  const int tile = unit / ks;
-  const int ksi = unit - tile * ks;
-  const int nch = K / CK;
-  const int c0 = ksi * a.cps;
-  const int c1 = min(nch, c0 + a.cps);
-  const int nrun = c1 - c0;
-  const size_t tile_bytes = (size_t)nch * kTile * 16;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
-  __amdgpu_buffer_rsrc_t sr = wr;
-  int g0 = 0;
-  if constexpr (Q4) {
-    g0 = c0 >> a.gshift;
-    const int g1 = (c1 - 1) >> a.gshift;
-    sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> a.gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
-              (uint32_t)(g1 - g0 + 1) * kTile * 2);
-  }
-  // the nb columns' rows (each column reads only its own runs of the wave's k-range)
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.X, (uint32_t)((size_t)a.nb * a.ldx * 4));
+// ------------------------------------------------------------------ matrix-core path (INT4)
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f4m __attribute__((ext_vector_type(4)));
 
-  float acc[NB];
+// fp16 pairs of the columns' activations for one batch of runs, in k order
+template <int NB>
+struct StageM {
+  _Float16 xh[NB][kRunsB * 32], xl[NB][kRunsB * 32];
+};
+
+template <int NB>
+struct BatchM {
+  u32x4 w[kRunsB];
+  uint64_t s4[kRunsB];  // fp16 scales of the four rows whose results this lane accumulates
+  f32x4 x[x_slots<32, NB>()];
+};
+
+// first of the four consecutive tile rows whose results lane holds (MFMA output element
+// (4 (lane / 16) + r, lane % 16), column block lane % 16 / 4)
+__device__ __forceinline__ int m_row0(int lane) { return 4 * (lane >> 4) + 16 * ((lane & 15) >> 2); }
+
+template <int NB>
+__device__ __forceinline__ void m_load(BatchM<NB> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                       __amdgpu_buffer_rsrc_t xr, int ldx, int r, int c0, int nrun, int g0, int gshift,
+                                       int lane) {
+  constexpr int CK = 32;
+  const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
+  const uint32_t r0 = (uint32_t)m_row0(lane);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-  BatchB<FMT, NB> A, B;
-  b_load<FMT, NB>(A, wr, sr, xr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  for (int i = 0; i < kRunsB; ++i) {
+    B.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, base + i * (kTile * 16), 0, kAuxStream));
+    const int g = ((c0 + r + i) >> gshift) - g0;
+    B.s4[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(sr, (uint32_t)g * (kTile * 2) + r0 * 2, 0, 0));
+  }
+  constexpr int PER_COL = kRunsB * CK / 4;
+#pragma unroll
+  for (int i = 0; i < x_slots<CK, NB>(); ++i) {
+    const int f = lane + 64 * i;
+    const int b = f / PER_COL, q = (f % PER_COL) * 4;
+    const bool in = b < NB && r + q / CK < nrun;
+    const uint32_t off = in ? (uint32_t)(((size_t)b * ldx + (size_t)(c0 + r) * CK + q) * 4) : 0x80000000u;
+    B.x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<NB> &B, StageM<NB> &sm, int lane) {
+  constexpr int CK = 32, PER_COL = kRunsB * CK / 4;
+  // stage the activations as fp16 pairs
+#pragma unroll
+  for (int i = 0; i < x_slots<CK, NB>(); ++i) {
+    const int f = lane + 64 * i;
+    const int b = f / PER_COL, q = (f % PER_COL) * 4;
+    if (b < NB) {
+      const f32x4 v = B.x[i];
+      const _Float16 h0 = (_Float16)v.x, h1 = (_Float16)v.y, h2 = (_Float16)v.z, h3 = (_Float16)v.w;
+      const _Float16 l0 = (_Float16)(v.x - (float)h0), l1 = (_Float16)(v.y - (float)h1);
+      const _Float16 l2 = (_Float16)(v.z - (float)h2), l3 = (_Float16)(v.w - (float)h3);
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<h4 *>(&sm.xh[b][q]) = h4{h0, h1, h2, h3};
+      *reinterpret_cast<h4 *>(&sm.xl[b][q]) = h4{l0, l1, l2, l3};
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool act = ((lane & 15) >> 2) == (lane >> 4);  // this lane's B block is on the diagonal
+  const int bsub = lane & 3;
+  // B operands: loaded in the diagonal lanes only; the other lanes keep the zeros they start with
+  h8 xh = {}, xl = {};
+  const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int i = 0; i < kRunsB; ++i) {
+    const uint32_t wd[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
+    f4m c[NB / 4];
+#pragma unroll
+    for (int bg = 0; bg < NB / 4; ++bg) c[bg] = f4m{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // the lane's codes k = 8 q .. 8 q + 7 of the run (byte b: k = 2 b low nibble, 2 b + 1 high
+      // nibble): 0x6400 | c is the fp16 1024 + c, minus 1032 gives c - 8 exactly
+      const uint32_t w = wd[q];
+      const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;          // (k0, k4)
+      const uint32_t p1 = ((w >> 4) & 0x000F000Fu) | 0x64006400u;   // (k1, k5)
+      const uint32_t p2 = ((w >> 8) & 0x000F000Fu) | 0x64006400u;   // (k2, k6)
+      const uint32_t p3 = ((w >> 12) & 0x000F000Fu) | 0x64006400u;  // (k3, k7)
+      const h2v c01 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p1, p0, 0x05040100u)) - off;
+      const h2v c23 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p3, p2, 0x05040100u)) - off;
+      const h2v c45 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p1, p0, 0x07060302u)) - off;
+      const h2v c67 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p3, p2, 0x07060302u)) - off;
+      const h8 av = {c01.x, c01.y, c23.x, c23.y, c45.x, c45.y, c67.x, c67.y};
+#pragma unroll
+      for (int bg = 0; bg < NB / 4; ++bg) {
+        const int b = 4 * bg + bsub;
+        if (act) {
+          xh = *reinterpret_cast<const h8 *>(&sm.xh[b][i * CK + 8 * q]);
+          xl = *reinterpret_cast<const h8 *>(&sm.xl[b][i * CK + 8 * q]);
+        }
+        c[bg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, xl, c[bg], 0, 0, 0);
+        c[bg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, xh, c[bg], 0, 0, 0);
+      }
+    }
+    // the run's sums times the group scales of the lane's four rows
+    const uint64_t sv = B.s4[i];
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float((uint16_t)(sv >> (16 * r)));
+#pragma unroll
+    for (int bg = 0; bg < NB / 4; ++bg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[bg][r] = fmaf(sc[r], c[bg][r], acc[bg][r]);
+  }
+  __builtin_amdgcn_wave_barrier();  // the batch after next overwrites this slot
+}
+
+// Split-K combine and epilogue of a tile, shared by both paths: acc[b] is this lane's row, column b.
+template <int FMT, int NB, int EPI>
+__device__ __forceinline__ void b_finish(const GemmBArgs &a, float (&acc)[NB], int tile, int ksi, int lane) {
+  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
+  const int ks = a.ks, N = a.N;
   const int n = tile * kTile + lane;
   const bool valid = n < N;
   const float pre_scale = Q4 ? 1.f : reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
-  const int nb = (nrun + kRunsB - 1) / kRunsB;
-  for (int bt = 0; bt < nb; bt += 2) {
-    b_load<FMT, NB>(B, wr, sr, xr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    b_compute<FMT, NB>(acc, A, sm[0], lane);
-    if (bt + 1 >= nb) break;
-    b_load<FMT, NB>(A, wr, sr, xr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    b_compute<FMT, NB>(acc, B, sm[1], lane);
-  }
-
   if (ks > 1) {
     // split-K: the NB partials of this wave as device-coherent stores, counted after they are
     // acknowledged; the last wave of the tile adds all splits in split order, per column
@@ -240,8 +326,118 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a)
   }
 }
 
+template <int NB, int EPI>
+__global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
+  constexpr int CK = 32;
+  __shared__ StageM<NB> stage_all[kWavesB][2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kWavesB + wave;
+  const int ks = a.ks, K = a.K, N = a.N;
+  const int tiles = (N + kTile - 1) / kTile;
+  if (unit >= tiles * ks) return;  // whole wave
+  StageM<NB>(&sm)[2] = stage_all[wave];
+  const int tile = unit / ks;
+  const int ksi = unit - tile * ks;
+  const int nch = K / CK;
+  const int c0 = ksi * a.cps;
+  const int c1 = min(nch, c0 + a.cps);
+  const int nrun = c1 - c0;
+  const size_t tile_bytes = (size_t)nch * kTile * 16;
+  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
+  const int g0 = c0 >> a.gshift, g1 = (c1 - 1) >> a.gshift;
+  const __amdgpu_buffer_rsrc_t sr =
+      rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> a.gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
+           (uint32_t)(g1 - g0 + 1) * kTile * 2);
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.X, (uint32_t)((size_t)a.nb * a.ldx * 4));
+
+  float acc4[NB / 4][4];
+#pragma unroll
+  for (int bg = 0; bg < NB / 4; ++bg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc4[bg][r] = 0.f;
+  BatchM<NB> A, B;
+  m_load<NB>(A, wr, sr, xr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  const int nb = (nrun + kRunsB - 1) / kRunsB;
+  for (int bt = 0; bt < nb; bt += 2) {
+    m_load<NB>(B, wr, sr, xr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_compute<NB>(acc4, A, sm[0], lane);
+    if (bt + 1 >= nb) break;
+    m_load<NB>(A, wr, sr, xr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_compute<NB>(acc4, B, sm[1], lane);
+  }
+  // back to one row per lane: lane holds rows m_row0 + r of columns 4 bg + lane % 4
+  float *tr = reinterpret_cast<float *>(&sm[0]);  // [64][NB + 1]
+  const int r0 = m_row0(lane);
+#pragma unroll
+  for (int bg = 0; bg < NB / 4; ++bg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tr[(r0 + r) * (NB + 1) + 4 * bg + (lane & 3)] = acc4[bg][r];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = tr[lane * (NB + 1) + b];
+  b_finish<QDEC_W_Q4_G_ZP8, NB, EPI>(a, acc, tile, ksi, lane);
+}
+
+template <int FMT, int NB, int EPI>
+__global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a) {
+  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
+  constexpr int CK = Q4 ? 32 : 16;
+  __shared__ StageB<CK, NB> stage_all[kWavesB][2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kWavesB + wave;
+  const int ks = a.ks, K = a.K, N = a.N;
+  const int tiles = (N + kTile - 1) / kTile;
+  if (unit >= tiles * ks) return;  // whole wave
+  StageB<CK, NB>(&sm)[2] = stage_all[wave];
+  const int tile = unit / ks;
+  const int ksi = unit - tile * ks;
+  const int nch = K / CK;
+  const int c0 = ksi * a.cps;
+  const int c1 = min(nch, c0 + a.cps);
+  const int nrun = c1 - c0;
+  const size_t tile_bytes = (size_t)nch * kTile * 16;
+  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
+  __amdgpu_buffer_rsrc_t sr = wr;
+  int g0 = 0;
+  if constexpr (Q4) {
+    g0 = c0 >> a.gshift;
+    const int g1 = (c1 - 1) >> a.gshift;
+    sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> a.gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
+              (uint32_t)(g1 - g0 + 1) * kTile * 2);
+  }
+  // the nb columns' rows (each column reads only its own runs of the wave's k-range)
+  const __amdgpu_buffer_rsrc_t xr = rsrc(a.X, (uint32_t)((size_t)a.nb * a.ldx * 4));
+
+  float acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+  BatchB<FMT, NB> A, B;
+  b_load<FMT, NB>(A, wr, sr, xr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  const int nb = (nrun + kRunsB - 1) / kRunsB;
+  for (int bt = 0; bt < nb; bt += 2) {
+    b_load<FMT, NB>(B, wr, sr, xr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_compute<FMT, NB>(acc, A, sm[0], lane);
+    if (bt + 1 >= nb) break;
+    b_load<FMT, NB>(A, wr, sr, xr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_compute<FMT, NB>(acc, B, sm[1], lane);
+  }
+  b_finish<FMT, NB, EPI>(a, acc, tile, ksi, lane);
+}
+
 template <int FMT, int NB>
 hipError_t launch_nb(const GemmBArgs &a, int blocks, hipStream_t st) {
+  if constexpr (FMT == QDEC_W_Q4_G_ZP8 && NB >= 4) {
+    if (a.epi == EPI_SWIGLU)
+      hipLaunchKernelGGL((gemm_b_mfma<NB, EPI_SWIGLU>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((gemm_b_mfma<NB, EPI_STORE>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+    return hipGetLastError();
+  }
   if (a.epi == EPI_SWIGLU)
     hipLaunchKernelGGL((gemm_b_tile64<FMT, NB, EPI_SWIGLU>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
   else

@@ -253,3 +253,33 @@ def test_step_sampling_matches_sampler_on_its_logits():
         assert int(host(p.gpu.token)[0]) == int(np.argmax(host(p.gpu.logits)))
     assert host(p.gpu.token_log)[:4].tolist() == toks
     assert int(host(p.gpu.step_count)[0]) == 5 and int(host(p.gpu.pos)[0]) == p.pos0 + 5
+
+
+@pytest.mark.parametrize("name", ["qwen2.5-7b-q4", "qwen2.5-1.5b-q8", "qwen3-8b-q8", "qwen2.5-7b-q4-32k"])
+def test_full_model_graph_steps_match_oracle(name):
+    """Whole models in the benchmarked launch configuration (the Qwen2.5-7B-shape INT4 model with
+    its 4096-token shuffled paged bf16 context is the benchmark itself): every layer, default
+    attention splits, no per-layer trace, hipGraph replay.  Three steps, each against the oracle
+    continuing from the GPU's token: final hidden state, every logit and the greedy token to the
+    step bars."""
+    wl = synth.WORKLOADS[name]
+    p = Pair(wl, extra_tokens=8, trace=False)
+    assert p.gpu.cfg.num_splits == q.default_splits(wl.n_kv_heads, wl.ctx)
+    tok = p.model["token"]
+    with torch.cuda.stream(torch.cuda.Stream()):
+        for s in range(3):
+            p.gpu.step(q.STEP_GRAPH)
+            sync()
+            ref = p.orc.step(p.pos0 + s, tok)
+            e = rel_max_err(host(p.gpu.hidden), ref["h"])
+            assert e <= HIDDEN_TOL, "step %d: final hidden rel err %.3g" % (s, e)
+            lg = host(p.gpu.logits)
+            e = float(np.abs(lg - ref["logits"]).max())
+            assert e <= LOGIT_TOL, "step %d: logits max abs err %.3g" % (s, e)
+            gtok = int(host(p.gpu.token)[0])
+            if gtok != ref["token"]:
+                srt = np.sort(ref["logits"].astype(np.float64))
+                assert srt[-1] - srt[-2] <= LOGIT_TOL, (s, gtok, ref["token"])
+            tok = gtok
+            p.gpu.token.fill_(tok)
+    assert int(host(p.gpu.pos)[0]) == p.pos0 + 3

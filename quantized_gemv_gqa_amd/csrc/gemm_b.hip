@@ -161,7 +161,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4m __attribute__((ext_vector_type(4)));
 
-// fp16 pairs of the columns' activations for one batch of runs, in k order
+// fp16 pairs of the columns' activations for one batch of runs; within each group of 8 k the
+// order is k0, k4, k1, k5, k2, k6, k3, k7, the order in which a 32-bit word's nibbles come out of
+// the masks (so the codes need no permutes)
 template <int NB>
 struct StageM {
   _Float16 xh[NB][kRunsB * 32], xl[NB][kRunsB * 32];
@@ -215,9 +217,11 @@ __device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<
       const _Float16 h0 = (_Float16)v.x, h1 = (_Float16)v.y, h2 = (_Float16)v.z, h3 = (_Float16)v.w;
       const _Float16 l0 = (_Float16)(v.x - (float)h0), l1 = (_Float16)(v.y - (float)h1);
       const _Float16 l2 = (_Float16)(v.z - (float)h2), l3 = (_Float16)(v.w - (float)h3);
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<h4 *>(&sm.xh[b][q]) = h4{h0, h1, h2, h3};
-      *reinterpret_cast<h4 *>(&sm.xl[b][q]) = h4{l0, l1, l2, l3};
+      // k = q .. q + 3 go to positions 2 j + (q mod 8) / 4 of their group of 8
+      _Float16 *ph = &sm.xh[b][(q & ~7) + ((q >> 2) & 1)];
+      _Float16 *pl = &sm.xl[b][(q & ~7) + ((q >> 2) & 1)];
+      ph[0] = h0; ph[2] = h1; ph[4] = h2; ph[6] = h3;
+      pl[0] = l0; pl[2] = l1; pl[4] = l2; pl[6] = l3;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -237,17 +241,14 @@ __device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // the lane's codes k = 8 q .. 8 q + 7 of the run (byte b: k = 2 b low nibble, 2 b + 1 high
-      // nibble): 0x6400 | c is the fp16 1024 + c, minus 1032 gives c - 8 exactly
+      // nibble) in the staged order: 0x6400 | c is the fp16 1024 + c, minus 1032 gives c - 8
+      // exactly
       const uint32_t w = wd[q];
-      const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;          // (k0, k4)
-      const uint32_t p1 = ((w >> 4) & 0x000F000Fu) | 0x64006400u;   // (k1, k5)
-      const uint32_t p2 = ((w >> 8) & 0x000F000Fu) | 0x64006400u;   // (k2, k6)
-      const uint32_t p3 = ((w >> 12) & 0x000F000Fu) | 0x64006400u;  // (k3, k7)
-      const h2v c01 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p1, p0, 0x05040100u)) - off;
-      const h2v c23 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p3, p2, 0x05040100u)) - off;
-      const h2v c45 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p1, p0, 0x07060302u)) - off;
-      const h2v c67 = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(p3, p2, 0x07060302u)) - off;
-      const h8 av = {c01.x, c01.y, c23.x, c23.y, c45.x, c45.y, c67.x, c67.y};
+      const h2v c04 = __builtin_bit_cast(h2v, (w & 0x000F000Fu) | 0x64006400u) - off;
+      const h2v c15 = __builtin_bit_cast(h2v, ((w >> 4) & 0x000F000Fu) | 0x64006400u) - off;
+      const h2v c26 = __builtin_bit_cast(h2v, ((w >> 8) & 0x000F000Fu) | 0x64006400u) - off;
+      const h2v c37 = __builtin_bit_cast(h2v, ((w >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+      const h8 av = {c04.x, c04.y, c15.x, c15.y, c26.x, c26.y, c37.x, c37.y};
 #pragma unroll
       for (int bg = 0; bg < NB / 4; ++bg) {
         const int b = 4 * bg + bsub;

@@ -196,9 +196,9 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
   const __amdgpu_buffer_rsrc_t kr = rsrc(a.k_pool, pool_bytes), vr = rsrc(a.v_pool, pool_bytes);
   const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
 
-  // the wave's first PF pages are requested before anything else (one for fp32 rows of 128,
-  // whose two pages would not fit the registers)
-  constexpr int PF = (KVF == QDEC_KV_F32 && D == 128) ? 1 : 2;
+  // the wave's first page is requested before anything else.  (A second page buffer spilled
+  // registers of the 7-query-head unit and was slower at every context and batch measured.)
+  constexpr int PF = 1;
   Row<D, KVF> kp[PF][4], vp[PF][4];
   bool have[PF];
 #pragma unroll

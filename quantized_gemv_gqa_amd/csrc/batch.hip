@@ -9,11 +9,13 @@
 // steps: everything a kernel needs is read from device memory, so one captured graph serves every
 // step.
 //
-// How: per layer, rows RMSNorm -> skinny GEMM (qkv, bias) -> attention unit per (sequence, KV head,
-// split) (q/k norm, RoPE, KV append and split-K attention, as in the single-sequence step) ->
-// skinny GEMM (o, + residual) -> rows RMSNorm -> skinny GEMM (gate/up + SwiGLU) -> skinny GEMM
-// (down, + residual); then the lm head and a per-row argmax.  Each weight byte is read once per
-// step for all running sequences.
+// How: per layer, skinny GEMM (RMSNorm folded in, qkv, bias) -> attention unit per (sequence, KV
+// head, split) (q/k norm, RoPE, KV append and split-K attention, as in the single-sequence step) ->
+// skinny GEMM (o, + residual) -> skinny GEMM (RMSNorm folded in, gate/up + SwiGLU) -> skinny GEMM
+// (down, + residual); then the lm head (final RMSNorm folded in) and a per-row argmax.  Each
+// weight byte is read once per step for all running sequences.  The RMSNorms cost no launch: the
+// kernels that write the residual stream (the embedding, the o and down GEMMs) also write its sums
+// of squares per 64-row tile, and the next GEMM normalises its activations while staging them.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,7 +30,7 @@ struct qdec_batch {
   std::vector<void *> kpools, vpools;
   qdec_batch_state state;
   int B = 0, nb_max = 0;
-  float *a = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
+  float *ssq = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
   double *rope_cs = nullptr;
   char *attn_ws = nullptr;
   size_t attn_ws_stride = 0;
@@ -46,7 +48,7 @@ namespace {
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BLayout {
-  size_t a, qkv, attn, mlp, rope_cs, attn_ws, attn_stride, gemm_ws, arg_ws, total;
+  size_t ssq, qkv, attn, mlp, rope_cs, attn_ws, attn_stride, gemm_ws, arg_ws, total;
 };
 
 BLayout blayout(const qdec_config &c, int B) {
@@ -54,7 +56,7 @@ BLayout blayout(const qdec_config &c, int B) {
   const int nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim, qd = c.n_heads * c.head_dim;
   const int nbm = gemm_b_columns(B);
   size_t o = 0;
-  L.a = o; o += al256((size_t)B * c.hidden * 4);
+  L.ssq = o; o += al256((size_t)B * ((c.hidden + 63) / 64) * 4);
   L.qkv = o; o += al256((size_t)B * nqkv * 4);
   L.attn = o; o += al256((size_t)B * qd * 4);
   L.mlp = o; o += al256((size_t)B * c.inter * 4);
@@ -108,11 +110,20 @@ qdec_status enqueue_batch(qdec_batch *h, hipStream_t st, int *count) {
   const int nqkv = (Hq + 2 * Hkv) * D, qd = Hq * D;
   const int wf = c.wfmt;
   int n = 0;
-  QDEC_BCK(launch_embed_rows(h->model.embed, s.tokens, s.pos, B, H, V, s.hidden, c.rope_base, D, h->rope_cs, st));
+  // the residual stream's per-tile sums of squares: written by each kernel that writes s.hidden,
+  // read by the next GEMM, which normalises while staging
+  const auto normed = [&](GemmBArgs &g, const float *gamma) {
+    g.gamma = gamma;
+    g.ssq = h->ssq;
+    g.ssq_n = (H + 63) / 64;
+    g.eps = c.rms_eps;
+  };
+  QDEC_BCK(launch_embed_rows(h->model.embed, s.tokens, s.pos, B, H, V, s.hidden, h->ssq, c.rope_base, D, h->rope_cs,
+                             st));
   for (int l = 0; l < c.n_layers; ++l) {
     const qdec_layer_weights &w = h->layers[l];
-    QDEC_BCK(launch_rmsnorm_rows(s.hidden, w.g_attn, h->a, B, H, c.rms_eps, st));
-    GemmBArgs q = gargs(h, w.w_qkv, w.s_qkv, h->a, H, h->qkv, nqkv, nqkv, H);
+    GemmBArgs q = gargs(h, w.w_qkv, w.s_qkv, s.hidden, H, h->qkv, nqkv, nqkv, H);
+    normed(q, w.g_attn);
     q.bias = c.has_qkv_bias ? w.b_qkv : nullptr;
     QDEC_BCK(launch_gemm_b(wf, q, h->gemm_ws, st));
     AttnBatch ab{};
@@ -140,17 +151,19 @@ qdec_status enqueue_batch(qdec_batch *h, hipStream_t st, int *count) {
     QDEC_BCK(launch_attention_batch(ab, st));
     GemmBArgs o = gargs(h, w.w_o, w.s_o, h->attn, qd, s.hidden, H, H, qd);
     o.residual = s.hidden;
+    o.ssq_out = h->ssq;
     QDEC_BCK(launch_gemm_b(wf, o, h->gemm_ws, st));
-    QDEC_BCK(launch_rmsnorm_rows(s.hidden, w.g_ffn, h->a, B, H, c.rms_eps, st));
-    GemmBArgs g = gargs(h, w.w_gu, w.s_gu, h->a, H, h->mlp, I, 2 * I, H);
+    GemmBArgs g = gargs(h, w.w_gu, w.s_gu, s.hidden, H, h->mlp, I, 2 * I, H);
+    normed(g, w.g_ffn);
     g.epi = EPI_SWIGLU;
     QDEC_BCK(launch_gemm_b(wf, g, h->gemm_ws, st));
     GemmBArgs d = gargs(h, w.w_down, w.s_down, h->mlp, I, s.hidden, H, H, I);
     d.residual = s.hidden;
+    d.ssq_out = h->ssq;
     QDEC_BCK(launch_gemm_b(wf, d, h->gemm_ws, st));
   }
-  QDEC_BCK(launch_rmsnorm_rows(s.hidden, h->model.g_out, h->a, B, H, c.rms_eps, st));
-  GemmBArgs lm = gargs(h, h->model.w_lm, h->model.s_lm, h->a, H, s.logits, V, V, H);
+  GemmBArgs lm = gargs(h, h->model.w_lm, h->model.s_lm, s.hidden, H, s.logits, V, V, H);
+  normed(lm, h->model.g_out);
   QDEC_BCK(launch_gemm_b(wf, lm, h->gemm_ws, st));
   QDEC_BCK(launch_argmax_rows(s.logits, B, V, s.tokens, s.pos, h->arg_ws, st));
   ++n;  // (two launches)
@@ -244,7 +257,7 @@ qdec_status qdec_batch_create(const qdec_config *cfg, const qdec_model *m, const
   h->B = s->max_batch;
   h->nb_max = gemm_b_columns(h->B);
   char *ws = reinterpret_cast<char *>(s->workspace);
-  h->a = reinterpret_cast<float *>(ws + L.a);
+  h->ssq = reinterpret_cast<float *>(ws + L.ssq);
   h->qkv = reinterpret_cast<float *>(ws + L.qkv);
   h->attn = reinterpret_cast<float *>(ws + L.attn);
   h->mlp = reinterpret_cast<float *>(ws + L.mlp);

@@ -231,8 +231,8 @@ __global__ void __launch_bounds__(1024) argmax_finish_k(const float *__restrict_
 // grid (ceil(H / 256), B): h[b] = E[tokens[b]] for running rows; block (0, b) also writes row b's
 // RoPE table (the same angles as embed_k)
 __global__ void __launch_bounds__(256) embed_rows_k(const uint16_t *__restrict__ E, const int32_t *__restrict__ tokens,
-                                                    const int32_t *__restrict__ pos, int H, int V, float *h, float base,
-                                                    int D, double *__restrict__ cs) {
+                                                    const int32_t *__restrict__ pos, int H, int V, float *h,
+                                                    float *__restrict__ ssq, float base, int D, double *__restrict__ cs) {
   const int b = blockIdx.y;
   const int t = pos[b];
   if (t < 0) return;
@@ -249,7 +249,14 @@ __global__ void __launch_bounds__(256) embed_rows_k(const uint16_t *__restrict__
   int tok = tokens[b];
   if (tok < 0 || tok >= V) tok = 0;  // documented precondition; never read outside the table
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < H) h[(size_t)b * H + i] = __builtin_bit_cast(float, (uint32_t)E[(size_t)tok * H + i] << 16);
+  const float v = i < H ? __builtin_bit_cast(float, (uint32_t)E[(size_t)tok * H + i] << 16) : 0.f;
+  if (i < H) h[(size_t)b * H + i] = v;
+  // wave w of the block covers the 64-value tile 4 blockIdx.x + w
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (ssq && tile * 64 < H) {
+    const float sq = wave_sum(v * v);
+    if ((threadIdx.x & 63) == 0) ssq[(size_t)b * ((H + 63) / 64) + tile] = sq;
+  }
 }
 
 // one workgroup of 1024 threads per row: y = gamma * x / sqrt(mean(x^2) + eps); rows of a
@@ -511,9 +518,9 @@ hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int3
 }
 
 hipError_t launch_embed_rows(const uint16_t *E, const int32_t *tokens, const int32_t *pos, int B, int H, int V,
-                             float *h, float rope_base, int D, double *rope_cs, hipStream_t st) {
-  hipLaunchKernelGGL(embed_rows_k, dim3((H + 255) / 256, B), dim3(256), 0, st, E, tokens, pos, H, V, h, rope_base, D,
-                     rope_cs);
+                             float *h, float *ssq, float rope_base, int D, double *rope_cs, hipStream_t st) {
+  hipLaunchKernelGGL(embed_rows_k, dim3((H + 255) / 256, B), dim3(256), 0, st, E, tokens, pos, H, V, h, ssq, rope_base,
+                     D, rope_cs);
   return hipGetLastError();
 }
 

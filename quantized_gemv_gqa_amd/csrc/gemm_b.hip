@@ -26,6 +26,13 @@
 // (22 significant bits; two instructions), products are exact in fp32, the run's sum is scaled
 // by the group scale in fp32.  A final LDS transpose returns to one row per lane for the shared
 // split-K combine and epilogues.
+//
+// RMSNorm in front of the GEMM is folded in: with gamma set, column b is normalised while it is
+// staged, x_b[k] -> gamma[k] (x_b[k] r_b) with r_b = 1 / sqrt(mean_k x_b[k]^2 + eps) (FlashQwen
+// README, "Optimization study": norms fused into the neighbouring kernels), r_b taken from the
+// per-64-row-tile sums of squares that the producing GEMM (or the embedding) wrote in its
+// epilogue; so the staged values are exactly the normalised activations and no launch of its own
+// is needed.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -51,6 +58,7 @@ struct BatchB {
   u32x4 w[kRunsB];
   uint16_t s[kRunsB];
   f32x4 x[x_slots<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB>()];  // this lane's share of the activations
+  f32x4 g;  // RMSNorm gains of those activations (the same k in every slot)
 };
 
 template <int CK, int NB>
@@ -59,12 +67,67 @@ struct StageB {
   float zp[NB][kRunsB];
 };
 
-template <int FMT, int NB>
+// RMSNorm factors of the columns from the producer's per-tile sums of squares ([nb][ssq_n]),
+// in two halves so that the first batch of weights is requested in between: norm_issue loads the
+// first 64 tiles of every column, norm_finish adds the rest and reduces.  rl[i] = r_b of the column
+// b that activation slot i of this lane belongs to (0 past nb); every wave reduces in the same
+// order.
+template <int NB>
+__device__ __forceinline__ void norm_issue(float (&v)[NB], const GemmBArgs &a, int lane) {
+  const int n = a.ssq_n;
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.ssq, (uint32_t)((size_t)a.nb * n * 4));
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    v[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, lane < n ? (uint32_t)((b * n + lane) * 4) : 0x80000000u, 0, 0));
+}
+
+template <int CK, int NB, int XS>
+__device__ __forceinline__ void norm_finish(float (&rl)[XS], float (&s)[NB], const GemmBArgs &a, int lane) {
+  constexpr int PER_COL = kRunsB * CK / 4;
+  const int n = a.ssq_n;
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.ssq, (uint32_t)((size_t)a.nb * n * 4));
+  for (int t0 = 64; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    float v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      v[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, t < n ? (uint32_t)((b * n + t) * 4) : 0x80000000u, 0, 0));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b] += v[b];
+  }
+#pragma unroll
+  for (int i = 0; i < XS; ++i) rl[i] = 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= a.nb) break;
+    const float r = rsqrtf(wave_sum(s[b]) / (float)a.K + a.eps);
+#pragma unroll
+    for (int i = 0; i < XS; ++i)
+      if ((lane + 64 * i) / PER_COL == b) rl[i] = r;
+  }
+}
+
+// the gains of this lane's activation slots for the batch of runs at r (zero past the k-range)
+template <int CK>
+__device__ __forceinline__ f32x4 gain_load(__amdgpu_buffer_rsrc_t gr, int r, int c0, int nrun, int lane) {
+  constexpr int PER_COL = kRunsB * CK / 4;
+  const int q = (lane % PER_COL) * 4;
+  const uint32_t off = r + q / CK < nrun ? (uint32_t)(((size_t)(c0 + r) * CK + q) * 4) : 0x80000000u;
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
+}
+
+// x_b[k] -> gamma[k] (x_b[k] r_b), the order of operations of a separate RMSNorm
+__device__ __forceinline__ f32x4 normed(f32x4 v, f32x4 g, float r) {
+  return f32x4{g.x * (v.x * r), g.y * (v.y * r), g.z * (v.z * r), g.w * (v.w * r)};
+}
+
+template <int FMT, int NB, bool NORM>
 __device__ __forceinline__ void b_load(BatchB<FMT, NB> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
-                                       __amdgpu_buffer_rsrc_t xr, int ldx, int r, int c0, int nrun, int g0, int gshift,
-                                       int lane) {
+                                       __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int ldx, int r, int c0,
+                                       int nrun, int g0, int gshift, int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;
+  if constexpr (NORM) B.g = gain_load<CK>(gr, r, c0, nrun, lane);
   const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
 #pragma unroll
   for (int i = 0; i < kRunsB; ++i) {
@@ -87,9 +150,10 @@ __device__ __forceinline__ void b_load(BatchB<FMT, NB> &B, __amdgpu_buffer_rsrc_
   }
 }
 
-template <int FMT, int NB>
+template <int FMT, int NB, bool NORM>
 __device__ __forceinline__ void b_compute(float (&acc)[NB], const BatchB<FMT, NB> &B,
-                                          StageB<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB> &sm, int lane) {
+                                          StageB<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB> &sm,
+                                          const float (&rl)[x_slots<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB>()], int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;
   constexpr int PER_COL = kRunsB * CK / 4;
@@ -99,7 +163,8 @@ __device__ __forceinline__ void b_compute(float (&acc)[NB], const BatchB<FMT, NB
   for (int i = 0; i < x_slots<CK, NB>(); ++i) {
     const int f = lane + 64 * i;
     const int b = f / PER_COL, q = (f % PER_COL) * 4;
-    const f32x4 v = B.x[i];
+    f32x4 v = B.x[i];
+    if constexpr (NORM) v = normed(v, B.g, rl[i]);
     float part = (v.x + v.y) + (v.z + v.w);
     if constexpr (LPR == 8) {
       part = sum8(part);
@@ -174,17 +239,19 @@ struct BatchM {
   u32x4 w[kRunsB];
   uint64_t s4[kRunsB];  // fp16 scales of the four rows whose results this lane accumulates
   f32x4 x[x_slots<32, NB>()];
+  f32x4 g;
 };
 
 // first of the four consecutive tile rows whose results lane holds (MFMA output element
 // (4 (lane / 16) + r, lane % 16), column block lane % 16 / 4)
 __device__ __forceinline__ int m_row0(int lane) { return 4 * (lane >> 4) + 16 * ((lane & 15) >> 2); }
 
-template <int NB>
+template <int NB, bool NORM>
 __device__ __forceinline__ void m_load(BatchM<NB> &B, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
-                                       __amdgpu_buffer_rsrc_t xr, int ldx, int r, int c0, int nrun, int g0, int gshift,
-                                       int lane) {
+                                       __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int ldx, int r, int c0,
+                                       int nrun, int g0, int gshift, int lane) {
   constexpr int CK = 32;
+  if constexpr (NORM) B.g = gain_load<CK>(gr, r, c0, nrun, lane);
   const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
   const uint32_t r0 = (uint32_t)m_row0(lane);
 #pragma unroll
@@ -204,8 +271,9 @@ __device__ __forceinline__ void m_load(BatchM<NB> &B, __amdgpu_buffer_rsrc_t wr,
   }
 }
 
-template <int NB>
-__device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<NB> &B, StageM<NB> &sm, int lane) {
+template <int NB, bool NORM>
+__device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<NB> &B, StageM<NB> &sm,
+                                          const float (&rl)[x_slots<32, NB>()], int lane) {
   constexpr int CK = 32, PER_COL = kRunsB * CK / 4;
   // stage the activations as fp16 pairs
 #pragma unroll
@@ -213,7 +281,8 @@ __device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<
     const int f = lane + 64 * i;
     const int b = f / PER_COL, q = (f % PER_COL) * 4;
     if (b < NB) {
-      const f32x4 v = B.x[i];
+      f32x4 v = B.x[i];
+      if constexpr (NORM) v = normed(v, B.g, rl[i]);
       const _Float16 h0 = (_Float16)v.x, h1 = (_Float16)v.y, h2 = (_Float16)v.z, h3 = (_Float16)v.w;
       const _Float16 l0 = (_Float16)(v.x - (float)h0), l1 = (_Float16)(v.y - (float)h1);
       const _Float16 l2 = (_Float16)(v.z - (float)h2), l3 = (_Float16)(v.w - (float)h3);
@@ -319,15 +388,22 @@ __device__ __forceinline__ void b_finish(const GemmBArgs &a, float (&acc)[NB], i
       const float u = __shfl(v, lane + 32, 64);
       const int i = tile * 32 + lane;
       if (lane < 32 && i < N / 2) a.Y[(size_t)b * a.ldy + i] = silu(v) * u;
-    } else if (valid) {
-      if (a.bias) v += a.bias[n];
-      if (a.residual) v += a.residual[(size_t)b * a.ldy + n];
-      a.Y[(size_t)b * a.ldy + n] = v;
+    } else {
+      if (valid) {
+        if (a.bias) v += a.bias[n];
+        if (a.residual) v += a.residual[(size_t)b * a.ldy + n];
+        a.Y[(size_t)b * a.ldy + n] = v;
+      }
+      // the sum of squares of the tile's stored outputs, for an RMSNorm folded into the next GEMM
+      if (a.ssq_out) {
+        const float sq = wave_sum(valid ? v * v : 0.f);
+        if (lane == 0) a.ssq_out[(size_t)b * ((N + kTile - 1) / kTile) + tile] = sq;
+      }
     }
   }
 }
 
-template <int NB, int EPI>
+template <int NB, int EPI, bool NORM>
 __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
   constexpr int CK = 32;
   __shared__ StageM<NB> stage_all[kWavesB][2];
@@ -351,6 +427,9 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
       rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> a.gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
            (uint32_t)(g1 - g0 + 1) * kTile * 2);
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.X, (uint32_t)((size_t)a.nb * a.ldx * 4));
+  const __amdgpu_buffer_rsrc_t gr = rsrc(a.gamma, (uint32_t)K * 4);
+  float rl[x_slots<CK, NB>()], ss[NB];
+  if constexpr (NORM) norm_issue<NB>(ss, a, lane);
 
   float acc4[NB / 4][4];
 #pragma unroll
@@ -358,14 +437,15 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc4[bg][r] = 0.f;
   BatchM<NB> A, B;
-  m_load<NB>(A, wr, sr, xr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  m_load<NB, NORM>(A, wr, sr, xr, gr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  if constexpr (NORM) norm_finish<CK, NB>(rl, ss, a, lane);
   const int nb = (nrun + kRunsB - 1) / kRunsB;
   for (int bt = 0; bt < nb; bt += 2) {
-    m_load<NB>(B, wr, sr, xr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    m_compute<NB>(acc4, A, sm[0], lane);
+    m_load<NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_compute<NB, NORM>(acc4, A, sm[0], rl, lane);
     if (bt + 1 >= nb) break;
-    m_load<NB>(A, wr, sr, xr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    m_compute<NB>(acc4, B, sm[1], lane);
+    m_load<NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_compute<NB, NORM>(acc4, B, sm[1], rl, lane);
   }
   // back to one row per lane: lane holds rows m_row0 + r of columns 4 bg + lane % 4
   float *tr = reinterpret_cast<float *>(&sm[0]);  // [64][NB + 1]
@@ -383,7 +463,7 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
   b_finish<QDEC_W_Q4_G_ZP8, NB, EPI>(a, acc, tile, ksi, lane);
 }
 
-template <int FMT, int NB, int EPI>
+template <int FMT, int NB, int EPI, bool NORM>
 __global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;
@@ -413,36 +493,42 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a)
   }
   // the nb columns' rows (each column reads only its own runs of the wave's k-range)
   const __amdgpu_buffer_rsrc_t xr = rsrc(a.X, (uint32_t)((size_t)a.nb * a.ldx * 4));
+  const __amdgpu_buffer_rsrc_t gr = rsrc(a.gamma, (uint32_t)K * 4);
+  float rl[x_slots<CK, NB>()], ss[NB];
+  if constexpr (NORM) norm_issue<NB>(ss, a, lane);
 
   float acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = 0.f;
   BatchB<FMT, NB> A, B;
-  b_load<FMT, NB>(A, wr, sr, xr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  b_load<FMT, NB, NORM>(A, wr, sr, xr, gr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
+  if constexpr (NORM) norm_finish<CK, NB>(rl, ss, a, lane);
   const int nb = (nrun + kRunsB - 1) / kRunsB;
   for (int bt = 0; bt < nb; bt += 2) {
-    b_load<FMT, NB>(B, wr, sr, xr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    b_compute<FMT, NB>(acc, A, sm[0], lane);
+    b_load<FMT, NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_compute<FMT, NB, NORM>(acc, A, sm[0], rl, lane);
     if (bt + 1 >= nb) break;
-    b_load<FMT, NB>(A, wr, sr, xr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
-    b_compute<FMT, NB>(acc, B, sm[1], lane);
+    b_load<FMT, NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_compute<FMT, NB, NORM>(acc, B, sm[1], rl, lane);
   }
   b_finish<FMT, NB, EPI>(a, acc, tile, ksi, lane);
 }
 
+template <int FMT, int NB, int EPI, bool NORM>
+void launch_k(const GemmBArgs &a, int blocks, hipStream_t st) {
+  if constexpr (FMT == QDEC_W_Q4_G_ZP8 && NB >= 4)
+    hipLaunchKernelGGL((gemm_b_mfma<NB, EPI, NORM>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_b_tile64<FMT, NB, EPI, NORM>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+}
+
 template <int FMT, int NB>
 hipError_t launch_nb(const GemmBArgs &a, int blocks, hipStream_t st) {
-  if constexpr (FMT == QDEC_W_Q4_G_ZP8 && NB >= 4) {
-    if (a.epi == EPI_SWIGLU)
-      hipLaunchKernelGGL((gemm_b_mfma<NB, EPI_SWIGLU>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
-    else
-      hipLaunchKernelGGL((gemm_b_mfma<NB, EPI_STORE>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
-    return hipGetLastError();
-  }
+  const bool norm = a.gamma != nullptr;
   if (a.epi == EPI_SWIGLU)
-    hipLaunchKernelGGL((gemm_b_tile64<FMT, NB, EPI_SWIGLU>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+    norm ? launch_k<FMT, NB, EPI_SWIGLU, true>(a, blocks, st) : launch_k<FMT, NB, EPI_SWIGLU, false>(a, blocks, st);
   else
-    hipLaunchKernelGGL((gemm_b_tile64<FMT, NB, EPI_STORE>), dim3(blocks), dim3(kWavesB * 64), 0, st, a);
+    norm ? launch_k<FMT, NB, EPI_STORE, true>(a, blocks, st) : launch_k<FMT, NB, EPI_STORE, false>(a, blocks, st);
   return hipGetLastError();
 }
 

@@ -21,6 +21,16 @@ struct GemmBArgs {
   int nb, nb_max;
   int epi;                 // EPI_STORE or EPI_SWIGLU
   const int32_t *pos;      // [nb] or null: columns with pos[b] < 0 are computed but not stored
+  // Folded RMSNorm (gamma non-null): column b is used as gamma * x_b / sqrt(mean(x_b^2) + eps),
+  // with sum(x_b^2) the sum of ssq[b * ssq_n + t] over t < ssq_n (per-64-row-tile sums, written
+  // by the producer of X).
+  const float *gamma;
+  const float *ssq;
+  int ssq_n;
+  float eps;
+  // EPI_STORE: if non-null, ssq_out[b * ceil(N / 64) + t] = sum of the squares of column b's
+  // stored outputs in rows 64 t .. 64 t + 63 (stored columns only)
+  float *ssq_out;
 };
 int gemm_b_columns(int batch);  // nb_max for a batch size (2, 4 or 8)
 size_t gemm_b_workspace_bytes(int wfmt, int N, int K, int nb_max);
@@ -89,9 +99,10 @@ struct AttnRows {
 hipError_t launch_attention_rows(const AttnRows &r, hipStream_t st);
 
 // Row kernels of the batched step (elementwise.hip).  A row b with pos[b] < 0 is idle.
-// h[b] = bf16 -> fp32 E[tokens[b]]; rope_cs[b] = the fp64 (cos, sin) table of pos[b] (D/2 pairs)
+// h[b] = bf16 -> fp32 E[tokens[b]]; rope_cs[b] = the fp64 (cos, sin) table of pos[b] (D/2 pairs);
+// ssq (if non-null) [B][ceil(H / 64)]: the sums of squares of h[b] per 64-value tile
 hipError_t launch_embed_rows(const uint16_t *E, const int32_t *tokens, const int32_t *pos, int B, int H, int V,
-                             float *h, float rope_base, int D, double *rope_cs, hipStream_t st);
+                             float *h, float *ssq, float rope_base, int D, double *rope_cs, hipStream_t st);
 // y[b] = gamma * x[b] / sqrt(mean(x[b]^2) + eps); dim a multiple of 4, at most 16384; x, y, gamma
 // 16-byte aligned
 hipError_t launch_rmsnorm_rows(const float *x, const float *gamma, float *y, int B, int dim, float eps, hipStream_t st);

@@ -130,7 +130,7 @@ def test_batch_step_matches_oracle():
                     assert pg[b] == ps[b] + 1
                     toks[b] = tg[b]
                     pos[b] += 1
-    assert bt.gpu.kernel_count == 1 + 7 * 2 + 4
+    assert bt.gpu.kernel_count == 1 + 5 * 2 + 3
 
 
 def test_batch_placement_does_not_matter():

@@ -58,7 +58,7 @@ class Batch:
     """One batched workload on both sides: device pools/tables and the oracle's copy."""
 
     def __init__(self, name, ctxs, n_layers=2, max_blocks=None, spare=8):
-        wl = synth.WORKLOADS[name]
+        wl = synth.WORKLOADS[name] if isinstance(name, str) else name
         self.wl = wl
         self.model = synth.make_model(wl, n_layers=n_layers)
         mb = max_blocks or max(-(-(c + 8) // 16) for c in ctxs) + 1
@@ -131,6 +131,32 @@ def test_batch_step_matches_oracle():
                     toks[b] = tg[b]
                     pos[b] += 1
     assert bt.gpu.kernel_count == 1 + 5 * 2 + 3
+
+
+@pytest.mark.parametrize("wfmt", ["q4", "q8"])
+@pytest.mark.parametrize("ctxs", [[20, 33], [20, 33, 7], [5, 9, 17, 30, 41, 47, 64, 70]])
+def test_batch_wide_hidden_matches_oracle(wfmt, ctxs):
+    """Hidden 4160 (65 tiles of 64 rows): each folded RMSNorm adds more than 64 per-tile sums of
+    squares per column, and the last tile is ragged for the norm's producers; 2, 3 and 8 slots take
+    the two-column, four-column and eight-column GEMMs."""
+    from dataclasses import replace
+    wl = replace(synth.WORKLOADS["qwen2.5-7b-q4"], name="wide-h4160-" + wfmt, hidden=4160, inter=512, vocab=1000,
+                 wfmt=wfmt, ctx=64, shuffled_pages=True, seed=1010)
+    bt = Batch(wl, ctxs, n_layers=1)
+    B = len(ctxs)
+    toks = (np.arange(B, dtype=np.int32) * 97 + 3) % wl.vocab
+    pos = np.array(ctxs, np.int32)
+    with torch.cuda.stream(torch.cuda.Stream()):
+        for s in range(2):
+            bt.map_blocks(pos)
+            bt.d_pos.copy_(torch.from_numpy(pos))
+            bt.d_tok.copy_(torch.from_numpy(toks))
+            bt.gpu.step(q.STEP_GRAPH)
+            sync()
+            nxt, lg = bt.orc.step_batch(bt.tables, pos, toks, bt.h_orc)
+            tg = _check_slots(bt, pos, toks, nxt, lg, "step %d" % s)
+            toks = tg.astype(np.int32)
+            pos = pos + 1
 
 
 def test_batch_placement_does_not_matter():

@@ -46,25 +46,29 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRunsB = 4;  // weight runs per pipeline batch
+// weight runs per pipeline batch: shorter batches keep more waves resident; at 8 columns the
+// staged activations of one run already fill the wave (measured on MI355X, 7B shapes: 2 runs at
+// 2 and 4 columns, 1 run at 8)
+template <int NB>
+constexpr int kRuns = NB >= 8 ? 1 : 2;
 constexpr int kWavesB = 4;
 
 // f32x4 slots per lane that hold the NB columns' activation chunks of one batch of runs
 template <int CK, int NB>
-constexpr int x_slots() { return (NB * kRunsB * CK / 4 + 63) / 64; }
+constexpr int x_slots() { return (NB * kRuns<NB> * CK / 4 + 63) / 64; }
 
 template <int FMT, int NB>
 struct BatchB {
-  u32x4 w[kRunsB];
-  uint16_t s[kRunsB];
+  u32x4 w[kRuns<NB>];
+  uint16_t s[kRuns<NB>];
   f32x4 x[x_slots<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB>()];  // this lane's share of the activations
   f32x4 g;  // RMSNorm gains of those activations (the same k in every slot)
 };
 
 template <int CK, int NB>
 struct StageB {
-  float x[NB][kRunsB * CK];
-  float zp[NB][kRunsB];
+  float x[NB][kRuns<NB> * CK];
+  float zp[NB][kRuns<NB>];
 };
 
 // RMSNorm factors of the columns from the producer's per-tile sums of squares ([nb][ssq_n]),
@@ -83,7 +87,7 @@ __device__ __forceinline__ void norm_issue(float (&v)[NB], const GemmBArgs &a, i
 
 template <int CK, int NB, int XS>
 __device__ __forceinline__ void norm_finish(float (&rl)[XS], float (&s)[NB], const GemmBArgs &a, int lane) {
-  constexpr int PER_COL = kRunsB * CK / 4;
+  constexpr int PER_COL = kRuns<NB> * CK / 4;
   const int n = a.ssq_n;
   const __amdgpu_buffer_rsrc_t qr = rsrc(a.ssq, (uint32_t)((size_t)a.nb * n * 4));
   for (int t0 = 64; t0 < n; t0 += 64) {
@@ -108,9 +112,9 @@ __device__ __forceinline__ void norm_finish(float (&rl)[XS], float (&s)[NB], con
 }
 
 // the gains of this lane's activation slots for the batch of runs at r (zero past the k-range)
-template <int CK>
+template <int CK, int NB>
 __device__ __forceinline__ f32x4 gain_load(__amdgpu_buffer_rsrc_t gr, int r, int c0, int nrun, int lane) {
-  constexpr int PER_COL = kRunsB * CK / 4;
+  constexpr int PER_COL = kRuns<NB> * CK / 4;
   const int q = (lane % PER_COL) * 4;
   const uint32_t off = r + q / CK < nrun ? (uint32_t)(((size_t)(c0 + r) * CK + q) * 4) : 0x80000000u;
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
@@ -127,10 +131,10 @@ __device__ __forceinline__ void b_load(BatchB<FMT, NB> &B, __amdgpu_buffer_rsrc_
                                        int nrun, int g0, int gshift, int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;
-  if constexpr (NORM) B.g = gain_load<CK>(gr, r, c0, nrun, lane);
+  if constexpr (NORM) B.g = gain_load<CK, NB>(gr, r, c0, nrun, lane);
   const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
 #pragma unroll
-  for (int i = 0; i < kRunsB; ++i) {
+  for (int i = 0; i < kRuns<NB>; ++i) {
     B.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, base + i * (kTile * 16), 0, kAuxStream));
     if constexpr (Q4) {
       const int g = ((c0 + r + i) >> gshift) - g0;
@@ -139,7 +143,7 @@ __device__ __forceinline__ void b_load(BatchB<FMT, NB> &B, __amdgpu_buffer_rsrc_
   }
   // column b, 4 values at chunk offset q: flat f = lane + 64 i, b = f / PER_COL, q = 4 (f % PER_COL);
   // runs past the wave's last one read zero (as their weights and scales do)
-  constexpr int PER_COL = kRunsB * CK / 4;  // f32x4 per column per batch
+  constexpr int PER_COL = kRuns<NB> * CK / 4;  // f32x4 per column per batch
 #pragma unroll
   for (int i = 0; i < x_slots<CK, NB>(); ++i) {
     const int f = lane + 64 * i;
@@ -156,7 +160,7 @@ __device__ __forceinline__ void b_compute(float (&acc)[NB], const BatchB<FMT, NB
                                           const float (&rl)[x_slots<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16, NB>()], int lane) {
   constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
   constexpr int CK = Q4 ? 32 : 16;
-  constexpr int PER_COL = kRunsB * CK / 4;
+  constexpr int PER_COL = kRuns<NB> * CK / 4;
   constexpr int LPR = CK / 4;  // lanes (f32x4 slots) per run
   // stage the activations and each (column, run)'s sum of x
 #pragma unroll
@@ -181,7 +185,7 @@ __device__ __forceinline__ void b_compute(float (&acc)[NB], const BatchB<FMT, NB
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int i = 0; i < kRunsB; ++i) {
+  for (int i = 0; i < kRuns<NB>; ++i) {
     // the run's codes as floats, in k order
     float c[CK];
     const uint32_t wd[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
@@ -231,13 +235,13 @@ typedef float f4m __attribute__((ext_vector_type(4)));
 // the masks (so the codes need no permutes)
 template <int NB>
 struct StageM {
-  _Float16 xh[NB][kRunsB * 32], xl[NB][kRunsB * 32];
+  _Float16 xh[NB][kRuns<NB> * 32], xl[NB][kRuns<NB> * 32];
 };
 
 template <int NB>
 struct BatchM {
-  u32x4 w[kRunsB];
-  uint64_t s4[kRunsB];  // fp16 scales of the four rows whose results this lane accumulates
+  u32x4 w[kRuns<NB>];
+  uint64_t s4[kRuns<NB>];  // fp16 scales of the four rows whose results this lane accumulates
   f32x4 x[x_slots<32, NB>()];
   f32x4 g;
 };
@@ -251,16 +255,16 @@ __device__ __forceinline__ void m_load(BatchM<NB> &B, __amdgpu_buffer_rsrc_t wr,
                                        __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t gr, int ldx, int r, int c0,
                                        int nrun, int g0, int gshift, int lane) {
   constexpr int CK = 32;
-  if constexpr (NORM) B.g = gain_load<CK>(gr, r, c0, nrun, lane);
+  if constexpr (NORM) B.g = gain_load<CK, NB>(gr, r, c0, nrun, lane);
   const uint32_t base = (uint32_t)r * (kTile * 16) + lane * 16;
   const uint32_t r0 = (uint32_t)m_row0(lane);
 #pragma unroll
-  for (int i = 0; i < kRunsB; ++i) {
+  for (int i = 0; i < kRuns<NB>; ++i) {
     B.w[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, base + i * (kTile * 16), 0, kAuxStream));
     const int g = ((c0 + r + i) >> gshift) - g0;
     B.s4[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(sr, (uint32_t)g * (kTile * 2) + r0 * 2, 0, 0));
   }
-  constexpr int PER_COL = kRunsB * CK / 4;
+  constexpr int PER_COL = kRuns<NB> * CK / 4;
 #pragma unroll
   for (int i = 0; i < x_slots<CK, NB>(); ++i) {
     const int f = lane + 64 * i;
@@ -274,7 +278,7 @@ __device__ __forceinline__ void m_load(BatchM<NB> &B, __amdgpu_buffer_rsrc_t wr,
 template <int NB, bool NORM>
 __device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<NB> &B, StageM<NB> &sm,
                                           const float (&rl)[x_slots<32, NB>()], int lane) {
-  constexpr int CK = 32, PER_COL = kRunsB * CK / 4;
+  constexpr int CK = 32, PER_COL = kRuns<NB> * CK / 4;
   // stage the activations as fp16 pairs
 #pragma unroll
   for (int i = 0; i < x_slots<CK, NB>(); ++i) {
@@ -302,7 +306,7 @@ __device__ __forceinline__ void m_compute(float (&acc)[NB / 4][4], const BatchM<
   h8 xh = {}, xl = {};
   const h2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
-  for (int i = 0; i < kRunsB; ++i) {
+  for (int i = 0; i < kRuns<NB>; ++i) {
     const uint32_t wd[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
     f4m c[NB / 4];
 #pragma unroll
@@ -406,14 +410,20 @@ __device__ __forceinline__ void b_finish(const GemmBArgs &a, float (&acc)[NB], i
 template <int NB, int EPI, bool NORM>
 __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
   constexpr int CK = 32;
-  __shared__ StageM<NB> stage_all[kWavesB][2];
+  // per wave: the two stage slots, reused at the end for the [64][NB + 1] transpose (which is
+  // larger than the slots when a batch holds one run)
+  union WaveLds {
+    StageM<NB> st[2];
+    float tr[64 * (NB + 1)];
+  };
+  __shared__ WaveLds lds_all[kWavesB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * kWavesB + wave;
   const int ks = a.ks, K = a.K, N = a.N;
   const int tiles = (N + kTile - 1) / kTile;
   if (unit >= tiles * ks) return;  // whole wave
-  StageM<NB>(&sm)[2] = stage_all[wave];
+  StageM<NB>(&sm)[2] = lds_all[wave].st;
   const int tile = unit / ks;
   const int ksi = unit - tile * ks;
   const int nch = K / CK;
@@ -439,16 +449,16 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_mfma(const GemmBArgs a) {
   BatchM<NB> A, B;
   m_load<NB, NORM>(A, wr, sr, xr, gr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
   if constexpr (NORM) norm_finish<CK, NB>(rl, ss, a, lane);
-  const int nb = (nrun + kRunsB - 1) / kRunsB;
+  const int nb = (nrun + kRuns<NB> - 1) / kRuns<NB>;
   for (int bt = 0; bt < nb; bt += 2) {
-    m_load<NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_load<NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRuns<NB>, c0, nrun, g0, a.gshift, lane);
     m_compute<NB, NORM>(acc4, A, sm[0], rl, lane);
     if (bt + 1 >= nb) break;
-    m_load<NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    m_load<NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRuns<NB>, c0, nrun, g0, a.gshift, lane);
     m_compute<NB, NORM>(acc4, B, sm[1], rl, lane);
   }
   // back to one row per lane: lane holds rows m_row0 + r of columns 4 bg + lane % 4
-  float *tr = reinterpret_cast<float *>(&sm[0]);  // [64][NB + 1]
+  float *tr = lds_all[wave].tr;  // [64][NB + 1]
   const int r0 = m_row0(lane);
 #pragma unroll
   for (int bg = 0; bg < NB / 4; ++bg)
@@ -503,12 +513,12 @@ __global__ void __launch_bounds__(kWavesB * 64) gemm_b_tile64(const GemmBArgs a)
   BatchB<FMT, NB> A, B;
   b_load<FMT, NB, NORM>(A, wr, sr, xr, gr, a.ldx, 0, c0, nrun, g0, a.gshift, lane);
   if constexpr (NORM) norm_finish<CK, NB>(rl, ss, a, lane);
-  const int nb = (nrun + kRunsB - 1) / kRunsB;
+  const int nb = (nrun + kRuns<NB> - 1) / kRuns<NB>;
   for (int bt = 0; bt < nb; bt += 2) {
-    b_load<FMT, NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_load<FMT, NB, NORM>(B, wr, sr, xr, gr, a.ldx, (bt + 1) * kRuns<NB>, c0, nrun, g0, a.gshift, lane);
     b_compute<FMT, NB, NORM>(acc, A, sm[0], rl, lane);
     if (bt + 1 >= nb) break;
-    b_load<FMT, NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRunsB, c0, nrun, g0, a.gshift, lane);
+    b_load<FMT, NB, NORM>(A, wr, sr, xr, gr, a.ldx, (bt + 2) * kRuns<NB>, c0, nrun, g0, a.gshift, lane);
     b_compute<FMT, NB, NORM>(acc, B, sm[1], rl, lane);
   }
   b_finish<FMT, NB, EPI>(a, acc, tile, ksi, lane);

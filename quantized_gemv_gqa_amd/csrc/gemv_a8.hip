@@ -101,12 +101,15 @@ __device__ __forceinline__ void a8_compute(float &acc, const BatchA8<FMT> &B, St
     const int run = lane >> 3, j = (lane >> 1) & 3, h = lane & 1;
     const uint32_t ev = __builtin_amdgcn_perm(0u, B.q, 0x0c0c0200u);  // bytes 0, 2 (even k)
     const uint32_t od = __builtin_amdgcn_perm(0u, B.q, 0x0c0c0301u);  // bytes 1, 3 (odd k)
-    uint16_t *q16 = reinterpret_cast<uint16_t *>(sm.q);
-    q16[run * 16 + j * 2 + h] = (uint16_t)ev;
-    q16[run * 16 + 8 + j * 2 + h] = (uint16_t)od;
-    // sum of the run's 32 codes (8 lanes), exact in fp32
+    // sum of the run's 32 codes (8 lanes), exact in fp32 (every lane takes part in the DPP sum;
+    // only the lanes that hold the batch's runs store)
     const float part = sum8((float)__builtin_amdgcn_sdot4((int)B.q, 0x01010101, 0, false));
-    if ((lane & 7) == 0) sm.zp[run] = -8 * (int)part;
+    if (lane * 4 < kBatch * CK) {
+      uint16_t *q16 = reinterpret_cast<uint16_t *>(sm.q);
+      q16[run * 16 + j * 2 + h] = (uint16_t)ev;
+      q16[run * 16 + 8 + j * 2 + h] = (uint16_t)od;
+      if ((lane & 7) == 0) sm.zp[run] = -8 * (int)part;
+    }
   } else {
     if (lane * 4 < kBatch * CK) sm.q[lane] = B.q;
     if (lane < kBatch) sm.zp[lane] = 0;

@@ -13,7 +13,10 @@ namespace dev {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBatch = 8;       // 16-byte weight runs a lane loads before computing
+// 16-byte weight runs a lane loads before computing.  Four (with the next four in flight) keep
+// the INT4 GEMV under 100 VGPRs, four or five waves per SIMD; eight ran at three waves per SIMD
+// and made the 7B decode step 5 % slower, two or three left too few bytes in flight.
+constexpr int kBatch = 4;
 constexpr int kAuxStream = 2;   // nt: weights are read once per step, do not keep them in L2
 constexpr int kAuxSc1 = 16;     // sc1: device-coherent access (bypasses non-coherent L2 copies)
 constexpr unsigned kSpinLimit = 1u << 24;  // bounded waits: ~1 s of polling, then give up

@@ -35,7 +35,7 @@ using namespace dev;
 // Waves a launch aims for: few k-splits keep the split-K tail short on small matrices (up to 128
 // tiles), more waves stream the large ones (measured on MI355X).
 constexpr int kTargetUnitsSmall = 1024;
-constexpr int kTargetUnitsLarge = 3072;
+constexpr int kTargetUnitsLarge = 2048;
 constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
 
 // Standalone launch: one wave per (tile, k-split) unit, no cross-phase dependency.

@@ -95,6 +95,9 @@ def lib(path: str | None = None):
         L.orc_decode_step.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Layer),
                                       ctypes.POINTER(_Head), _P, I, I, _P, _P, _P, I]
         L.orc_decode_step.restype = I
+        L.orc_decode_step_kv.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(_Layer),
+                                         ctypes.POINTER(_Head), _P, I, I, _P, _P, _P, I, _P, _P, _P]
+        L.orc_decode_step_kv.restype = I
         _lib = L
     return _lib
 
@@ -302,11 +305,25 @@ class OracleDecoder:
                                _p(tk), _p(h), _p(lg), _p(nxt), self.nthreads)
         return nxt, lg
 
-    def step(self, pos: int, token: int = 0, trace: bool = False, logits: bool = True):
+    def step(self, pos: int, token: int = 0, trace: bool = False, logits: bool = True, kv_pre: bool = False,
+             kv_force: dict | None = None):
+        """One decode step.  kv_pre: also return the new token's fp32 k, v per layer before they are
+        rounded into the cache ("kv_pre", [L][2][Hkv][D]).  kv_force: {layer: (k_codes, v_codes)}
+        of bf16 codes ([Hkv][D] uint16) stored as the new token's entries of those layers instead
+        of the rounding (teacher forcing of a rounding tie)."""
         wl = self.wl
-        tr = np.empty((self.cfg.n_layers + 1, wl.hidden), np.float32) if trace else None
+        L = self.cfg.n_layers
+        tr = np.empty((L + 1, wl.hidden), np.float32) if trace else None
         lg = np.empty(wl.vocab, np.float32) if (logits and wl.has_lm_head) else None
-        nxt = lib().orc_decode_step(ctypes.byref(self.cfg), self.layers, ctypes.byref(self.head),
-                                    _p(self.page_table), int(pos), int(token), _p(self.h), _p(tr),
-                                    _p(lg), self.nthreads)
-        return {"token": nxt, "trace": tr, "logits": lg, "h": self.h.copy()}
+        pre = np.empty((L, 2, wl.n_kv_heads, wl.head_dim), np.float32) if kv_pre else None
+        force = mask = None
+        if kv_force:
+            assert wl.kv_fmt == "bf16", "forced cache codes are bf16"
+            force = np.zeros((L, 2, wl.n_kv_heads, wl.head_dim), np.uint16)
+            mask = np.zeros(L, np.uint8)
+            for l, (kc, vc) in kv_force.items():
+                force[l, 0], force[l, 1], mask[l] = kc, vc, 1
+        nxt = lib().orc_decode_step_kv(ctypes.byref(self.cfg), self.layers, ctypes.byref(self.head),
+                                       _p(self.page_table), int(pos), int(token), _p(self.h), _p(tr),
+                                       _p(lg), self.nthreads, _p(pre), _p(force), _p(mask))
+        return {"token": nxt, "trace": tr, "logits": lg, "h": self.h.copy(), "kv_pre": pre}

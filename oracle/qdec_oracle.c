@@ -427,6 +427,21 @@ int orc_sample(const float *logits, int V, double temperature, int top_k, double
 int orc_decode_step(const orc_config *c, const orc_layer *layers, const orc_head *head,
                     const int32_t *page_table, int pos, int token, float *h, float *trace,
                     float *logits, int nthreads) {
+  return orc_decode_step_kv(c, layers, head, page_table, pos, token, h, trace, logits, nthreads, NULL, NULL, NULL);
+}
+
+/* Stores given bf16 codes as token t's entries of one layer's pool (the layout of orc_kv_store). */
+static void kv_store_codes(void *pool, const int32_t *page_table, int page_size, int n_kv_heads, int head_dim,
+                           int t, const uint16_t *codes) {
+  for (int j = 0; j < n_kv_heads; ++j)
+    for (int d = 0; d < head_dim; ++d)
+      ((uint16_t *)pool)[kv_index(page_table, page_size, n_kv_heads, head_dim, t, j, d)] = codes[j * head_dim + d];
+}
+
+int orc_decode_step_kv(const orc_config *c, const orc_layer *layers, const orc_head *head,
+                       const int32_t *page_table, int pos, int token, float *h, float *trace,
+                       float *logits, int nthreads, float *kv_pre, const uint16_t *kv_force,
+                       const uint8_t *force_mask) {
   const int H = c->hidden, Hq = c->n_heads, Hkv = c->n_kv_heads, D = c->head_dim, I = c->inter;
   const int qd = Hq * D, kvd = Hkv * D, T = pos + 1;
   const double scale = 1.0 / sqrt((double)D);
@@ -461,8 +476,17 @@ int orc_decode_step(const orc_config *c, const orc_layer *layers, const orc_head
     orc_rope(q, Hq, D, pos, c->rope_base);
     orc_rope(k, Hkv, D, pos, c->rope_base);
     /* append the new token, then attend over keys 0..pos read back from the cache */
-    orc_kv_store(L->k_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, k);
-    orc_kv_store(L->v_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, v);
+    if (kv_pre) {
+      memcpy(kv_pre + (int64_t)(2 * l) * kvd, k, sizeof(float) * (size_t)kvd);
+      memcpy(kv_pre + (int64_t)(2 * l + 1) * kvd, v, sizeof(float) * (size_t)kvd);
+    }
+    if (kv_force && force_mask && force_mask[l] && c->kv_fmt == ORC_KV_BF16) {
+      kv_store_codes(L->k_pool, page_table, c->page_size, Hkv, D, pos, kv_force + (int64_t)(2 * l) * kvd);
+      kv_store_codes(L->v_pool, page_table, c->page_size, Hkv, D, pos, kv_force + (int64_t)(2 * l + 1) * kvd);
+    } else {
+      orc_kv_store(L->k_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, k);
+      orc_kv_store(L->v_pool, c->kv_fmt, page_table, c->page_size, Hkv, D, pos, v);
+    }
     orc_attention(q, L->k_pool, L->v_pool, c->kv_fmt, page_table, c->page_size, T, Hq, Hkv, D, scale,
                   att, NULL);
     orc_gemv(c->wfmt, L->wo, L->so, c->group, att, NULL, h, h, H, qd, nthreads);

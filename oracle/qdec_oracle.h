@@ -99,6 +99,22 @@ int orc_decode_step(const orc_config *cfg, const orc_layer *layers, const orc_he
                     const int32_t *page_table, int pos, int token, float *h, float *trace,
                     float *logits, int nthreads);
 
+/*
+ * The same step with the new token's cache entries exposed, for comparisons in which the
+ * rounding of a stored value is a tie (both neighbouring codes are correct roundings within
+ * fp32 accumulation error):
+ *   kv_pre: optional out [L][2][Hkv * D], the fp32 k (after q/k norm and RoPE) and v of the new
+ *           token at each layer, before they are rounded into the cache;
+ *   kv_force, force_mask: optional (bf16 pools only): for every layer l with force_mask[l] != 0
+ *           the new token's entries are stored as the given codes kv_force[l][0] (k) and
+ *           kv_force[l][1] (v), [Hkv * D] each, instead of the rounding of kv_pre; the layer
+ *           then attends over the cache as always.  Everything else is unchanged.
+ */
+int orc_decode_step_kv(const orc_config *cfg, const orc_layer *layers, const orc_head *head,
+                       const int32_t *page_table, int pos, int token, float *h, float *trace,
+                       float *logits, int nthreads, float *kv_pre, const uint16_t *kv_force,
+                       const uint8_t *force_mask);
+
 /* Batched decode: the single-sequence step for every slot b with pos[b] >= 0, with block table
    row b ([B][max_blocks]), token tokens[b] and residual stream h[b] ([B][H]); logits [B][V] or
    NULL; next[b] gets the greedy token (idle slots untouched). */

@@ -57,8 +57,11 @@ class NumpyDecoder:
         self.K = [list(k) for k in kv_logical_k]
         self.V = [list(v) for v in kv_logical_v]
 
-    def step(self, pos: int, token: int):
+    def step(self, pos: int, token: int, kv_hook=None):
+        """kv_hook(l, k, v) -> (k, v): replaces the new token's stored (rounded) entries of layer l;
+        self.pre[l] keeps that layer's k, v before the rounding."""
         wl, m = self.wl, self.m
+        self.pre = []
         H, Hq, Hkv, D = wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim
         G = Hq // Hkv
         grp = wl.group
@@ -75,8 +78,11 @@ class NumpyDecoder:
             if wl.qk_norm:
                 q, k = f32(rmsnorm(q, P["g_q"], wl.eps)), f32(rmsnorm(k, P["g_k"], wl.eps))
             q, k = f32(rope(q, pos, wl.rope_base)), f32(rope(k, pos, wl.rope_base))
+            self.pre.append((k.copy(), v.copy()))
             if wl.kv_fmt == "bf16":
                 k, v = bf16_round(k), bf16_round(v)
+            if kv_hook is not None:
+                k, v = kv_hook(l, k, v)
             assert len(self.K[l]) == pos
             self.K[l].append(k); self.V[l].append(v)
             Kt = np.stack(self.K[l]).astype(np.float64)   # [T][Hkv][D]

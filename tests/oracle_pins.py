@@ -563,6 +563,48 @@ def check_decode_against_numpy(steps: int = 3):
             tok = b["token"]
 
 
+def check_decode_kv_pre_and_forced_codes():
+    """The step's exposure of the new token's cache entries, against the independent numpy
+    decoder: kv_pre equals numpy's fp32 k, v before the bf16 rounding; forcing every layer's own
+    codes reproduces the plain step bit for bit; forcing a code one bf16 step away stores exactly
+    that code, and the step then equals numpy's step with the same cache entry replaced."""
+    wl = S.tiny("q4", shuffled_pages=True)
+    m = S.make_model(wl)
+    kv = S.make_kv(wl, 32)
+    pos, tok, L = wl.ctx, m["token"], wl.n_layers
+    pg, sl = int(kv["page_table"][pos // wl.page_size]), pos % wl.page_size
+    od = O.OracleDecoder(m, kv)
+    a = od.step(pos, tok, trace=True, kv_pre=True)
+    kl, vl = logical_kv(kv, wl, L)
+    nd = NumpyDecoder(m, kl, vl)
+    nd.step(pos, tok)
+    for l in range(L):
+        for i in range(2):
+            want = np.asarray(nd.pre[l][i], np.float64)
+            assert np.all(np.abs(a["kv_pre"][l, i] - want) <= 1e-5 * np.abs(want).max()), (l, i)
+    own = {l: (od.k[l][pg, :, sl, :].copy(), od.v[l][pg, :, sl, :].copy()) for l in range(L)}
+    b = O.OracleDecoder(m, kv).step(pos, tok, trace=True, kv_force=own)
+    assert np.array_equal(a["trace"].view(np.uint32), b["trace"].view(np.uint32))
+    assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+    moved_k = own[0][0].copy()
+    moved_k[1, 2] += 1   # the next bf16 code of the same sign
+    od3 = O.OracleDecoder(m, kv)
+    c = od3.step(pos, tok, trace=True, kv_force={0: (moved_k, own[0][1])})
+    assert np.array_equal(od3.k[0][pg, :, sl, :], moved_k)
+    assert np.array_equal(od3.v[0][pg, :, sl, :], own[0][1])
+
+    def hook(l, k, v):
+        if l == 0:
+            k = bf16_bits_to_f32(moved_k)
+        return k, v
+
+    nd3 = NumpyDecoder(m, *logical_kv(kv, wl, L))
+    r = nd3.step(pos, tok, kv_hook=hook)
+    scale = np.abs(r["trace"]).max(axis=1, keepdims=True)
+    assert np.all(np.abs(c["trace"] - r["trace"]) <= 1e-5 * scale)
+    assert not np.array_equal(c["trace"][1:], a["trace"][1:])   # the moved code changed the step
+
+
 def check_decode_batch_against_numpy():
     """Batched step: every running slot equals the independent numpy decoder of that sequence alone
     (its own block table into the shared pool, its own position and token); an idle slot is left
@@ -646,6 +688,7 @@ ALL_CHECKS = [
     check_rmsnorm_closed_forms, check_rope_invariants, check_rope_textbook_cases,
     check_swiglu_identities, check_attention_bruteforce, check_attention_special_cases,
     check_kv_layout_against_page_figures, check_workload_shapes_against_pages, check_argmax_ties,
-    check_decode_zero_weights_identity, check_decode_against_numpy, check_decode_batch_against_numpy,
+    check_decode_zero_weights_identity, check_decode_against_numpy, check_decode_kv_pre_and_forced_codes,
+    check_decode_batch_against_numpy,
     check_prefill_against_numpy,
 ]

@@ -1,10 +1,15 @@
-"""Decode-step benchmark: Qwen2.5-7B-shaped INT4 (groups of 64) model, paged bf16 KV of 4096
-tokens, batch 1, greedy, one hipGraph replay per token, on one MI355X.
+"""Decode-step benchmark, one MI355X.  Default workload: the Qwen2.5-7B-shaped INT4 (groups of
+64) model, paged bf16 KV of 4096 tokens, batch 1, greedy, one hipGraph replay per token;
+`--workload` selects any other decode workload (the Qwen2.5-1.5B and Qwen3-8B shapes with INT8
+weights, the 32K-context attention-stress case, or the single Qwen2-style layer, timed
+cache-resident and cold).
 
 Prints one JSON line.  `value` is decode throughput (tokens/s) over K timed graph replays with
-the inputs resident in HBM; `roofline` relates the algorithmic bytes of the dominant kernel to
-its launch duration measured with HIP events on its own stream; `cpu_baseline` times the CPU
-oracle on a bounded sample (whole decode steps) of the same workload.
+the inputs resident in HBM; `kernels` gives every kernel role's duration (HIP events after each
+launch of a few eager steps, on the launch stream), algorithmic bytes, GB/s and share of the
+step; `roofline` is the role with the largest share; `cpu_baseline` times the CPU oracle on a
+bounded sample (whole decode steps) of the same workload, and `oracle_token_check` compares its
+greedy tokens with the GPU's from the same state.
 """
 import argparse
 import hashlib
@@ -20,10 +25,12 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-# HBM traffic of the roofline kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs, scaled by
+METRIC = "decode ms/token + achieved HBM GB/s (% of peak), Qwen2.5-7B-shape INT4, 1 GPU"
+# HBM traffic of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs, scaled by
 # the same counters on a plain copy of known size; valid only for the kernel sources it was taken on
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemv_q4_traffic.json")
-KERNEL_SOURCES = ("quantized_gemv_gqa_amd/csrc/gemv.hip", "quantized_gemv_gqa_amd/csrc/qdec_device.h",
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic_qwen25_7b_q4.json")
+KERNEL_SOURCES = ("quantized_gemv_gqa_amd/csrc/gemv.hip", "quantized_gemv_gqa_amd/csrc/layer.hip",
+                  "quantized_gemv_gqa_amd/csrc/qdec_device.h", "quantized_gemv_gqa_amd/csrc/qdec_attention.h",
                   "quantized_gemv_gqa_amd/csrc/qdec_internal.h")
 
 
@@ -35,8 +42,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Bytes per launch from the committed counter record, or None if absent or stale."""
+def measured_traffic(role: str):
+    """HBM bytes per launch of a kernel role from the committed counter record, or None if absent
+    or taken on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -44,7 +52,7 @@ def measured_traffic():
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch", {}).get(role)
 
 
 def step_bytes(wl, T: int) -> int:
@@ -71,14 +79,6 @@ def step_bytes(wl, T: int) -> int:
     if wl.has_lm_head:
         total += wbytes(wl.vocab, H) + H * 4 + H * 2
     return total
-
-
-def dominant_kernel_bytes(wl) -> int:
-    """Packed gate/up GEMV of one layer (weights + scales): the largest per-layer kernel."""
-    N, K = 2 * wl.inter, wl.hidden
-    if wl.wfmt == "q4":
-        return N * K // 2 + N * (K // wl.group) * 2
-    return N * K + N * 4
 
 
 def gemv_ab(wl, reps: int = 40, replays: int = 5):
@@ -270,6 +270,152 @@ def prefill_bench(wl, T: int, reps: int, warmup: int):
             "gemm_flop": gemm_flop, "attn_flop": attn_flop, "ms_each": times, "gen_s": gen_s}
 
 
+def kernel_roles(wl, n_kernels: int, sampling: bool = False):
+    """Role of each kernel of one step, in launch order: the embedding, then per layer either
+    the fused attention launch + gate/up + down, or the five per-op launches, then the lm head
+    (+ the two sampling launches), or the position update of a model without one."""
+    L = wl.n_layers
+    tail = ["lm_head"] + (["sample", "sample"] if sampling else []) if wl.has_lm_head else ["finish"]
+    fused = 1 + 3 * L + len(tail)
+    per_op = 1 + 5 * L + len(tail)
+    if n_kernels == fused:
+        body = ["attn_layer", "gate_up", "down"] * L
+    elif n_kernels == per_op:
+        body = ["qkv", "attention", "o", "gate_up", "down"] * L
+    else:
+        raise RuntimeError("unexpected kernel count %d for %d layers" % (n_kernels, L))
+    return ["embed"] + body + tail
+
+
+def role_bytes(wl, T: int) -> dict:
+    """Algorithmic HBM bytes each kernel role moves at T attended keys (step_bytes split by kernel)."""
+    H, I, D = wl.hidden, wl.inter, wl.head_dim
+    qd, kvd = wl.n_heads * D, wl.n_kv_heads * D
+
+    def wbytes(N, K):
+        if wl.wfmt == "q4":
+            return N * K // 2 + N * (K // wl.group) * 2
+        return N * K + N * 4
+
+    kvb = 4 if wl.kv_fmt == "f32" else 2
+    qkv = wbytes(qd + 2 * kvd, H) + H * 4 + ((qd + 2 * kvd) * 4 if wl.qkv_bias else 0) + (2 * D * 4 if wl.qk_norm else 0)
+    att = 2 * kvd * kvb * T + 2 * kvd * kvb
+    o = wbytes(H, qd)
+    r = {"embed": H * 2 if wl.has_lm_head else 0, "qkv": qkv, "attention": att, "o": o, "attn_layer": qkv + att + o,
+         "gate_up": wbytes(2 * I, H) + H * 4, "down": wbytes(H, I), "finish": 0, "sample": 0}
+    if wl.has_lm_head:
+        r["lm_head"] = wbytes(wl.vocab, H) + H * 4
+    return r
+
+
+ROLE_NAMES = {"attn_layer": "fused attention launch (qkv GEMV + RoPE/KV append + split attention + merge + o GEMV)",
+              "gate_up": "gate/up GEMV + SwiGLU", "down": "down GEMV + residual", "lm_head": "lm head GEMV + greedy argmax",
+              "embed": "embedding row", "qkv": "qkv GEMV", "attention": "split attention + merge", "o": "o GEMV",
+              "finish": "position update", "sample": "sampling"}
+
+
+def per_kernel_roofline(wl, st, stream, reps: int):
+    """Per-kernel durations of `reps` eager steps (a HIP event after every launch, on the launch
+    stream), grouped by role: average microseconds, algorithmic bytes and GB/s of each role, and
+    its share of the summed kernel time."""
+    times = []
+    T0 = int(st.pos.item()) + 1
+    for _ in range(reps):
+        times.append(st.kernel_times(stream=stream))
+    n = len(times[0])
+    roles = kernel_roles(wl, n, sampling=False)
+    rb = role_bytes(wl, T0 + reps // 2)
+    acc = {}
+    for t in times:
+        for role, us in zip(roles, t):
+            a = acc.setdefault(role, [0.0, 0])
+            a[0] += us
+            a[1] += 1
+    total = sum(sum(t) for t in times) / reps
+    out = []
+    for role, (us_sum, cnt) in acc.items():
+        per_step = us_sum / reps
+        avg = us_sum / cnt
+        b = rb.get(role, 0)
+        out.append({"role": role, "kernel": ROLE_NAMES.get(role, role), "launches_per_step": cnt // reps,
+                    "us_per_launch": avg, "bytes_per_launch": b,
+                    "gbps": (b / (avg * 1e-6) / 1e9) if b else None,
+                    "frac_of_peak": (b / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS) if b else None,
+                    "share_of_step": per_step / total})
+    out.sort(key=lambda r: -r["share_of_step"])
+    return out, total
+
+
+def stream_read_gbps(dev, stream, gib: float = 2.0, reps: int = 5):
+    """Plain streaming read of `gib` GiB (qdec_stream_read), HIP events around `reps` reads."""
+    import quantized_gemv_gqa_amd as q
+    buf = torch.empty(int(gib * (1 << 30)) // 16 * 4, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        q.stream_read(buf, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            q.stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    nbytes = buf.numel() * 4
+    del buf
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def describe(wl) -> dict:
+    return {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": [wl.n_heads, wl.n_kv_heads],
+            "head_dim": wl.head_dim, "inter": wl.inter, "vocab": wl.vocab,
+            "weights": ("int4 g%d zp8 fp16 scales" % wl.group) if wl.wfmt == "q4" else "int8 per-row fp32 scales",
+            "kv": "%s, 16-token pages%s" % ("paged bf16" if wl.kv_fmt == "bf16" else "fp32",
+                                            ", shuffled" if wl.shuffled_pages else ", identity page table"),
+            "context": wl.ctx, "batch": 1}
+
+
+def layer_bench(wl, K: int, W: int, copies: int):
+    """The single-layer workload (no embedding or lm head): its 15 MB of weights fit in the 256 MB
+    last-level cache, so it is timed both as is (cache-resident) and cold, over `copies` rotating
+    copies of the layer (one step handle and graph each, replayed round-robin)."""
+    import quantized_gemv_gqa_amd as q
+    import synth
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    model = synth.make_model(wl)
+    kv = synth.make_kv(wl, wl.ctx + W + K + 16)
+    stream = torch.cuda.Stream()
+    res = {}
+    for label, n in (("cache_resident", 1), ("cold", copies)):
+        steps = []
+        for _ in range(n):
+            dm = q.upload_model(model, dev)
+            dk = q.upload_kv(kv, wl.kv_fmt, dev)
+            steps.append(q.DecodeStep(dm, dk, pos0=wl.ctx, h0=model["h0"], device=dev))
+        with torch.cuda.stream(stream):
+            for i in range(max(W, n)):
+                steps[i % n].step(q.STEP_GRAPH)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                steps[i % n].step(q.STEP_GRAPH)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        err = max(st.read_error() for st in steps)
+        assert err == 0, "step error word %d" % err
+        b = step_bytes(wl, wl.ctx + 1)
+        res[label] = {"copies": n, "us_per_step": us, "gbps": b / (us * 1e-6) / 1e9,
+                      "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del steps
+        torch.cuda.empty_cache()
+    return {"metric": METRIC.replace("Qwen2.5-7B-shape INT4", "single Qwen2-style layer"),
+            "value": res["cold"]["gbps"], "unit": "GB/s", "steps": K, "warmup": W, "higher_is_better": True,
+            "dtype": "f32", "data": "synthetic", "config": describe(wl), "step_bytes": step_bytes(wl, wl.ctx + 1),
+            "layer_step": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +424,9 @@ def main():
     ap.add_argument("--workload", default="qwen2.5-7b-q4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager-steps", type=int, default=8, help="eager (kernel-by-kernel) steps timed after the graph")
+    ap.add_argument("--kernel-steps", type=int, default=6, help="eager steps with an event after every kernel")
+    ap.add_argument("--cold-copies", type=int, default=48, help="single-layer workload: rotating weight copies")
     ap.add_argument("--calib-copy-mib", type=int, default=512,
                     help="size of one plain device copy run after the timed region (counter calibration)")
     ap.add_argument("--sampling", default="",
@@ -308,8 +457,12 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps({"workload": wl.name, "weights": wl.wfmt, "group": wl.group, "gemv_ab": gemv_ab(wl)}))
         return
-    K, W = args.steps, args.warmup
-    max_ctx = wl.ctx + W + K + 16
+    if not wl.has_lm_head:
+        print(json.dumps(layer_bench(wl, args.steps, args.warmup, args.cold_copies)))
+        return
+    K, W, E, KT = args.steps, args.warmup, args.eager_steps, args.kernel_steps
+    n_all = W + K + E + KT
+    max_ctx = wl.ctx + n_all + 16
     t0 = time.time()
     model = synth.make_model(wl)
     kv = synth.make_kv(wl, max_ctx)
@@ -321,7 +474,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    st = q.DecodeStep(dm, dk, pos0=wl.ctx, token0=model.get("token", 0), log_len=W + K, device=dev)
+    st = q.DecodeStep(dm, dk, pos0=wl.ctx, token0=model.get("token", 0), log_len=n_all, device=dev)
     sampling = None
     if args.sampling:
         T_s, k_s, p_s = args.sampling.split(",")
@@ -340,36 +493,35 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / K
+    err_word = st.read_error()
+    assert err_word == 0, "the timed steps set the step error word (%d)" % err_word
     pos_end = int(st.pos.item())
     assert pos_end == wl.ctx + W + K, pos_end
-    tokens = st.token_log.cpu().numpy()
     T0 = wl.ctx + W + 1
     bytes_timed = sum(step_bytes(wl, T0 + i) for i in range(K))
     gbps_step = bytes_timed / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
-    # dominant kernel: the gate/up GEMV of a layer, one HIP event pair around each launch on the
-    # stream it runs on; the layer rotates so the weights come from HBM, not from cache
-    xin = torch.randn(wl.hidden, device=dev)
-    y_gu = torch.empty(2 * wl.inter, device=dev)
-    gu_ws = q.gemv_workspace(wl.wfmt, 2 * wl.inter, wl.hidden, dev)
-    reps = 56
-    layers = dm["layers"]
+    # eager submission (every kernel launched from the host) for comparison with graph replay
     with torch.cuda.stream(stream):
-        def gu(i):
-            d = layers[i % len(layers)]
-            q.gemv(wl.wfmt, d["w_gu"], d["s_gu"], xin, 2 * wl.inter, y=y_gu, workspace=gu_ws, group=wl.group)
-
-        for i in range(5):
-            gu(i)
-        # back-to-back launches between one event pair: the per-launch average then matches the
-        # kernel-trace duration (which runs from one dispatch's start to its end)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for i in range(reps):
-            gu(i)
-        ev1.record(stream)
+        st.step(q.STEP_EAGER)
         torch.cuda.synchronize()
-    us_gu = ev0.elapsed_time(ev1) * 1e3 / reps
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        for _ in range(E - 1):
+            st.step(q.STEP_EAGER)
+        e3.record(stream)
+        torch.cuda.synchronize()
+    ms_eager = e2.elapsed_time(e3) / max(1, E - 1)
+
+    # per-kernel durations (HIP events on the launch stream), grouped by role
+    kernels = []
+    kernel_sum_us = None
+    if sampling is None and KT > 0:
+        kernels, kernel_sum_us = per_kernel_roofline(wl, st, stream, KT)
+    err_word = st.read_error()
+    assert err_word == 0, "the eager steps set the step error word (%d)" % err_word
+
+    stream_gbps = stream_read_gbps(dev, stream)
     # one plain copy of known size (read + write of calib-copy-mib MiB), the reference the HBM
     # byte counters are scaled by when this command runs under rocprofv3 --pmc
     if args.calib_copy_mib > 0:
@@ -379,11 +531,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    gu_bytes = dominant_kernel_bytes(wl)
-    gu_gbps = gu_bytes / (us_gu * 1e-6) / 1e9
+    tokens = st.token_log.cpu().numpy()
 
+    cfg = describe(wl)
+    cfg.update({"submission": "hipGraph replay per token", "kernels_per_step": st.kernel_count,
+                "num_splits": st.cfg.num_splits, "next_token": sampling or "greedy"})
     out = {
-        "metric": "decode ms/token + achieved HBM GB/s (% of peak), Qwen2.5-7B-shape INT4, 1 GPU",
+        "metric": METRIC if wl.name == "qwen2.5-7b-q4" else METRIC.replace("Qwen2.5-7B-shape INT4", wl.name),
         "value": K / (e0.elapsed_time(e1) * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -395,21 +549,26 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": wl.n_layers, "hidden": wl.hidden, "heads": [wl.n_heads, wl.n_kv_heads],
-                   "head_dim": wl.head_dim, "inter": wl.inter, "vocab": wl.vocab, "weights": "int4 g%d zp8 fp16 scales" % wl.group,
-                   "kv": "paged bf16, 16-token pages, shuffled", "context": wl.ctx, "batch": 1,
-                   "submission": "hipGraph replay per token", "kernels_per_step": st.kernel_count,
-                   "num_splits": st.cfg.num_splits, "next_token": sampling or "greedy"},
+        "config": cfg,
         "step_bytes": bytes_timed / K,
         "step_gbps": gbps_step,
         "step_frac_of_peak": gbps_step / HBM_PEAK_GBPS,
+        "stream_read_gbps": stream_gbps,
+        "step_frac_of_stream_read": gbps_step / stream_gbps,
+        "eager_ms_per_step": ms_eager,
+        "error_word": 0,
         "wall_s_timed": wall,
-        "roofline": {"bound": "hbm", "kernel": "gate/up GEMV (INT4, %dx%d)" % (2 * wl.inter, wl.hidden),
-                     "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gu_gbps / HBM_PEAK_GBPS,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": us_gu, "traffic": measured_traffic(),
-                     "kernel_source_hash": kernel_source_hash()},
-        "tokens_head": [int(t) for t in tokens[:8]],
     }
+    if kernels:
+        top = kernels[0]
+        out["roofline"] = {"bound": "hbm", "kernel": top["kernel"], "achieved": top["gbps"], "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": top["frac_of_peak"], "traffic": measured_traffic(top["role"]),
+                           "bytes_per_launch": top["bytes_per_launch"], "us_per_launch": top["us_per_launch"],
+                           "share_of_step": top["share_of_step"], "kernel_source_hash": kernel_source_hash(),
+                           "timing": "HIP events after every launch of %d eager steps, on the launch stream" % KT}
+        out["kernels"] = kernels
+        out["kernel_sum_ms_per_step"] = kernel_sum_us / 1e3
+    out["tokens_head"] = [int(t) for t in tokens[:8]]
 
     if not args.no_cpu_baseline:
         import oracle
@@ -417,14 +576,26 @@ def main():
         od = oracle.OracleDecoder(model, kv, nthreads=nthreads)
         tok = model.get("token", 0)
         n, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and n < 64:
+        orc_tokens, margins = [], []
+        while t_cpu < args.cpu_seconds and n < min(64, W + K):
             c0 = time.perf_counter()
             r = od.step(wl.ctx + n, tok, logits=True)
             t_cpu += time.perf_counter() - c0
             tok = r["token"]
+            orc_tokens.append(int(tok))
+            srt = np.sort(r["logits"].astype(np.float64))
+            margins.append(float(srt[-1] - srt[-2]))
             n += 1
         out["cpu_baseline"] = {"value": n / t_cpu, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
                                "sample": "%d whole decode steps of the same model from position %d (greedy)" % (n, wl.ctx)}
+        if sampling is None:
+            gpu_t = [int(t) for t in tokens[:n]]
+            same = sum(int(a == b) for a, b in zip(gpu_t, orc_tokens))
+            first_diff = next((i for i, (a, b) in enumerate(zip(gpu_t, orc_tokens)) if a != b), None)
+            out["oracle_token_check"] = {"steps": n, "identical": same, "first_difference": first_diff,
+                                         "min_oracle_margin": min(margins),
+                                         "note": "GPU greedy tokens of the warm-up and timed steps against the oracle's "
+                                                 "decode of the same model from the same state"}
     out["gen_s"] = gen_s
     print(json.dumps(out))
 

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(_ROOT, "include")
 QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EHIP, QDEC_ESTATE = 0, -1, -2, -3, -4
 W_Q8, W_Q4 = 1, 2
 KV_F32, KV_BF16 = 1, 2
-STEP_EAGER, STEP_GRAPH, STEP_FUSED = 0, 1, 2
+STEP_EAGER, STEP_GRAPH = 0, 1
 STEP_PER_OP = 4  # flag for EAGER / GRAPH: one launch per operation instead of two per layer
 PAGE = 16
 TILE = 64
@@ -150,6 +150,7 @@ def lib():
         L.qdec_rmsnorm_rope.argtypes = [_P, _P, _P, _I, _I, F, F, _P, _P]; L.qdec_rmsnorm_rope.restype = S
         L.qdec_swiglu.argtypes = [_P, _P, _P, _I, _P]; L.qdec_swiglu.restype = S
         L.qdec_argmax.argtypes = [_P, _I, _P, _P]; L.qdec_argmax.restype = S
+        L.qdec_stream_read.argtypes = [_P, Z, _P, _P]; L.qdec_stream_read.restype = S
         L.qdec_attn_workspace_bytes.argtypes = [_I, _I, _I]; L.qdec_attn_workspace_bytes.restype = Z
         L.qdec_attn_decode_paged.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _P, _I, _I, _I, F,
                                              _I, _P, Z, _P, _P]
@@ -162,12 +163,11 @@ def lib():
         L.qdec_decode_step.argtypes = [_P, _I, _P]; L.qdec_decode_step.restype = S
         L.qdec_step_set_sampling.argtypes = [_P, F, _I, F, ctypes.c_uint64]; L.qdec_step_set_sampling.restype = S
         L.qdec_step_kernel_count.argtypes = [_P]; L.qdec_step_kernel_count.restype = _I
+        L.qdec_step_kernel_times.argtypes = [_P, _I, _P, _I, _P]; L.qdec_step_kernel_times.restype = _I
+        L.qdec_step_layer_blocks.argtypes = [_P]; L.qdec_step_layer_blocks.restype = _I
+        L.qdec_step_layer_timeline.argtypes = [_P, _P]; L.qdec_step_layer_timeline.restype = S
         L.qdec_step_destroy.argtypes = [_P]; L.qdec_step_destroy.restype = None
-        L.qdec_step_fused_supported.argtypes = [_P]; L.qdec_step_fused_supported.restype = _I
         L.qdec_step_read_error.argtypes = [_P, ctypes.POINTER(_I)]; L.qdec_step_read_error.restype = S
-        L.qdec_step_phase_times.argtypes = [_P, _P]; L.qdec_step_phase_times.restype = S
-        L.qdec_step_wave_times.argtypes = [_P, _P]; L.qdec_step_wave_times.restype = S
-        L.qdec_step_fused_waves.argtypes = [_P]; L.qdec_step_fused_waves.restype = _I
         _lib = L
     return _lib
 
@@ -179,10 +179,9 @@ EXPORTED = [
     "qdec_gemm_workspace_bytes", "qdec_gemm_q8", "qdec_gemm_q4", "qdec_batch_workspace_bytes", "qdec_batch_create",
     "qdec_batch_decode_step", "qdec_batch_kernel_count", "qdec_batch_destroy", "qdec_prefill_workspace_bytes",
     "qdec_prefill", "qdec_gemm_mfma",
-    "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_attn_workspace_bytes",
+    "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_stream_read", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
-    "qdec_step_kernel_count", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_fused_supported", "qdec_step_read_error",
-    "qdec_step_phase_times", "qdec_step_wave_times", "qdec_step_fused_waves",
+    "qdec_step_kernel_count", "qdec_step_kernel_times", "qdec_step_layer_blocks", "qdec_step_layer_timeline", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_read_error",
 ]
 
 
@@ -353,6 +352,15 @@ def argmax(logits, stream=None):
     tok = torch.empty(1, dtype=torch.int32, device=logits.device)
     _check(lib().qdec_argmax(_ptr(logits), logits.numel(), _ptr(tok), _stream(stream)), "qdec_argmax")
     return tok
+
+
+def stream_read(src, sink=None, stream=None):
+    """Bandwidth reference: read every byte of the device tensor `src` once (qdec_stream_read)."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    _check(lib().qdec_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "qdec_stream_read")
+    return sink
 
 
 def attn_workspace(n_heads: int, head_dim: int, num_splits: int, device="cuda"):
@@ -627,26 +635,27 @@ class DecodeStep:
     def kernel_count(self) -> int:
         return lib().qdec_step_kernel_count(self.handle)
 
+    def kernel_times(self, per_op: bool = False, stream=None):
+        """One eager step with a HIP event after every kernel: the list of kernel durations in
+        microseconds, in launch order (the step advances like any other)."""
+        import numpy as np
+        buf = np.zeros(8 + 8 * self.n_layers, np.float32)
+        n = lib().qdec_step_kernel_times(self.handle, STEP_EAGER | (STEP_PER_OP if per_op else 0),
+                                         buf.ctypes.data_as(_P), buf.size, _stream(stream))
+        if n < 0:
+            raise QdecError(n, "qdec_step_kernel_times")
+        return buf[:n].tolist()
+
     @property
-    def fused_supported(self) -> bool:
-        return bool(lib().qdec_step_fused_supported(self.handle))
+    def layer_blocks(self) -> int:
+        """Workgroups of the fused attention launch (0: the step has none)."""
+        return lib().qdec_step_layer_blocks(self.handle)
 
-    def phase_times(self, ts=None):
-        """Record per-phase completion times of fused steps into `ts` (int64 device tensor of
-        2 + 5 * n_layers entries, zeroed by the caller before each step, 100 MHz ticks); None stops
-        recording."""
-        _check(lib().qdec_step_phase_times(self.handle, _ptr(ts)), "qdec_step_phase_times")
-        self._ts = ts
-
-    @property
-    def fused_waves(self) -> int:
-        return lib().qdec_step_fused_waves(self.handle)
-
-    def wave_times(self, ts=None):
-        """Record per-wave marks of fused steps into `ts` (int32 device tensor of
-        (5 * n_layers + 1) * fused_waves * 4 entries); None stops recording."""
-        _check(lib().qdec_step_wave_times(self.handle, _ptr(ts)), "qdec_step_wave_times")
-        self._wts = ts
+    def layer_timeline(self, ts=None):
+        """Record per-wave clock marks of the fused attention launches of later steps into `ts`
+        (int64 device tensor [n_layers][blocks][8][16], zeroed by the caller); None stops."""
+        _check(lib().qdec_step_layer_timeline(self.handle, _ptr(ts)), "qdec_step_layer_timeline")
+        self._tl = ts
 
     def read_error(self) -> int:
         """The step's device error flag (a bounded wait gave up), cleared after reading."""

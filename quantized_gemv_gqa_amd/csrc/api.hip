@@ -334,6 +334,14 @@ qdec_status qdec_swiglu(const float *gate, const float *up, float *out, int n, v
   return QDEC_OK;
 }
 
+qdec_status qdec_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  QDEC_REQUIRE(src && sink, QDEC_EINVAL, "qdec_stream_read: null pointer");
+  QDEC_REQUIRE(bytes >= 16 && bytes % 16 == 0 && aligned(src, 16), QDEC_EINVAL,
+               "qdec_stream_read: bytes must be a positive multiple of 16 and src 16-byte aligned");
+  if (launch_stream_read(src, bytes, sink, (hipStream_t)stream) != hipSuccess) return check_launch("qdec_stream_read");
+  return QDEC_OK;
+}
+
 qdec_status qdec_argmax(const float *logits, int n, int32_t *token, void *stream) {
   QDEC_REQUIRE(logits && token, QDEC_EINVAL, "qdec_argmax: null pointer");
   QDEC_REQUIRE(n >= 1, QDEC_EINVAL, "qdec_argmax: n must be >= 1 (n=%d)", n);
@@ -373,6 +381,8 @@ qdec_status qdec_attn_decode_paged(const float *q, const float *k_new, const flo
   QDEC_REQUIRE(n_kv_heads <= (int)(kAttnCounterBytes / 128), QDEC_EUNSUPPORTED, "%s: at most %d KV heads", nm,
                (int)(kAttnCounterBytes / 128));
   QDEC_REQUIRE(n_pages >= 1, QDEC_EINVAL, "%s: n_pages must be >= 1", nm);
+  QDEC_REQUIRE(kv_pool_fits(n_pages, n_kv_heads, head_dim, kv_fmt), QDEC_EUNSUPPORTED,
+               "%s: a KV pool of %d pages x %d heads x 16 x %d must stay below 4 GiB", nm, n_pages, n_kv_heads, head_dim);
   QDEC_REQUIRE(std::isfinite(sm_scale), QDEC_EINVAL, "%s: sm_scale must be finite", nm);
   QDEC_REQUIRE(workspace_bytes >= attn_workspace_bytes(n_heads, head_dim, num_splits), QDEC_EINVAL,
                "%s: workspace too small", nm);

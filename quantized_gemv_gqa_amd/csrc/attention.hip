@@ -73,6 +73,7 @@ __global__ void kv_append(const float *__restrict__ k, const float *__restrict__
                           void *v_pool, int kv_fmt, const int32_t *__restrict__ page_table,
                           int n_pages, const int32_t *__restrict__ pos, int Hkv, int D) {
   const int t = *pos;
+  if (t < 0 || (t >> 4) >= n_pages) return;
   const int phys = page_table[t >> 4];
   if (phys < 0 || phys >= n_pages) return;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < Hkv * D; i += gridDim.x * blockDim.x) {

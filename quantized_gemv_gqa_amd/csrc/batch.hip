@@ -186,6 +186,8 @@ qdec_status validate_batch(const qdec_config *c, int B) {
                "qdec_batch: unknown kv format %d", c->kv_fmt);
   QDEC_REQUIRE(c->page_size == QDEC_PAGE_SIZE && c->n_pages >= 1, QDEC_EUNSUPPORTED,
                "qdec_batch: page_size must be 16 and n_pages >= 1");
+  QDEC_REQUIRE(kv_pool_fits(c->n_pages, c->n_kv_heads, c->head_dim, c->kv_fmt), QDEC_EUNSUPPORTED,
+               "qdec_batch: a layer's KV pool (%d pages) must stay below 4 GiB", c->n_pages);
   QDEC_REQUIRE(c->num_splits >= 1 && c->num_splits <= kMaxMergeSplits, QDEC_EINVAL, "qdec_batch: num_splits in [1, %d]",
                kMaxMergeSplits);
   QDEC_REQUIRE(c->n_kv_heads <= (int)(kAttnCounterBytes / 128), QDEC_EUNSUPPORTED, "qdec_batch: too many KV heads");

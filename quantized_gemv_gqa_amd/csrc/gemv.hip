@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(256) gemv_tile64(const GemvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * 4 + wave;
   if (unit >= ((a.N + kTile - 1) / kTile) * a.ks) return;  // whole wave
-  gemv_unit<FMT, NORM, EPI>(a, unit, stage_all[wave], lane);
+  gemv_unit<FMT, NORM, EPI, kSyncNone>(a, unit, stage_all[wave], lane);
 }
 
 template <int FMT>

@@ -1,33 +1,34 @@
-// Fused attention kernel: the attention half of a decoder layer (qkv GEMV, split attention, o
-// GEMV) in one launch instead of three.
+// Fused attention kernel: the attention half of a decoder layer (qkv GEMV, split attention with
+// its merge, o GEMV) in one launch.
 //
-// What they compute is exactly what the per-op kernels compute (the same device code runs); what
-// changes is when.  Launched one after another, each piece pays its own ramp-up and drain, which
-// for the small pieces (the qkv and o GEMVs, attention) is most of their time.  Here pieces with
-// a narrow data dependency share one launch, as workgroup roles ordered by block index:
+// What it computes is exactly what the per-op kernels compute (the same device code runs, with
+// the same split of the work, so results are equal bit for bit); what changes is when.
 //
-//   [qkv GEMV units] [attention units (KV head j, split s)] [o GEMV units]
-//
-// and a consumer waits only for the producers of its own inputs:
-//   * attention unit (j, s) requests its first KV pages, then waits until the 2G + 4 qkv tiles of
-//     KV head j (its G q heads, its k and v) are stored, counted per head;
-//   * an o GEMV unit requests its first weights, then waits for the attention outputs of the KV
-//     heads whose query heads cover its k-range (a flag per KV head, set by the split merge).
-// The MLP half stays two plain launches: the RMSNorm before gate/up needs the whole o output, and
-// all gate/up tiles finish at about the same time, so a down GEMV sharing their launch could
-// only wait (measured: one launch for both was slower than two).  The residual stream alternates
-// between two buffers (hA, read by the qkv GEMV and as o's residual, written by down; hB, written
-// by o and read by gate/up and down), so no unit overwrites a vector that a unit of the same
-// launch may still read.
-//
-// Ordering and progress: workgroups are dispatched in block-index order, so every producer a
-// unit waits for was dispatched before it; producers never wait.  Waits are bounded polls: a step
-// whose producers do not arrive in time sets the step's error word instead of hanging.
+// One workgroup of 8 waves per compute unit, and every workgroup takes part in every phase:
+//   wave w of workgroup b holds qkv GEMV unit 8 b + w, o GEMV unit 8 (nblk - 1 - b) + w, and the
+//   workgroup as a whole holds attention unit (KV head b / splits, split b % splits) if b is
+//   below Hkv * splits.
+// Before it waits for anything, a workgroup requests all of its HBM bytes: its qkv weights (into
+// registers, computed first), its first KV page (registers) and its o weights, which are copied
+// straight from HBM into an LDS stash and need no registers while the attention runs.  So the
+// whole launch's 24 MB (at the Qwen2.5-7B shape) stream at once instead of phase by phase, and
+// what remains are the hand-offs:
+//   * attention unit (j, s) waits until the 2G + 4 qkv tiles of KV head j (its G q heads, its k
+//     and v) are stored, counted per head;
+//   * an o GEMV unit waits for the attention outputs of the KV heads whose query heads cover its
+//     k-range (a flag per KV head, set by the split merge).
+// Producers never wait for consumers, and the grid is one workgroup per compute unit of a
+// kernel that fits once per unit, so all workgroups are resident together and every wait is
+// for a workgroup that is running.  Waits are bounded polls: a step whose producers do not
+// arrive in time sets the step's error word instead of hanging.
 //
 // Flags and counters are monotonic: the step number e (advanced by the embedding kernel at the
 // start of each step) is the target, so nothing has to be cleared between steps.  Data crossing
 // workgroups inside a launch uses device-coherent stores and loads (sc1), and a producer's
-// counter moves only after its stores are acknowledged.
+// counter moves only after its stores are acknowledged.  The residual stream alternates between
+// two buffers (hA, read by the qkv GEMV and as o's residual, written by down; hB, written by o
+// and read by gate/up and down), so no unit overwrites a vector that a unit of the same launch
+// may still read.
 #include <hip/hip_runtime.h>
 
 #include "qdec_attention.h"
@@ -50,36 +51,58 @@ __global__ void __launch_bounds__(attn::kAttnThreads) attn_layer_k(const LayerAr
     attn::AttnSmem<128, G, true> at;
   };
   __shared__ Smem sm;
+  __shared__ u32x4 stash[kAttnLayerWaves][kStashRuns * kTile];  // o weights, 8 KiB per wave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b = blockIdx.x;
-  if (b < a.nb_qkv) {
-    const int unit = b * kAttnLayerWaves + wave;
-    if (unit < gemv_units(a.qkv)) gemv_unit<FMT, true, EPI_STORE, kSyncProducer>(a.qkv, unit, sm.st[wave], lane);
-    return;
-  }
-  b -= a.nb_qkv;
-  const int natt = a.at.Hkv * a.at.splits;
-  if (b < natt) {
-    attn::attn_unit<128, G, KVF, true, true>(a.at, b / a.at.splits, b % a.at.splits, sm.at);
-    return;
-  }
-  b -= natt;
-  const int unit = b * kAttnLayerWaves + wave;
-  if (unit < gemv_units(a.o)) gemv_unit<FMT, false, EPI_STORE, kSyncConsumer>(a.o, unit, sm.st[wave], lane);
+  const int b = blockIdx.x;
+  const int uq = b * kAttnLayerWaves + wave;
+  const int uo = (a.nblk - 1 - b) * kAttnLayerWaves + wave;
+  const bool q_role = uq < gemv_units(a.qkv);
+  const bool o_role = uo < gemv_units(a.o);
+  const bool at_role = b < a.at.Hkv * a.at.splits;  // the same for the whole workgroup
+  const int j = b / a.at.splits, s = b - j * a.at.splits;
+
+  GemvUnit<FMT, true, EPI_STORE, kSyncProducer> gq;
+  attn::AttnUnit<128, G, KVF, true, true> at;
+  GemvUnit<FMT, false, EPI_STORE, kSyncConsumer, true> go;
+  // optional timeline: per wave 16 marks (clock at entry, loads issued, qkv computed / combined /
+  // stored, attention wait done / pages done / published / merged, o wait done / computed /
+  // combined / stored)
+  unsigned long long *rec = a.timeline ? a.timeline + ((size_t)b * kAttnLayerWaves + wave) * 16 : nullptr;
+  mark(rec, 0);
+  if (q_role) gq.start(a.qkv, uq, lane);
+  if (at_role) at.start(a.at, j, s);
+  if (o_role) go.start(a.o, uo, lane, stash[wave]);
+  mark(rec, 1);
+  if (q_role) gq.finish(a.qkv, sm.st[wave], lane, nullptr, rec ? rec + 2 : nullptr);
+  mark(rec, 5);
+  // (the attention's first LDS write follows a workgroup barrier, so every wave is past its
+  // qkv unit's use of the union by then)
+  if (at_role) at.finish(a.at, j, s, sm.at, rec ? rec + 6 : nullptr);
+  if (o_role) go.finish(a.o, sm.st[wave], lane, stash[wave], rec ? rec + 10 : nullptr);
+  mark(rec, 13);
+}
+
+template <int FMT, int G, int KVF>
+const void *kernel_ptr() {
+  return reinterpret_cast<const void *>(&attn_layer_k<FMT, G, KVF>);
 }
 
 template <int FMT, int KVF>
-hipError_t launch_attn_g(const LayerArgs &a, int G, hipStream_t st) {
-  const int blocks = a.nb_qkv + a.at.Hkv * a.at.splits + a.nb_o;
+const void *kernel_g(int G) {
   switch (G) {
-    case 4: hipLaunchKernelGGL((attn_layer_k<FMT, 4, KVF>), dim3(blocks), dim3(attn::kAttnThreads), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((attn_layer_k<FMT, 6, KVF>), dim3(blocks), dim3(attn::kAttnThreads), 0, st, a); break;
-    case 7: hipLaunchKernelGGL((attn_layer_k<FMT, 7, KVF>), dim3(blocks), dim3(attn::kAttnThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((attn_layer_k<FMT, 8, KVF>), dim3(blocks), dim3(attn::kAttnThreads), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+    case 4: return kernel_ptr<FMT, 4, KVF>();
+    case 6: return kernel_ptr<FMT, 6, KVF>();
+    case 7: return kernel_ptr<FMT, 7, KVF>();
+    case 8: return kernel_ptr<FMT, 8, KVF>();
+    default: return nullptr;
   }
-  return hipGetLastError();
+}
+
+const void *layer_kernel(int wfmt, int kv_fmt, int G) {
+  if (wfmt == QDEC_W_Q4_G_ZP8)
+    return kv_fmt == QDEC_KV_BF16 ? kernel_g<QDEC_W_Q4_G_ZP8, QDEC_KV_BF16>(G) : kernel_g<QDEC_W_Q4_G_ZP8, QDEC_KV_F32>(G);
+  return kv_fmt == QDEC_KV_BF16 ? kernel_g<QDEC_W_Q8_ROW, QDEC_KV_BF16>(G) : kernel_g<QDEC_W_Q8_ROW, QDEC_KV_F32>(G);
 }
 
 }  // namespace
@@ -88,13 +111,20 @@ bool layer_fusion_supported(int G, int D) { return D == 128 && (G == 4 || G == 6
 
 int attn_layer_waves() { return kAttnLayerWaves; }
 
+int attn_layer_stash_runs() { return kStashRuns; }
+
+int attn_layer_blocks_per_cu(int wfmt, int kv_fmt, int G) {
+  const void *k = layer_kernel(wfmt, kv_fmt, G);
+  int nb = 0;
+  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, attn::kAttnThreads, 0) != hipSuccess) return 0;
+  return nb;
+}
+
 hipError_t launch_attn_layer(const LayerArgs &a, int wfmt, hipStream_t st) {
-  const int G = a.at.Hq / a.at.Hkv;
-  if (wfmt == QDEC_W_Q4_G_ZP8)
-    return a.at.kv_fmt == QDEC_KV_BF16 ? launch_attn_g<QDEC_W_Q4_G_ZP8, QDEC_KV_BF16>(a, G, st)
-                                       : launch_attn_g<QDEC_W_Q4_G_ZP8, QDEC_KV_F32>(a, G, st);
-  return a.at.kv_fmt == QDEC_KV_BF16 ? launch_attn_g<QDEC_W_Q8_ROW, QDEC_KV_BF16>(a, G, st)
-                                     : launch_attn_g<QDEC_W_Q8_ROW, QDEC_KV_F32>(a, G, st);
+  const void *k = layer_kernel(wfmt, a.at.kv_fmt, a.at.Hq / a.at.Hkv);
+  if (!k) return hipErrorInvalidValue;
+  void *args[] = {const_cast<LayerArgs *>(&a)};
+  return hipLaunchKernel(k, dim3(a.nblk), dim3(attn::kAttnThreads), args, 0, st);
 }
 
 }  // namespace qdec

@@ -165,12 +165,61 @@ struct AttnSmem {
 };
 
 // One (KV head j, split s) attention unit, run by a whole workgroup of kAttnThreads threads.
-// SYNC: the step-synchronised form of the fused layer kernel (AttnArgs: epoch, wait_cnt, done).
+// SYNC: the step-synchronised form of the fused layer kernels (AttnArgs: epoch, wait_cnt, done).
+// start() requests the wave's first KV page (nothing else happens before it); finish() does the
+// rest, so a kernel can issue other roles' loads, or compute, between the two.
 template <int D, int G, int KVF, bool ROPE, bool SYNC>
-__device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm) {
-  constexpr int DPL = D / 16;
-  constexpr int EB = Row<D, KVF>::EB;
-  constexpr int NW = kAttnWaves;
+struct AttnUnit {
+  static constexpr int DPL = D / 16;
+  static constexpr int EB = Row<D, KVF>::EB;
+  static constexpr int NW = kAttnWaves;
+  // (A second page buffer spilled registers of the 7-query-head unit and was slower at every
+  // context and batch measured.)
+  static constexpr int PF = 1;
+  int pos, T, P, nwt, gw, last_page;
+  __amdgpu_buffer_rsrc_t kr, vr;
+  Row<D, KVF> kp[PF][4], vp[PF][4];
+  bool have[PF];
+
+  __device__ __forceinline__ void start(const AttnArgs &a, int j, int s) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slot = lane >> 4;
+    const int part = lane & 15;
+    pos = *a.pos;
+    T = pos + 1;
+    P = max(0, min((T + 15) >> 4, a.n_pages));  // never index outside the page table
+    // pages are dealt round-robin over all NW * splits waves of the KV head: wave gw = NW s + wave
+    // takes pages gw, gw + nwt, gw + 2 nwt, ...
+    nwt = NW * a.splits;
+    gw = NW * s + wave;
+    last_page = ((T + 15) >> 4) - 1;
+    const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
+    kr = rsrc(a.k_pool, pool_bytes);
+    vr = rsrc(a.v_pool, pool_bytes);
+    const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int p = gw + nwt * i;
+      have[i] = false;
+      if (p < P) {
+        const int phys = a.page_table[p];
+        if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
+          have[i] = true;
+          const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+            const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
+            kp[i][sub].load(kr, off);
+            vp[i][sub].load(vr, off);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void finish(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm,
+                                        unsigned long long *rec = nullptr) {
   constexpr int C = G * D / 4;                                                // f32x4 columns
   constexpr int R = (kAttnThreads / C) < NW ? (kAttnThreads / C) : NW;        // merge threads per column
   auto &sm_m = sm.m;
@@ -184,41 +233,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane >> 4;
   const int part = lane & 15;
-  const int pos = *a.pos;
-  const int T = pos + 1;
-  const int P = min((T + 15) >> 4, a.n_pages);  // never index past the page table
-  // pages are dealt round-robin over all NW * splits waves of the KV head: wave gw = NW s + wave
-  // takes pages gw, gw + nwt, gw + 2 nwt, ...
-  const int nwt = NW * a.splits;
-  const int gw = NW * s + wave;
-  const int last_page = ((T + 15) >> 4) - 1;
-  const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
-  const __amdgpu_buffer_rsrc_t kr = rsrc(a.k_pool, pool_bytes), vr = rsrc(a.v_pool, pool_bytes);
-  const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
-
-  // the wave's first page is requested before anything else.  (A second page buffer spilled
-  // registers of the 7-query-head unit and was slower at every context and batch measured.)
-  constexpr int PF = 1;
-  Row<D, KVF> kp[PF][4], vp[PF][4];
-  bool have[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int p = gw + nwt * i;
-    have[i] = false;
-    if (p < P) {
-      const int phys = a.page_table[p];
-      if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
-        have[i] = true;
-        const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-          const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
-          kp[i][sub].load(kr, off);
-          vp[i][sub].load(vr, off);
-        }
-      }
-    }
-  }
+  const size_t head_stride = (size_t)16 * D;
 
   unsigned e = 0;
   if constexpr (SYNC) {
@@ -230,6 +245,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
     if (!last) return;  // (every thread of the workgroup leaves together)
     __syncthreads();    // everyone has read the flag before it is reused
   }
+  mark(rec, 0);
   float q[G][DPL];
   Row<D, KVF> knew, vnew;
   if constexpr (ROPE) {
@@ -271,14 +287,21 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
     norm_rope<D>(own, mate, part, a.g_k, a.eps, cs);
     knew.set(own);
     vnew.set(vv);
-    // split 0 appends them for later steps (every split uses the register copy for this token)
-    if (s == 0 && wave == 0 && slot == 0 && last_page < a.n_pages) {
-      const int phys = a.page_table[last_page];
-      if (phys >= 0 && phys < a.n_pages) {
-        const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (pos & 15)) * D + part * DPL;
-        knew.store(a.k_pool, e0);
-        vnew.store(a.v_pool, e0);
+    // split 0 appends them for later steps (every split uses the register copy for this token).
+    // A token without a cache slot (pos < 0, past the page table, or an unmapped entry) is not
+    // stored and sets the error word: its attention would leave the newest key out.
+    if (s == 0 && wave == 0 && slot == 0) {
+      bool stored = false;
+      if (pos >= 0 && last_page < a.n_pages) {
+        const int phys = a.page_table[last_page];
+        if (phys >= 0 && phys < a.n_pages) {
+          const size_t e0 = (((size_t)phys * a.Hkv + j) * 16 + (pos & 15)) * D + part * DPL;
+          knew.store(a.k_pool, e0);
+          vnew.store(a.v_pool, e0);
+          stored = true;
+        }
       }
+      if (!stored && part == 0 && a.err) __hip_atomic_store(a.err, kErrKvSlot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
 #pragma unroll
@@ -343,6 +366,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
       m[h] = mx;
     }
   };
+  mark(rec, 1);
   merge_pairs(pair16);
   merge_pairs(pair32);
   if (slot == 0) {
@@ -393,6 +417,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
     last = __hip_atomic_fetch_add(&a.counters[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            (unsigned)(a.splits - 1);
   __syncthreads();
+  mark(rec, 2);
   if (!last) return;
 
   // The last split block of KV head j merges all splits of its G query heads:
@@ -475,6 +500,15 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnS
     __syncthreads();
     if (t == 0) __hip_atomic_store(a.done + j, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  mark(rec, 3);
+  }
+};
+
+template <int D, int G, int KVF, bool ROPE, bool SYNC>
+__device__ __forceinline__ void attn_unit(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm) {
+  AttnUnit<D, G, KVF, ROPE, SYNC> u;
+  u.start(a, j, s);
+  u.finish(a, j, s, sm);
 }
 
 

@@ -1,5 +1,5 @@
-// Device-side building blocks shared by the per-op kernels and the persistent decode-step kernel
-// (gfx950, wave64).  Everything here runs inside one wave unless a comment says otherwise.
+// Device-side building blocks shared by the per-op kernels and the fused layer kernels (gfx950,
+// wave64).  Everything here runs inside one wave unless a comment says otherwise.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -22,6 +22,10 @@ constexpr int kAuxSc1 = 16;     // sc1: device-coherent access (bypasses non-coh
 constexpr unsigned kSpinLimit = 1u << 24;  // bounded waits: ~1 s of polling, then give up
 constexpr unsigned kLayerSpinLimit = 1u << 22;  // backed-off polls of the layer kernels: ~3.5 s
 constexpr float kNegBig = -1e30f;          // finite "minus infinity" for running maxima
+#ifndef QDEC_COMBINE_BURST
+#define QDEC_COMBINE_BURST 32
+#endif
+constexpr int kCombineBurst = QDEC_COMBINE_BURST;  // split-K partials a combining wave requests at once
 
 // ------------------------------------------------------------------------------ small helpers
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3: 32-bit data format).
@@ -172,7 +176,7 @@ __device__ inline bool poll_count(const unsigned *p, unsigned target, unsigned *
     ++spins;
     if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
     if (spins > kLayerSpinLimit) {
-      __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
   }
@@ -193,13 +197,19 @@ __device__ inline bool poll_flags(const unsigned *flags, int f0, int f1, unsigne
       ++spins;
       if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
       if (spins > kLayerSpinLimit) {
-        if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
       }
     }
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return true;
+}
+
+// Timeline marks (diagnostics): lane 0 stores the 100 MHz device clock at slot i of a wave's
+// record when the record pointer is set.
+__device__ __forceinline__ void mark(unsigned long long *rec, int i) {
+  if (rec && (threadIdx.x & 63) == 0) rec[i] = __builtin_amdgcn_s_memrealtime();
 }
 
 __device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
@@ -389,18 +399,21 @@ __device__ __forceinline__ bool splitk_combine(float &acc, float *part, unsigned
   if (prev != (unsigned)(ks - 1)) return false;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const __amdgpu_buffer_rsrc_t pr = rsrc(part + (size_t)tile * ks * kTile, (uint32_t)ks * kTile * 4);
+  // every partial of a burst is requested at once (one round trip per 32 splits; loads past the
+  // last split read zero), then added in split order
   acc = 0.f;
-  int i = 0;
-  for (; i + 8 <= ks; i += 8) {
-    float t[8];
+  for (int i = 0; i < ks; i += kCombineBurst) {
+    float t[kCombineBurst];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      t[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, (i + j) * kTile * 4, kAuxSc1));
+    for (int j = 0; j < kCombineBurst; ++j) {
+      t[j] = 0.f;
+      if (i + (j & ~7) < ks)  // whole groups of 8 (wave-uniform)
+        t[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (uint32_t)((i + j) * kTile + lane) * 4u, 0, kAuxSc1));
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += t[j];
+    for (int j = 0; j < kCombineBurst; ++j)
+      if (i + j < ks) acc += t[j];
   }
-  for (; i < ks; ++i)
-    acc += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, lane * 4, i * kTile * 4, kAuxSc1));
   if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
@@ -474,94 +487,23 @@ __device__ __forceinline__ void argmax_tiles(const GemvArgs &a, int tile, int ti
   }
 }
 
-// One GEMV work unit (64-row tile t, k-split s) executed by one wave of a standalone launch.
-//   * the wave streams its runs in batches of kBatch, one batch in flight while the previous
-//     one is computed;
-//   * split-K partials travel through device-coherent memory and the last wave of a tile adds
-//     them in a fixed order, then runs the epilogue.
-// SYNC selects the unit's role in the fused attention kernel: kSyncNone (standalone),
-// kSyncProducer (the qkv GEMV: device-coherent output stores, then a count for the KV head of
-// its rows), kSyncConsumer (the o GEMV: weights requested, then a wait on the producers of its
-// k-range, then device-coherent activation loads).
-constexpr int kSyncNone = 0, kSyncProducer = 1, kSyncConsumer = 2;
-
-template <int FMT, bool NORM, int EPI, int SYNC = kSyncNone>
-__device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> (&sm)[2], int lane) {
-  constexpr bool XCOH = SYNC == kSyncConsumer;
-  constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
-  constexpr int CK = Q4 ? 32 : 16;  // k per 16-byte run
-  const int ks = a.ks, K = a.K, N = a.N;
-  const int tile = unit / ks;
-  const int ksi = unit - tile * ks;
-  const int nch = K / CK;
-  const int c0 = ksi * a.cps;
-  const int c1 = min(nch, c0 + a.cps);
-  const int nrun = c1 - c0;
-  const int gshift = a.group;  // Q4: log2(group / 32), set by the launcher
-  const size_t tile_bytes = (size_t)nch * kTile * 16;
-  const __amdgpu_buffer_rsrc_t wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
-  __amdgpu_buffer_rsrc_t sr = wr;
-  int g0 = 0;
-  if constexpr (Q4) {
-    g0 = c0 >> gshift;
-    const int g1 = (c1 - 1) >> gshift;
-    sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
-              (uint32_t)(g1 - g0 + 1) * kTile * 2);
-  }
-  const __amdgpu_buffer_rsrc_t xr = rsrc(a.x + (size_t)c0 * CK, (uint32_t)nrun * CK * 4);
-  const __amdgpu_buffer_rsrc_t gr = NORM ? rsrc(a.gamma + (size_t)c0 * CK, (uint32_t)nrun * CK * 4) : xr;
-
-  // Software pipeline: batch b + 1 is in flight while batch b is staged and computed; past the
-  // last run the loads read zeros.
-  float acc = 0.f;
-  GemvBatch<FMT, NORM> A, B;
-  load_weights<FMT, NORM>(A, wr, sr, 0, c0, g0, gshift, lane);
-  // The epilogue's inputs (sums of squares, bias, residual, INT8 row scale) are fetched now, so
-  // the wave that finishes a tile does not wait on memory for them.
-  const int n = tile * kTile + lane;
-  const bool valid = n < N;
-  float pre_ssq = 0.f, pre_bias = 0.f, pre_res = 0.f, pre_scale = 1.f;
-  if constexpr (NORM) {
-    // one plain load per lane (a sum here would make the wave wait for the weights above too)
-    if (lane < a.ssq_n) pre_ssq = a.ssq[lane];
-    for (int i = lane + 64; i < a.ssq_n; i += 64) pre_ssq += a.ssq[i];
-  }
-  if (EPI != EPI_SWIGLU && valid) {
-    if (a.bias) pre_bias = a.bias[n];
-    if (a.residual) pre_res = a.residual[n];  // (y may alias it: only this tile's epilogue writes y[n])
-  }
-  if constexpr (FMT == QDEC_W_Q8_ROW) pre_scale = reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
-  unsigned e = 0;
-  if constexpr (SYNC != kSyncNone) e = __builtin_amdgcn_readfirstlane(*a.epoch);
-  if constexpr (SYNC == kSyncConsumer) {
-    // the producers of activations k = c0 CK .. c1 CK - 1 (the weights above are already on
-    // their way)
-    if (!poll_flags(a.wait_flags, (c0 * CK) / a.wait_div, (c1 * CK - 1) / a.wait_div, e, a.err, lane)) return;
-  }
-  load_acts<FMT, NORM, XCOH>(A, xr, gr, 0, lane);
-  const int nb = (nrun + kBatch - 1) / kBatch;
-  for (int b = 0; b < nb; b += 2) {
-    load_batch<FMT, NORM, XCOH>(B, wr, sr, xr, gr, (b + 1) * kBatch, c0, g0, gshift, lane);
-    compute_batch<FMT, NORM>(acc, A, sm[0], lane);
-    if (b + 1 >= nb) break;
-    load_batch<FMT, NORM, XCOH>(A, wr, sr, xr, gr, (b + 2) * kBatch, c0, g0, gshift, lane);
-    compute_batch<FMT, NORM>(acc, B, sm[1], lane);
-  }
-  if constexpr (Q4) acc *= 16777216.0f;  // 2^24, exact
-
-  if (ks > 1 && !splitk_combine(acc, a.part, a.counters, tile, ks, ksi, lane)) return;
-
-  // ------------------------------------------------------------------ epilogue (one tile)
+// The epilogue of one 64-row tile once its k-splits are summed into acc (the wave that finished
+// the tile): 1/rms of an RMSNorm prologue, INT8 row scale, bias, residual, then the store (and a
+// count for the qkv tile's KV head when COUNT), the tile's sum of squares for the next RMSNorm,
+// or SwiGLU, or the greedy argmax candidate.  pre_*: the epilogue's inputs fetched earlier.
+template <int FMT, bool NORM, int EPI, bool COUNT>
+__device__ __forceinline__ void gemv_tile_epilogue(const GemvArgs &a, float acc, int tile, int n, bool valid, float pre_ssq,
+                                                   float pre_bias, float pre_res, float pre_scale, int lane) {
   float v = acc;
-  if constexpr (NORM) v *= rsqrtf(wave_sum(pre_ssq) / (float)K + a.eps);
+  if constexpr (NORM) v *= rsqrtf(wave_sum(pre_ssq) / (float)a.K + a.eps);
   if constexpr (FMT == QDEC_W_Q8_ROW) v *= pre_scale;
   if constexpr (EPI == EPI_STORE || EPI == EPI_ARGMAX) {
     if (valid) {
       if (a.bias) v += pre_bias;
       if (a.residual) v += pre_res;
-      st_f<SYNC == kSyncProducer>(a.y + n, v);
+      st_f<COUNT>(a.y + n, v);
     }
-    if constexpr (SYNC == kSyncProducer) {
+    if constexpr (COUNT) {
       // qkv: count this tile for the KV head its rows belong to (tiles never straddle heads)
       drain_stores();
       const int row0 = tile * kTile, qd = a.Hq * a.hd, kd = a.Hkv * a.hd;
@@ -577,14 +519,174 @@ __device__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G
       float bv = (valid && v == v) ? v : -INFINITY;
       int bi = (valid && v == v) ? n : INT_MAX;
       wave_argmax(bv, bi);
-      argmax_tiles(a, tile, (N + kTile - 1) / kTile, bv, bi, lane);
+      argmax_tiles(a, tile, (a.N + kTile - 1) / kTile, bv, bi, lane);
     }
   } else {
     // lanes 0..31: gate rows 32 tile + lane; lanes 32..63: the matching up rows
     const float u = __shfl(v, lane + 32, 64);
     const int i = tile * 32 + lane;
-    if (lane < 32 && i < N / 2) a.y[i] = silu(v) * u;
+    if (lane < 32 && i < a.N / 2) a.y[i] = silu(v) * u;
   }
+}
+
+// One GEMV work unit (64-row tile t, k-split s) executed by one wave.
+//   * the wave streams its runs in batches of kBatch, one batch in flight while the previous
+//     one is computed;
+//   * split-K partials travel through device-coherent memory and the last wave of a tile adds
+//     them in a fixed order, then runs the epilogue.
+// SYNC selects the unit's role in the fused attention kernels: kSyncNone (standalone),
+// kSyncProducer (the qkv GEMV: device-coherent output stores, then a count for the KV head of
+// its rows), kSyncConsumer (the o GEMV: weights requested, then a wait on the producers of its
+// k-range, then device-coherent activation loads).
+// start() issues the unit's first weight loads and fetches the epilogue's inputs; finish() does
+// the rest, so a kernel can issue the loads of several roles before computing any of them.
+// With WLDS the unit's runs (at most kStashRuns) are copied by start() straight from HBM into
+// the wave's LDS stash (no registers held; the copy lands while the wave does other work), and
+// finish() reads them from there.
+constexpr int kSyncNone = 0, kSyncProducer = 1, kSyncConsumer = 2;
+constexpr int kStashRuns = 8;  // 1 KiB runs of one unit an LDS stash holds
+
+__device__ __forceinline__ void lds_dma_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void *lds_slot) {
+  // each lane's 16 bytes land at lds_slot + 16 * lane
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)(const_cast<void *>(lds_slot)), 16, voff, 0, 0, kAuxStream);
+}
+
+template <int FMT, bool NORM, int EPI, int SYNC = kSyncNone, bool WLDS = false, int PF = 2>
+struct GemvUnit {
+  static constexpr bool XCOH = SYNC == kSyncConsumer;
+  static constexpr bool Q4 = FMT == QDEC_W_Q4_G_ZP8;
+  static constexpr int CK = Q4 ? 32 : 16;  // k per 16-byte run
+  static_assert(PF >= 2 && PF % 2 == 0, "an even number of batches in flight (the two stage slots alternate)");
+  int tile, ksi, c0, nrun, g0, gshift, n;
+  bool valid;
+  __amdgpu_buffer_rsrc_t wr, sr, xr, gr;
+  GemvBatch<FMT, NORM> A;            // the stash path's first batch
+  GemvBatch<FMT, NORM> buf[WLDS ? 1 : PF];
+  uint16_t s_all[WLDS ? kStashRuns : 1];
+  float pre_ssq, pre_bias, pre_res, pre_scale;
+
+  __device__ __forceinline__ void start(const GemvArgs &a, int unit, int lane, const u32x4 *stash = nullptr) {
+    const int ks = a.ks, K = a.K;
+    tile = unit / ks;
+    ksi = unit - tile * ks;
+    const int nch = K / CK;
+    c0 = ksi * a.cps;
+    const int c1 = min(nch, c0 + a.cps);
+    nrun = c1 - c0;
+    gshift = a.group;  // Q4: log2(group / 32), set by the launcher
+    const size_t tile_bytes = (size_t)nch * kTile * 16;
+    wr = rsrc(a.W + (size_t)tile * tile_bytes + (size_t)c0 * kTile * 16, (uint32_t)nrun * kTile * 16);
+    sr = wr;
+    g0 = 0;
+    if constexpr (Q4) {
+      g0 = c0 >> gshift;
+      const int g1 = (c1 - 1) >> gshift;
+      sr = rsrc(reinterpret_cast<const uint8_t *>(a.S) + (size_t)tile * ((size_t)(nch >> gshift) * kTile * 2) + (size_t)g0 * kTile * 2,
+                (uint32_t)(g1 - g0 + 1) * kTile * 2);
+    }
+    xr = rsrc(a.x + (size_t)c0 * CK, (uint32_t)nrun * CK * 4);
+    gr = NORM ? rsrc(a.gamma + (size_t)c0 * CK, (uint32_t)nrun * CK * 4) : xr;
+    // The epilogue's inputs (sums of squares, bias, residual, INT8 row scale) are fetched first,
+    // so the wave that finishes a tile does not wait on memory for them; then the batches, each
+    // as weights + activations, in the order the loop reissues them (so the loop's waits count
+    // exactly the loads of the batch being computed).
+    n = tile * kTile + lane;
+    valid = n < a.N;
+    pre_ssq = 0.f;
+    pre_bias = 0.f;
+    pre_res = 0.f;
+    pre_scale = 1.f;
+    if constexpr (NORM) {
+      // one plain load per lane (a sum here would make the wave wait for the weights above too)
+      if (lane < a.ssq_n) pre_ssq = a.ssq[lane];
+      for (int i = lane + 64; i < a.ssq_n; i += 64) pre_ssq += a.ssq[i];
+    }
+    if (EPI != EPI_SWIGLU && valid) {
+      if (a.bias) pre_bias = a.bias[n];
+      if (a.residual) pre_res = a.residual[n];  // (y may alias it: only this tile's epilogue writes y[n])
+    }
+    if constexpr (FMT == QDEC_W_Q8_ROW) pre_scale = reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
+    if constexpr (WLDS) {
+#pragma unroll
+      for (int r = 0; r < kStashRuns; ++r) {
+        if (r < nrun) lds_dma_b128(wr, (uint32_t)r * (kTile * 16) + lane * 16, stash + r * kTile);
+        if constexpr (Q4)
+          s_all[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, (uint32_t)(((c0 + r) >> gshift) - g0) * (kTile * 2) + lane * 2, 0, 0);
+      }
+    } else {
+      static_assert(SYNC != kSyncConsumer, "a consumer's activations are loaded after its wait");
+#pragma unroll
+      for (int i = 0; i + 1 < PF; ++i) load_batch<FMT, NORM, XCOH>(buf[i], wr, sr, xr, gr, i * kBatch, c0, g0, gshift, lane);
+    }
+  }
+
+  __device__ __forceinline__ void finish(const GemvArgs &a, Stage<CK> (&sm)[2], int lane, const u32x4 *stash = nullptr,
+                                        unsigned long long *rec = nullptr) {
+    unsigned e = 0;
+    if constexpr (SYNC != kSyncNone) e = __builtin_amdgcn_readfirstlane(*a.epoch);
+    if constexpr (SYNC == kSyncConsumer) {
+      // the producers of activations k = c0 CK .. (c0 + nrun) CK - 1 (the weights are already
+      // on their way)
+      if (!poll_flags(a.wait_flags, (c0 * CK) / a.wait_div, ((c0 + nrun) * CK - 1) / a.wait_div, e, a.err, lane)) return;
+      mark(rec, 0);
+    }
+    float acc = 0.f;
+    const int nb = (nrun + kBatch - 1) / kBatch;
+    if constexpr (WLDS) {
+      static_assert(kStashRuns == 2 * kBatch, "two batches per stash");
+      GemvBatch<FMT, NORM> B;
+      load_acts<FMT, NORM, XCOH>(A, xr, gr, 0, lane);
+      load_acts<FMT, NORM, XCOH>(B, xr, gr, kBatch, lane);
+      __builtin_amdgcn_s_waitcnt(0);  // the stash copies (not tracked by the compiler) have landed
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        A.w[i] = (i < nrun) ? stash[i * kTile + lane] : u32x4{0u, 0u, 0u, 0u};
+        A.s[i] = (i < nrun) ? s_all[i] : (uint16_t)0;
+      }
+      compute_batch<FMT, NORM>(acc, A, sm[0], lane);
+      if (nb > 1) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          B.w[i] = (kBatch + i < nrun) ? stash[(kBatch + i) * kTile + lane] : u32x4{0u, 0u, 0u, 0u};
+          B.s[i] = (kBatch + i < nrun) ? s_all[kBatch + i] : (uint16_t)0;
+        }
+        compute_batch<FMT, NORM>(acc, B, sm[1], lane);
+      }
+    } else {
+      // Software pipeline over PF batch slots: batches 0 .. PF - 2 were requested by start();
+      // each step requests the batch PF - 1 ahead into the slot computed last, then stages and
+      // computes the current one, so PF - 1 batches are in flight meanwhile.  The loop is entered
+      // (from start() and from its own end) with the same loads pending, in the same order, so
+      // the wait before each compute counts exactly the loads issued after that batch's.  Past
+      // the last run the loads read zeros.
+      for (int b = 0; b < nb; b += PF) {
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+          load_batch<FMT, NORM, XCOH>(buf[(k + PF - 1) % PF], wr, sr, xr, gr, (b + k + PF - 1) * kBatch, c0, g0, gshift,
+                                      lane);
+          compute_batch<FMT, NORM>(acc, buf[k], sm[k & 1], lane);
+          if (b + k + 1 >= nb) break;
+        }
+      }
+    }
+    if constexpr (Q4) acc *= 16777216.0f;  // 2^24, exact
+    mark(rec, 1);
+
+    if (a.ks > 1 && !splitk_combine(acc, a.part, a.counters, tile, a.ks, ksi, lane)) return;
+    mark(rec, 2);
+    gemv_tile_epilogue<FMT, NORM, EPI, SYNC == kSyncProducer>(a, acc, tile, n, valid, pre_ssq, pre_bias, pre_res, pre_scale,
+                                                             lane);
+  }
+};
+
+template <int FMT, bool NORM, int EPI, int SYNC = kSyncNone, int PF = 2>
+__device__ __forceinline__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> (&sm)[2],
+                                          int lane) {
+  GemvUnit<FMT, NORM, EPI, SYNC, false, PF> u;
+  u.start(a, unit, lane);
+  u.finish(a, sm, lane);
 }
 
 }  // namespace dev

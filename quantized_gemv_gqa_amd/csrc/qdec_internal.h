@@ -69,7 +69,6 @@ constexpr int kArgGroups = 64;                   // argmax reduction groups (til
 constexpr int kArgGroupLine0 = kCounterLines - kArgGroups;
 constexpr int kArgTopLine = kArgGroupLine0 - 1;
 constexpr int kMaxSplitTiles = kArgTopLine;      // tiles 0 .. kMaxSplitTiles-1 own lines 0 ..
-constexpr int kProgressReplicas = 64;            // persistent step: one 128-byte line each
 
 struct GemvPlan {
   int tiles, nch, ks, cps, units, blocks;
@@ -132,6 +131,15 @@ struct AttnArgs {
   unsigned *err;
 };
 constexpr int kMaxMergeSplits = 256;
+// The attention kernels address a layer's K or V pool through one buffer resource with 32-bit
+// byte offsets, so a pool must stay below 4 GiB.
+inline bool kv_pool_fits(long long n_pages, int Hkv, int D, int kv_fmt) {
+  const long long eb = kv_fmt == QDEC_KV_BF16 ? 2 : 4;
+  return n_pages >= 1 && n_pages * Hkv * QDEC_PAGE_SIZE * D * eb < (1LL << 32);
+}
+// Error word values of the step handles: a bounded wait gave up, or the token being decoded has
+// no cache slot (position < 0, past the page table, or an unmapped page-table entry).
+constexpr unsigned kErrWait = 1u, kErrKvSlot = 2u;
 constexpr size_t kAttnCounterBytes = 64 * 128;  // one line per KV head, up to 64 KV heads
 size_t attn_workspace_bytes(int Hq, int D, int splits);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
@@ -142,16 +150,20 @@ hipError_t launch_kv_append(const float *k, const float *v, void *k_pool, void *
                             int D, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- fused layer
-// The attention half of a decoder layer as one launch (see layer.hip): qkv GEMV, attention and
-// o GEMV as workgroup roles.  GEMV units are unit = block * waves + wave within their role's
-// block range.
+// The attention half of a decoder layer as one launch (see layer.hip): nblk workgroups (one per
+// compute unit) of attn_layer_waves() waves; wave w of workgroup b holds qkv unit b * waves + w
+// and o unit (nblk - 1 - b) * waves + w, workgroup b < Hkv * splits attention unit (b / splits,
+// b % splits).  The o units' runs (at most attn_layer_stash_runs()) are staged in LDS.
 struct LayerArgs {
   GemvArgs qkv, o;
   AttnArgs at;
-  int nb_qkv, nb_o;  // blocks per GEMV role
+  int nblk;
+  unsigned long long *timeline;  // diagnostics: [nblk * waves][16] clock marks, or null
 };
 bool layer_fusion_supported(int G, int D);
 int attn_layer_waves();
+int attn_layer_stash_runs();
+int attn_layer_blocks_per_cu(int wfmt, int kv_fmt, int G);  // 0: the kernel does not fit a CU
 hipError_t launch_attn_layer(const LayerArgs &a, int wfmt, hipStream_t st);
 
 // ---------------------------------------------------------------------------------- small ops
@@ -187,5 +199,8 @@ hipError_t launch_argmax_finish(const float *logits, int n, int32_t *token, int3
                                 int32_t *token_log, int32_t *step_count, int log_len,
                                 hipStream_t st);
 hipError_t launch_copy(const float *src, float *dst, int n, hipStream_t st);
+// Bandwidth reference: reads bytes (a multiple of 16) at src once; *sink is written only in the
+// unlikely case that the bytes' XOR is one fixed value.
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace qdec

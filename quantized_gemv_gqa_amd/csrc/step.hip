@@ -15,7 +15,6 @@
 #include <cmath>
 #include <vector>
 
-#include "qdec_fused.h"
 #include "qdec_batch.h"
 
 struct qdec_step {
@@ -35,6 +34,9 @@ struct qdec_step {
   size_t lsync_layer_words = 0;
   void *gemv_ws = nullptr;
   qdec::GemvPlan p_qkv, p_o, p_gu, p_down, p_lm;
+  int nblk = 0;    // workgroups of the fused attention launch (one per compute unit)
+  unsigned long long *timeline = nullptr;  // diagnostics: per-wave clock marks of the fused launches
+  int splits = 1;  // attention splits per KV head in use (the config's, capped for the fused launch)
   int ssq_n = 0;
   hipGraph_t graph[2] = {nullptr, nullptr};      // [per-op]: captured step
   hipGraphExec_t exec[2] = {nullptr, nullptr};
@@ -46,11 +48,11 @@ struct qdec_step {
   int top_k = 0;
   uint64_t seed = 0;
   void *sample_ws = nullptr;
-  // persistent step
-  bool fused_ok = false;
-  int fused_blocks = 0;
-  qdec::FusedArgs fa{};
   unsigned *err = nullptr;
+  // per-kernel timing of one eager step (qdec_step_kernel_times): an event after every launch
+  std::vector<hipEvent_t> tev;
+  size_t tev_n = 0;
+  bool timing = false;
 };
 
 namespace qdec {
@@ -59,62 +61,32 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, fused_layers, err, sample_ws, total;
-  // persistent step
-  size_t hB, xa, xb, ssqA, ssqB, sync, gu_flag, tile_cnt, cand, sub_cand, part[5];
-  size_t part_bytes[5];
-  int tiles[5], nch[5];
+  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, err, sample_ws, hB, ssqB, total;
 };
 
-// Largest wave count the stream-K partitions are sized for (512 CUs x 8 waves); a larger grid
-// leaves the extra waves idle in the GEMV phases.
-constexpr int kMaxFusedWaves = 4096;
+// The fused attention launch has one workgroup per compute unit, at most this many (the GEMV
+// workspaces hold one split-K partial tile per wave of that grid).
+constexpr int kMaxLayerBlocks = 512;
 
-// Sync region of the persistent step, in 128-byte lines
-struct SyncLines {
-  int epoch, qkv_done, attn_all, o_done, down_done, progress, lm_sub, lm_top, total;
-};
-SyncLines sync_lines(const qdec_config &c) {
-  SyncLines s{};
-  int o = 0;
-  s.epoch = o; o += 1;
-  s.qkv_done = o; o += c.n_layers * c.n_kv_heads;
-  s.attn_all = o; o += c.n_layers;
-  s.o_done = o; o += c.n_layers;
-  s.down_done = o; o += c.n_layers;
-  s.progress = o; o += kProgressReplicas;
-  s.lm_sub = o; o += 64;
-  s.lm_top = o; o += 1;
-  s.total = o;
-  return s;
-}
-
-int sk_wave_h(const SkPhase &p, long r) {
-  const long big = (long)p.rem * (p.q + 1);
-  return (int)(r < big ? r / (p.q + 1) : p.rem + (r - big) / p.q);
-}
-
-// Stream-K partition of a GEMV of `tiles` x `nch` runs over at most `waves` waves, with at most
-// kMaxSlots contributors per tile (fewer waves take part if needed).
-SkPhase plan_sk(int tiles, int nch, int waves) {
-  SkPhase p{};
-  p.tiles = tiles;
-  p.nch = nch;
-  const long R = (long)tiles * nch;
-  int nw = (int)std::min<long>(std::min(waves, kMaxFusedWaves), R);
-  for (;;) {
-    p.nw = nw;
-    p.q = (int)(R / nw);
-    p.rem = (int)(R % nw);
-    int mx = 1;
-    for (int t = 0; t < tiles; ++t)
-      mx = std::max(mx, sk_wave_h(p, (long)t * nch + nch - 1) - sk_wave_h(p, (long)t * nch) + 1);
-    if (mx <= kMaxSlots || nw == 1) {
-      p.slots = mx;
-      return p;
-    }
-    nw = std::max(1, (int)((long)nw * (kMaxSlots - 1) / mx));
+// GEMV plan of the fused attention launch: the fewest runs per unit, at least one pipeline batch
+// (or the whole row), such that every unit has a wave of the grid; an o unit's runs must also fit
+// the LDS stash (max_cps).  units == 0: no split fits.
+GemvPlan layer_plan(int wfmt, int N, int K, int waves, int max_cps) {
+  GemvPlan p{};
+  const int ck = (wfmt == QDEC_W_Q4_G_ZP8) ? 32 : 16;
+  p.tiles = (N + kTile - 1) / kTile;
+  p.nch = K / ck;
+  for (int cps = std::min(4, p.nch); cps <= std::min(max_cps, p.nch); ++cps) {
+    const int ks = (p.nch + cps - 1) / cps;
+    if ((long)p.tiles * ks > waves) continue;
+    p.cps = (p.nch + ks - 1) / ks;
+    p.ks = (p.nch + p.cps - 1) / p.cps;
+    p.units = p.tiles * p.ks;
+    p.blocks = (p.units + 3) / 4;
+    return p;
   }
+  p.units = 0;
+  return p;
 }
 
 // Per layer: the qkv tile counts (one 128-byte line per KV head) and the attention-done flags
@@ -137,39 +109,14 @@ Layout layout_of(const qdec_config &c) {
   g = std::max(g, gemv_workspace_bytes(c.wfmt, 2 * c.inter, c.hidden));
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, c.inter));
   if (c.vocab > 0) g = std::max(g, gemv_workspace_bytes(c.wfmt, c.vocab, c.hidden, true));
+  g = std::max(g, kCounterBytes + (size_t)kMaxLayerBlocks * attn_layer_waves() * kTile * sizeof(float));
   L.gemv_ws = off; off += align256(g);
   L.gemv_ws2 = off; off += align256(g);
   L.lsync = off; off += align256((32 + (size_t)c.n_layers * lsync_layer_words(c.n_kv_heads)) * 4);
   L.err = off; off += 256;
   L.sample_ws = off; off += align256(sample_workspace_bytes());
-  // persistent step: activations, sync lines, per-phase split state
-  L.fused_layers = off; off += align256((size_t)c.n_layers * sizeof(FusedLayer));
   L.hB = off; off += align256((size_t)c.hidden * 4);
-  L.xa = off; off += align256((size_t)c.hidden * 4);
-  L.xb = off; off += align256((size_t)c.hidden * 4);
-  L.ssqA = off; off += align256(std::max<size_t>(256, (size_t)((c.hidden + 63) / 64) * 4));
   L.ssqB = off; off += align256(std::max<size_t>(256, (size_t)((c.hidden + 63) / 64) * 4));
-  L.sync = off; off += (size_t)sync_lines(c).total * 128;
-  const int ck = (c.wfmt == QDEC_W_Q4_G_ZP8) ? 32 : 16;
-  const int Ns[5] = {nqkv, c.hidden, 2 * c.inter, c.hidden, std::max(c.vocab, 1)};
-  const int Ks[5] = {c.hidden, qd, c.hidden, c.inter, c.hidden};
-  size_t ntiles = 0;
-  for (int i = 0; i < 5; ++i) {
-    L.tiles[i] = (Ns[i] + kTile - 1) / kTile;
-    L.nch[i] = Ks[i] / ck;
-    ntiles += (size_t)L.tiles[i];
-    // sized for the largest grid; a smaller one has fewer contributors per tile
-    const SkPhase p = plan_sk(L.tiles[i], std::max(L.nch[i], 1), kMaxFusedWaves);
-    L.part_bytes[i] = p.slots > 1 ? (size_t)L.tiles[i] * p.slots * kTile * 4 : 0;
-  }
-  L.gu_flag = off; off += align256((size_t)c.n_layers * L.tiles[2] * 4);
-  L.tile_cnt = off; off += align256(ntiles * 128);
-  L.cand = off; off += align256((size_t)L.tiles[4] * 8);
-  L.sub_cand = off; off += align256(64 * 8);
-  for (int i = 0; i < 5; ++i) {
-    L.part[i] = off;
-    off += align256(L.part_bytes[i]);
-  }
   L.total = off;
   return L;
 }
@@ -189,6 +136,8 @@ qdec_status validate(const qdec_config *c) {
                "qdec_step: unknown kv format %d", c->kv_fmt);
   QDEC_REQUIRE(c->page_size == QDEC_PAGE_SIZE && c->n_pages >= 1, QDEC_EUNSUPPORTED,
                "qdec_step: page_size must be 16 and n_pages >= 1");
+  QDEC_REQUIRE(kv_pool_fits(c->n_pages, c->n_kv_heads, c->head_dim, c->kv_fmt), QDEC_EUNSUPPORTED,
+               "qdec_step: a layer's KV pool (%d pages) must stay below 4 GiB", c->n_pages);
   QDEC_REQUIRE(c->num_splits >= 1 && c->num_splits <= kMaxMergeSplits, QDEC_EINVAL,
                "qdec_step: num_splits in [1, %d]", kMaxMergeSplits);
   QDEC_REQUIRE(c->n_kv_heads <= (int)(kAttnCounterBytes / 128), QDEC_EUNSUPPORTED, "qdec_step: too many KV heads");
@@ -225,6 +174,11 @@ GemvArgs gemv_args(const qdec_step *h, const void *W, const void *S, const float
   return a;
 }
 
+// Records the next timing event after a launch while qdec_step_kernel_times runs a step.
+void step_mark(qdec_step *h, hipStream_t st) {
+  if (h->timing && h->tev_n < h->tev.size()) (void)hipEventRecord(h->tev[h->tev_n++], st);
+}
+
 #define QDEC_CK(expr)                                      \
   do {                                                     \
     hipError_t e_ = (expr);                                \
@@ -233,6 +187,7 @@ GemvArgs gemv_args(const qdec_step *h, const void *W, const void *S, const float
       return QDEC_EHIP;                                    \
     }                                                      \
     ++n;                                                   \
+    step_mark(h, st);                                      \
   } while (0)
 
 AttnArgs step_attn_args(const qdec_step *h, int l) {
@@ -255,7 +210,7 @@ AttnArgs step_attn_args(const qdec_step *h, int l) {
   at.Hkv = c.n_kv_heads;
   at.D = c.head_dim;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
-  at.splits = c.num_splits;
+  at.splits = h->splits;
   at.counters = reinterpret_cast<unsigned *>(h->attn_ws);
   at.ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
   at.out = h->attn;
@@ -302,11 +257,11 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   la.o.err = h->err;
   gemv_apply_plan(la.qkv, h->p_qkv, c.wfmt);
   gemv_apply_plan(la.o, h->p_o, c.wfmt);
-  const int aw = attn_layer_waves();
-  la.nb_qkv = (h->p_qkv.units + aw - 1) / aw;
-  la.nb_o = (h->p_o.units + aw - 1) / aw;
+  la.nblk = h->nblk;
+  la.timeline = h->timeline ? h->timeline + (size_t)l * h->nblk * attn_layer_waves() * 16 : nullptr;
   hipError_t e = launch_attn_layer(la, c.wfmt, st);
   if (e != hipSuccess) return e;
+  step_mark(h, st);
   // the MLP block as two plain launches: its gate/up tiles all finish together, so a down GEMV
   // in the same launch could only wait for them
   GemvArgs g = gemv_args(h, w.w_gu, w.s_gu, h->hB, h->mlp, 2 * I, H, h->p_gu);
@@ -315,6 +270,7 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   g.epi = EPI_SWIGLU;
   e = launch_gemv(c.wfmt, g, h->p_gu, st);
   if (e != hipSuccess) return e;
+  step_mark(h, st);
   GemvArgs d = gemv_args(h, w.w_down, w.s_down, h->mlp, hA, H, I, h->p_down);
   d.residual = h->hB;
   d.ssq_out = h->ssq;
@@ -364,10 +320,11 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count, bool per_op) 
     at.Hkv = Hkv;
     at.D = D;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
-    at.splits = c.num_splits;
+    at.splits = h->splits;
     at.counters = reinterpret_cast<unsigned *>(h->attn_ws);
     at.ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
     at.out = h->attn;
+    at.err = h->err;
     QDEC_CK(launch_attention(at, st));
     GemvArgs o = gemv_args(h, w.w_o, w.s_o, h->attn, s.hidden, H, qd, h->p_o);
     o.residual = s.hidden;
@@ -409,94 +366,6 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count, bool per_op) 
     QDEC_CK(launch_argmax_finish(nullptr, 0, nullptr, s.pos, nullptr, s.step_count, 0, st));
   }
   if (count) *count = n;
-  return QDEC_OK;
-}
-
-qdec_status setup_fused(qdec_step *h, const Layout &L, int G) {
-  const qdec_config &c = h->cfg;
-  const qdec_state &s = h->state;
-  char *ws = reinterpret_cast<char *>(s.workspace);
-  std::vector<FusedLayer> tab(c.n_layers);
-  for (int l = 0; l < c.n_layers; ++l) {
-    const qdec_layer_weights &w = h->layers[l];
-    FusedLayer &f = tab[l];
-    f.w_qkv = reinterpret_cast<const uint8_t *>(w.w_qkv);
-    f.w_o = reinterpret_cast<const uint8_t *>(w.w_o);
-    f.w_gu = reinterpret_cast<const uint8_t *>(w.w_gu);
-    f.w_down = reinterpret_cast<const uint8_t *>(w.w_down);
-    f.s_qkv = w.s_qkv; f.s_o = w.s_o; f.s_gu = w.s_gu; f.s_down = w.s_down;
-    f.b_qkv = c.has_qkv_bias ? w.b_qkv : nullptr;
-    f.g_attn = w.g_attn; f.g_ffn = w.g_ffn;
-    f.g_q = c.has_qk_norm ? w.g_q : nullptr;
-    f.g_k = c.has_qk_norm ? w.g_k : nullptr;
-    f.k_pool = h->kpools[l]; f.v_pool = h->vpools[l];
-  }
-  hipError_t e = hipMemcpy(ws + L.fused_layers, tab.data(), tab.size() * sizeof(FusedLayer), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    set_error("qdec_step_create: copying the layer table: %s", hipGetErrorString(e));
-    return QDEC_EHIP;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
-    set_error("qdec_step_create: cannot read the CU count");
-    return QDEC_EHIP;
-  }
-  const int per_cu = std::min(2, fused_blocks_per_cu(c.wfmt, G));
-  if (per_cu < 1) return QDEC_OK;  // not co-resident: the fused mode stays unavailable
-  h->fused_blocks = cus * per_cu;
-  const int waves = h->fused_blocks * 4;
-  FusedArgs &a = h->fa;
-  const int D = c.head_dim;
-  a.layers = reinterpret_cast<const FusedLayer *>(ws + L.fused_layers);
-  a.L = c.n_layers; a.H = c.hidden; a.Hq = c.n_heads; a.Hkv = c.n_kv_heads; a.V = c.vocab; a.I = c.inter;
-  a.splits = c.num_splits; a.n_pages = c.n_pages;
-  int gshift = 0;
-  if (c.wfmt == QDEC_W_Q4_G_ZP8)
-    while ((32 << gshift) < c.group) ++gshift;
-  a.gshift = gshift;
-  a.eps = c.rms_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D)); a.rope_base = c.rope_base;
-  a.embed = h->model.embed;
-  a.w_lm = reinterpret_cast<const uint8_t *>(h->model.w_lm);
-  a.s_lm = h->model.s_lm;
-  a.g_out = h->model.g_out;
-  a.page_table = s.page_table; a.pos = s.pos; a.token = s.token;
-  a.token_log = s.token_log; a.step_count = s.step_count; a.log_len = s.log_len;
-  a.hA = s.hidden;
-  a.hB = reinterpret_cast<float *>(ws + L.hB);
-  a.xa = reinterpret_cast<float *>(ws + L.xa);
-  a.xb = reinterpret_cast<float *>(ws + L.xb);
-  a.ssqA = reinterpret_cast<float *>(ws + L.ssqA);
-  a.ssqB = reinterpret_cast<float *>(ws + L.ssqB);
-  a.trace = s.trace; a.logits = s.logits;
-  a.qkv = h->qkv; a.attn = h->attn; a.mlp = h->mlp;
-  a.attn_cnt = reinterpret_cast<unsigned *>(h->attn_ws);
-  a.attn_ws = reinterpret_cast<float *>(reinterpret_cast<char *>(h->attn_ws) + kAttnCounterBytes);
-  const SyncLines sl = sync_lines(c);
-  unsigned *sync = reinterpret_cast<unsigned *>(ws + L.sync);
-  a.epoch = sync + sl.epoch * 32;
-  a.qkv_done = sync + sl.qkv_done * 32;
-  a.attn_all = sync + sl.attn_all * 32;
-  a.o_done = sync + sl.o_done * 32;
-  a.down_done = sync + sl.down_done * 32;
-  a.progress = sync + sl.progress * 32;
-  a.lm_sub = sync + sl.lm_sub * 32;
-  a.lm_top = sync + sl.lm_top * 32;
-  a.gu_flag = reinterpret_cast<unsigned *>(ws + L.gu_flag);
-  a.cand = reinterpret_cast<float *>(ws + L.cand);
-  a.sub_cand = reinterpret_cast<float *>(ws + L.sub_cand);
-  a.err = h->err;
-  SkPhase *ph[5] = {&a.p_qkv, &a.p_o, &a.p_gu, &a.p_down, &a.p_lm};
-  unsigned *tc = reinterpret_cast<unsigned *>(ws + L.tile_cnt);
-  for (int i = 0; i < 5; ++i) {
-    SkPhase p = plan_sk(L.tiles[i], std::max(L.nch[i], 1), waves);
-    if (p.slots > 1 && (size_t)L.tiles[i] * p.slots * kTile * 4 > L.part_bytes[i]) return QDEC_OK;
-    p.part = reinterpret_cast<float *>(ws + L.part[i]);
-    p.tile_cnt = tc;
-    tc += (size_t)L.tiles[i] * kLine;
-    *ph[i] = p;
-  }
-  h->fused_ok = true;
   return QDEC_OK;
 }
 
@@ -754,6 +623,7 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   const int nqkv = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
   h->p_qkv = gemv_plan(cfg->wfmt, nqkv, cfg->hidden, true);
   h->p_o = gemv_plan(cfg->wfmt, cfg->hidden, qd, true);
+  h->splits = cfg->num_splits;
   h->p_gu = gemv_plan(cfg->wfmt, 2 * cfg->inter, cfg->hidden, true);
   h->p_down = gemv_plan(cfg->wfmt, cfg->hidden, cfg->inter, true);
   if (lm) h->p_lm = gemv_plan(cfg->wfmt, cfg->vocab, cfg->hidden, true);
@@ -764,13 +634,27 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   h->ssqB = reinterpret_cast<float *>(ws + L.ssqB);
   h->lsync = reinterpret_cast<unsigned *>(ws + L.lsync);
   h->lsync_layer_words = lsync_layer_words(cfg->n_kv_heads);
-  h->layer_ok = layer_fusion_supported(G, cfg->head_dim) && cfg->n_kv_heads <= kLine;
-  if (lm && m->embed && cfg->hidden % 64 == 0 && cfg->hidden <= 4096 &&
-      fused_supported(cfg->wfmt, G, cfg->head_dim, cfg->kv_fmt)) {
-    qdec_status r2 = setup_fused(h, L, G);
-    if (r2 != QDEC_OK) {
-      delete h;
-      return r2;
+  // The fused attention launch, when the shape has one and a workgroup per compute unit covers
+  // its work; the per-op launches then use the same GEMV plans and splits, so the two agree bit
+  // for bit.
+  h->layer_ok = false;
+  if (layer_fusion_supported(G, cfg->head_dim) && cfg->n_kv_heads <= kLine &&
+      attn_layer_blocks_per_cu(cfg->wfmt, cfg->kv_fmt, G) >= 1) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= 1) {
+      const int nblk = std::min(cus, kMaxLayerBlocks);
+      const int waves = nblk * attn_layer_waves();
+      const GemvPlan pq = layer_plan(cfg->wfmt, nqkv, cfg->hidden, waves, 1 << 30);
+      const GemvPlan po = layer_plan(cfg->wfmt, cfg->hidden, qd, waves, attn_layer_stash_runs());
+      const int S = std::min(cfg->num_splits, nblk / cfg->n_kv_heads);
+      if (pq.units > 0 && po.units > 0 && S >= 1) {
+        h->layer_ok = true;
+        h->nblk = nblk;
+        h->p_qkv = pq;
+        h->p_o = po;
+        h->splits = S;
+      }
     }
   }
   *out = h;
@@ -783,19 +667,6 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
   const bool per_op = (mode & QDEC_STEP_PER_OP) != 0;
   const int base = mode & ~QDEC_STEP_PER_OP;
   if (base == QDEC_STEP_EAGER) return enqueue_step(h, st, &h->n_kernels, per_op);
-  if (base == QDEC_STEP_FUSED) {
-    QDEC_REQUIRE(!per_op, QDEC_EINVAL, "qdec_decode_step: QDEC_STEP_PER_OP does not apply to the fused step");
-    QDEC_REQUIRE(!(h->temperature > 0.f), QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step decodes greedily only");
-    QDEC_REQUIRE(h->fused_ok, QDEC_EUNSUPPORTED, "qdec_decode_step: the fused step is not available for this model");
-    const int G = h->cfg.n_heads / h->cfg.n_kv_heads;
-    hipError_t e = launch_fused(h->fa, h->cfg.wfmt, G, h->fused_blocks, st);
-    if (e != hipSuccess) {
-      set_error("qdec_decode_step (fused): %s", hipGetErrorString(e));
-      return QDEC_EHIP;
-    }
-    h->n_kernels = 1;
-    return QDEC_OK;
-  }
   QDEC_REQUIRE(base == QDEC_STEP_GRAPH, QDEC_EINVAL, "qdec_decode_step: unknown mode %d", mode);
   const int v = per_op ? 1 : 0;
   if (!h->exec[v]) {
@@ -841,6 +712,47 @@ qdec_status qdec_decode_step(qdec_step *h, int mode, void *stream) {
 
 int qdec_step_kernel_count(const qdec_step *h) { return h ? h->n_kernels : 0; }
 
+int qdec_step_kernel_times(qdec_step *h, int mode, float *us, int max, void *stream) {
+  const char *nm = "qdec_step_kernel_times";
+  QDEC_REQUIRE(h && (us || max == 0) && max >= 0, QDEC_EINVAL, "%s: null argument", nm);
+  QDEC_REQUIRE((mode & ~QDEC_STEP_PER_OP) == QDEC_STEP_EAGER, QDEC_EINVAL, "%s: mode must be EAGER (| PER_OP)", nm);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t need = 8 + 8 * (size_t)h->cfg.n_layers;  // more than any step launches
+  while (h->tev.size() < need) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      set_error("%s: hipEventCreate failed", nm);
+      return QDEC_EHIP;
+    }
+    h->tev.push_back(e);
+  }
+  h->tev_n = 0;
+  h->timing = true;
+  step_mark(h, st);
+  int nk = 0;
+  const qdec_status r = enqueue_step(h, st, &nk, (mode & QDEC_STEP_PER_OP) != 0);
+  h->timing = false;
+  const size_t marks = h->tev_n;
+  hipError_t e = hipStreamSynchronize(st);
+  if (r != QDEC_OK) return r;
+  if (e != hipSuccess) {
+    set_error("%s: %s", nm, hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  const int n = (int)marks - 1;
+  for (int i = 0; i < n && i < max; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->tev[i], h->tev[i + 1]);
+    if (e != hipSuccess) {
+      set_error("%s: %s", nm, hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    us[i] = ms * 1000.f;
+  }
+  h->n_kernels = nk;
+  return n;
+}
+
 qdec_status qdec_step_set_sampling(qdec_step *h, float temperature, int top_k, float top_p, uint64_t seed) {
   const char *nm = "qdec_step_set_sampling";
   QDEC_REQUIRE(h, QDEC_EINVAL, "%s: null handle", nm);
@@ -870,21 +782,18 @@ qdec_status qdec_step_set_sampling(qdec_step *h, float temperature, int top_k, f
   return QDEC_OK;
 }
 
-int qdec_step_fused_supported(const qdec_step *h) { return h && h->fused_ok ? 1 : 0; }
 
-qdec_status qdec_step_phase_times(qdec_step *h, uint64_t *ts) {
-  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_phase_times: null handle");
-  h->fa.phase_ts = reinterpret_cast<unsigned long long *>(ts);
+
+
+
+int qdec_step_layer_blocks(const qdec_step *h) { return h && h->layer_ok ? h->nblk : 0; }
+
+qdec_status qdec_step_layer_timeline(qdec_step *h, uint64_t *ts) {
+  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_layer_timeline: null handle");
+  QDEC_REQUIRE(!ts || h->layer_ok, QDEC_EUNSUPPORTED, "qdec_step_layer_timeline: this step has no fused attention launch");
+  h->timeline = reinterpret_cast<unsigned long long *>(ts);
   return QDEC_OK;
 }
-
-qdec_status qdec_step_wave_times(qdec_step *h, uint32_t *ts) {
-  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_wave_times: null handle");
-  h->fa.wave_ts = reinterpret_cast<unsigned *>(ts);
-  return QDEC_OK;
-}
-
-int qdec_step_fused_waves(const qdec_step *h) { return h && h->fused_ok ? h->fused_blocks * 4 : 0; }
 
 qdec_status qdec_step_read_error(qdec_step *h, int *flag) {
   QDEC_REQUIRE(h && flag, QDEC_EINVAL, "qdec_step_read_error: null argument");
@@ -904,6 +813,7 @@ qdec_status qdec_step_read_error(qdec_step *h, int *flag) {
 
 void qdec_step_destroy(qdec_step *h) {
   if (!h) return;
+  for (hipEvent_t e : h->tev) (void)hipEventDestroy(e);
   for (int v = 0; v < 2; ++v) {
     if (h->exec[v]) (void)hipGraphExecDestroy(h->exec[v]);
     if (h->graph[v]) (void)hipGraphDestroy(h->graph[v]);

@@ -180,6 +180,24 @@ def test_attention_rejects_bad_arguments(L):
     assert _attn(L, out=None) == q.QDEC_EINVAL
 
 
+def test_kv_pools_over_4gib_are_refused(L):
+    """A layer's K or V pool is addressed with 32-bit byte offsets: pools of 4 GiB or more are
+    refused by every entry point that takes one, instead of reading zeros or wrong rows."""
+    # 8 KV heads x 16 x 128 x 2 B = 32 KiB per bf16 page: 131072 pages is exactly 4 GiB
+    # (the accepted size still stops at the too-small workspace, so nothing is launched)
+    st = _attn(L, n_heads=32, n_kv_heads=8, n_pages=131071, workspace_bytes=100)
+    assert st == q.QDEC_EINVAL and "workspace" in _err(L)
+    st = _attn(L, n_heads=32, n_kv_heads=8, n_pages=131072, workspace_bytes=100)
+    assert st == q.QDEC_EUNSUPPORTED and "4 GiB" in _err(L)
+    # fp32 pages are twice as large
+    assert _attn(L, n_heads=32, n_kv_heads=8, kv_fmt=q.KV_F32, n_pages=65536, workspace_bytes=100) == q.QDEC_EUNSUPPORTED
+    big = dict(n_heads=32, n_kv_heads=8, num_splits=8)
+    assert L.qdec_step_workspace_bytes(ctypes.byref(_cfg(n_pages=131071, **big))) > 0
+    assert L.qdec_step_workspace_bytes(ctypes.byref(_cfg(n_pages=131072, **big))) == 0
+    assert L.qdec_batch_workspace_bytes(ctypes.byref(_cfg(n_pages=131071, **big)), 8) > 0
+    assert L.qdec_batch_workspace_bytes(ctypes.byref(_cfg(n_pages=131072, **big)), 8) == 0
+
+
 def _cfg(**kw):
     c = q.QdecConfig()
     base = dict(n_layers=28, hidden=3584, n_heads=28, n_kv_heads=4, head_dim=128, inter=18944,

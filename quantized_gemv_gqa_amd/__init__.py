@@ -124,6 +124,8 @@ def lib():
         L.qdec_gemv_workspace_bytes.argtypes = [_I, _I, _I]; L.qdec_gemv_workspace_bytes.restype = Z
         L.qdec_gemv_q8.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _P, Z, _P]; L.qdec_gemv_q8.restype = S
         L.qdec_gemv_q4.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P, Z, _P]; L.qdec_gemv_q4.restype = S
+        L.qdec_gemv_q4_noalloc.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P]
+        L.qdec_gemv_q4_noalloc.restype = S
         L.qdec_quantize_act_i8.argtypes = [_P, _I, _I, _P, _P, _P]; L.qdec_quantize_act_i8.restype = S
         L.qdec_gemv_q8_a8.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _P, Z, _P]
         L.qdec_gemv_q8_a8.restype = S
@@ -175,6 +177,7 @@ def lib():
 EXPORTED = [
     "qdec_last_error", "qdec_version", "qdec_packed_weight_bytes", "qdec_packed_scale_bytes",
     "qdec_pack_q8", "qdec_pack_q4", "qdec_gemv_workspace_bytes", "qdec_gemv_q8", "qdec_gemv_q4",
+    "qdec_gemv_q4_noalloc",
     "qdec_quantize_act_i8", "qdec_gemv_q8_a8", "qdec_gemv_q4_a8", "qdec_sample_workspace_bytes", "qdec_sample",
     "qdec_gemm_workspace_bytes", "qdec_gemm_q8", "qdec_gemm_q4", "qdec_batch_workspace_bytes", "qdec_batch_create",
     "qdec_batch_decode_step", "qdec_batch_kernel_count", "qdec_batch_destroy", "qdec_prefill_workspace_bytes",
@@ -253,6 +256,16 @@ def gemv(wfmt: str, Wp, Sp, x, N: int, bias=None, residual=None, y=None, workspa
         st = lib().qdec_gemv_q4(_ptr(Wp), _ptr(Sp), group, _ptr(x), _ptr(bias), _ptr(residual), _ptr(y),
                                 N, K, ws, wsb, _stream(stream))
     _check(st, "qdec_gemv_" + wfmt)
+    return y
+
+
+def gemv_q4_noalloc(Wp, Sp, x, N: int, bias=None, residual=None, y=None, group: int = 64, stream=None):
+    """qdec_gemv_q4 without a workspace: the library's static per-GPU scratch holds the split-K state."""
+    K = x.numel()
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=x.device)
+    _check(lib().qdec_gemv_q4_noalloc(_ptr(Wp), _ptr(Sp), group, _ptr(x), _ptr(bias), _ptr(residual), _ptr(y), N, K,
+                                      _stream(stream)), "qdec_gemv_q4_noalloc")
     return y
 
 

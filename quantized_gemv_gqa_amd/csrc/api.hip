@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "qdec_batch.h"
 
@@ -29,6 +30,58 @@ qdec_status check_launch(const char *what) {
 }
 
 static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Scratch of qdec_gemv_q4_noalloc: the layout of a GEMV workspace (arrival counters, then split-K
+// partial sums) in a static device array, one copy per GPU for the life of the process.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not a device address):
+// it uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = kCounterBytes + 512 * 1024;  // 768 KiB: up to 2048 split units
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];
+
+// Device address of this GPU's scratch, looked up once per device with that device current.
+static qdec_status scratch_address(void **out, void *stream, const char *name) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("%s: hipGetDevice: %s", name, hipGetErrorString(e));
+    return QDEC_EHIP;
+  }
+  QDEC_REQUIRE(dev >= 0 && dev < kMaxDevices, QDEC_EUNSUPPORTED, "%s: device %d is beyond the %d devices supported",
+               name, dev, kMaxDevices);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) {
+      set_error("%s: hipStreamGetDevice: %s", name, hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    QDEC_REQUIRE(sdev == dev, QDEC_EINVAL, "%s: the stream belongs to device %d, the current device is %d", name,
+                 sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_error("%s: hipGetSymbolAddress(scratch) on device %d: %s", name, dev, hipGetErrorString(e));
+      return QDEC_EHIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return QDEC_OK;
+}
+
+// Zeroes the first `lines` arrival counters (one per 128-byte line).  A kernel, not a memset, so
+// that a captured graph replays it correctly.
+__global__ void clear_counter_lines(unsigned *counters, int lines) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < lines) counters[(size_t)i * kLine] = 0u;
+}
 
 }  // namespace qdec
 
@@ -88,9 +141,8 @@ size_t qdec_gemv_workspace_bytes(int wfmt, int N, int K) {
   return gemv_workspace_bytes(wfmt, N, K);
 }
 
-static qdec_status gemv_common(int wfmt, const void *Wp, const void *Sp, int group, const float *x,
-                               const float *bias, const float *residual, float *y, int N, int K,
-                               void *ws, size_t ws_bytes, void *stream, const char *name) {
+static qdec_status gemv_check(int wfmt, const void *Wp, const void *Sp, int group, const float *x, const float *y,
+                              int N, int K, const char *name) {
   QDEC_REQUIRE(Wp && Sp && x && y, QDEC_EINVAL, "%s: null pointer", name);
   QDEC_REQUIRE(N >= 1 && K >= 1, QDEC_EINVAL, "%s: N and K must be >= 1 (N=%d K=%d)", name, N, K);
   if (wfmt == QDEC_W_Q8_ROW) {
@@ -104,14 +156,12 @@ static qdec_status gemv_common(int wfmt, const void *Wp, const void *Sp, int gro
   QDEC_REQUIRE(aligned(Wp, 16) && aligned(x, 16) && aligned(y, 4), QDEC_EINVAL,
                "%s: packed weights and x must be 16-byte aligned", name);
   QDEC_REQUIRE(x != y && !(x < y + N && y < x + K), QDEC_EINVAL, "%s: x must not overlap y", name);
-  const bool split = ws != nullptr;
-  if (split) {
-    QDEC_REQUIRE(aligned(ws, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", name);
-    QDEC_REQUIRE(ws_bytes >= gemv_workspace_bytes(wfmt, N, K), QDEC_EINVAL,
-                 "%s: workspace too small (%zu < %zu bytes)", name, ws_bytes,
-                 gemv_workspace_bytes(wfmt, N, K));
-  }
-  GemvPlan p = gemv_plan(wfmt, N, K, split);
+  return QDEC_OK;
+}
+
+static qdec_status gemv_launch(int wfmt, const void *Wp, const void *Sp, int group, const float *x,
+                               const float *bias, const float *residual, float *y, int N, int K,
+                               const GemvPlan &p, void *ws, void *stream, const char *name) {
   GemvArgs a{};
   a.W = reinterpret_cast<const uint8_t *>(Wp);
   a.S = Sp;
@@ -128,6 +178,22 @@ static qdec_status gemv_common(int wfmt, const void *Wp, const void *Sp, int gro
   return QDEC_OK;
 }
 
+static qdec_status gemv_common(int wfmt, const void *Wp, const void *Sp, int group, const float *x,
+                               const float *bias, const float *residual, float *y, int N, int K,
+                               void *ws, size_t ws_bytes, void *stream, const char *name) {
+  const qdec_status c = gemv_check(wfmt, Wp, Sp, group, x, y, N, K, name);
+  if (c != QDEC_OK) return c;
+  const bool split = ws != nullptr;
+  if (split) {
+    QDEC_REQUIRE(aligned(ws, 256), QDEC_EINVAL, "%s: workspace must be 256-byte aligned", name);
+    QDEC_REQUIRE(ws_bytes >= gemv_workspace_bytes(wfmt, N, K), QDEC_EINVAL,
+                 "%s: workspace too small (%zu < %zu bytes)", name, ws_bytes,
+                 gemv_workspace_bytes(wfmt, N, K));
+  }
+  return gemv_launch(wfmt, Wp, Sp, group, x, bias, residual, y, N, K, gemv_plan(wfmt, N, K, split), ws, stream,
+                     name);
+}
+
 qdec_status qdec_gemv_q8(const void *Wp, const float *Sp, const float *x, const float *bias,
                          const float *residual, float *y, int N, int K, void *workspace,
                          size_t workspace_bytes, void *stream) {
@@ -140,6 +206,29 @@ qdec_status qdec_gemv_q4(const void *Wp, const uint16_t *Sp, int group, const fl
                          void *workspace, size_t workspace_bytes, void *stream) {
   return gemv_common(QDEC_W_Q4_G_ZP8, Wp, Sp, group, x, bias, residual, y, N, K, workspace,
                      workspace_bytes, stream, "qdec_gemv_q4");
+}
+
+qdec_status qdec_gemv_q4_noalloc(const void *Wp, const uint16_t *Sp, int group, const float *x, const float *bias,
+                                 const float *residual, float *y, int N, int K, void *stream) {
+  const char *name = "qdec_gemv_q4_noalloc";
+  const qdec_status c = gemv_check(QDEC_W_Q4_G_ZP8, Wp, Sp, group, x, y, N, K, name);
+  if (c != QDEC_OK) return c;
+  const size_t need = gemv_workspace_bytes(QDEC_W_Q4_G_ZP8, N, K);
+  QDEC_REQUIRE(need <= kNoAllocScratchBytes, QDEC_EINVAL,
+               "%s: N=%d K=%d needs %zu bytes of scratch, more than the library's static %zu bytes "
+               "(use qdec_gemv_q4 with a workspace)",
+               name, N, K, need, kNoAllocScratchBytes);
+  void *ws = nullptr;
+  const qdec_status sa = scratch_address(&ws, stream, name);
+  if (sa != QDEC_OK) return sa;
+  const GemvPlan p = gemv_plan(QDEC_W_Q4_G_ZP8, N, K, true);
+  if (p.ks > 1) {  // the counters a split launch uses start at zero whatever an earlier call left
+    hipLaunchKernelGGL(clear_counter_lines, dim3((p.tiles + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<unsigned *>(ws), p.tiles);
+    const qdec_status lc = check_launch(name);
+    if (lc != QDEC_OK) return lc;
+  }
+  return gemv_launch(QDEC_W_Q4_G_ZP8, Wp, Sp, group, x, bias, residual, y, N, K, p, ws, stream, name);
 }
 
 static bool pow2_group(int group) { return group >= 32 && group <= 4096 && (group & (group - 1)) == 0; }

@@ -168,6 +168,7 @@ def lib():
         L.qdec_step_kernel_times.argtypes = [_P, _I, _P, _I, _P]; L.qdec_step_kernel_times.restype = _I
         L.qdec_step_layer_blocks.argtypes = [_P]; L.qdec_step_layer_blocks.restype = _I
         L.qdec_step_layer_timeline.argtypes = [_P, _P]; L.qdec_step_layer_timeline.restype = S
+        L.qdec_step_mlp_timeline.argtypes = [_P, _P, ctypes.POINTER(_I)]; L.qdec_step_mlp_timeline.restype = S
         L.qdec_step_destroy.argtypes = [_P]; L.qdec_step_destroy.restype = None
         L.qdec_step_read_error.argtypes = [_P, ctypes.POINTER(_I)]; L.qdec_step_read_error.restype = S
         _lib = L
@@ -184,7 +185,7 @@ EXPORTED = [
     "qdec_prefill", "qdec_gemm_mfma",
     "qdec_rmsnorm_rope", "qdec_swiglu", "qdec_argmax", "qdec_stream_read", "qdec_attn_workspace_bytes",
     "qdec_attn_decode_paged", "qdec_step_workspace_bytes", "qdec_step_create", "qdec_decode_step",
-    "qdec_step_kernel_count", "qdec_step_kernel_times", "qdec_step_layer_blocks", "qdec_step_layer_timeline", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_read_error",
+    "qdec_step_kernel_count", "qdec_step_kernel_times", "qdec_step_layer_blocks", "qdec_step_layer_timeline", "qdec_step_mlp_timeline", "qdec_step_set_sampling", "qdec_step_destroy", "qdec_step_read_error",
 ]
 
 
@@ -669,6 +670,19 @@ class DecodeStep:
         (int64 device tensor [n_layers][blocks][8][16], zeroed by the caller); None stops."""
         _check(lib().qdec_step_layer_timeline(self.handle, _ptr(ts)), "qdec_step_layer_timeline")
         self._tl = ts
+
+    def mlp_units(self):
+        """(gate/up units, down units): wave jobs of the two MLP GEMV launches of a layer."""
+        u = (_I * 2)()
+        _check(lib().qdec_step_mlp_timeline(self.handle, None, u), "qdec_step_mlp_timeline")
+        return int(u[0]), int(u[1])
+
+    def mlp_timeline(self, ts=None):
+        """Record per-unit clock marks of the gate/up and down launches of later steps into `ts`
+        (int64 device tensor [n_layers][gate/up units + down units][8], zeroed by the caller);
+        None stops."""
+        _check(lib().qdec_step_mlp_timeline(self.handle, _ptr(ts), None), "qdec_step_mlp_timeline")
+        self._mtl = ts
 
     def read_error(self) -> int:
         """The step's device error flag (a bounded wait gave up), cleared after reading."""

@@ -22,6 +22,7 @@
 // INT8 codes are biased to unsigned by XOR 0x80 (c + 128) and folded the same way.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 
 #include "qdec_device.h"
@@ -40,13 +41,21 @@ constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
 
 // Standalone launch: one wave per (tile, k-split) unit, no cross-phase dependency.
 template <int FMT, bool NORM, int EPI>
-__global__ void __launch_bounds__(256) gemv_tile64(const GemvArgs a) {
-  __shared__ Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> stage_all[4][2];
+__global__ void __launch_bounds__(64 * kMaxGemvWaves) gemv_tile64(const GemvArgs a) {
+  __shared__ Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> stage_all[kMaxGemvWaves][2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * 4 + wave;
+  const int unit = wave * gridDim.x + blockIdx.x;
   if (unit >= ((a.N + kTile - 1) / kTile) * a.ks) return;  // whole wave
-  gemv_unit<FMT, NORM, EPI, kSyncNone>(a, unit, stage_all[wave], lane);
+  // optional timeline, per unit: entry, loads issued, computed, combined (the tile's last wave),
+  // exit (slots 0, 1, 3, 4, 5)
+  unsigned long long *rec = a.timeline ? a.timeline + (size_t)unit * 8 : nullptr;
+  mark(rec, 0);
+  GemvUnit<FMT, NORM, EPI, kSyncNone> u;
+  u.start(a, unit, lane);
+  mark(rec, 1);
+  u.finish(a, stage_all[wave], lane, nullptr, rec ? rec + 2 : nullptr);
+  mark(rec, 5);
 }
 
 template <int FMT>
@@ -92,7 +101,7 @@ template <int FMT, bool NORM, int EPI>
 hipError_t launch_t(const GemvArgs &a0, const GemvPlan &p, hipStream_t st) {
   GemvArgs a = a0;
   gemv_apply_plan(a, p, FMT);
-  hipLaunchKernelGGL((gemv_tile64<FMT, NORM, EPI>), dim3(p.blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((gemv_tile64<FMT, NORM, EPI>), dim3(p.blocks), dim3(64 * p.wpb), 0, st, a);
   return hipGetLastError();
 }
 
@@ -130,8 +139,13 @@ GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split) {
   p.cps = (p.nch + ks - 1) / ks;
   p.ks = (p.nch + p.cps - 1) / p.cps;
   p.units = p.tiles * p.ks;
-  p.blocks = (p.units + 3) / 4;
+  gemv_set_grid(p);
   return p;
+}
+
+void gemv_set_grid(GemvPlan &p) {
+  p.wpb = std::max(1, std::min(kMaxGemvWaves, (p.units + kComputeUnits - 1) / kComputeUnits));
+  p.blocks = (p.units + p.wpb - 1) / p.wpb;
 }
 
 // Workspace layout, shared by every GEMV that runs on it one after another: the arrival counters

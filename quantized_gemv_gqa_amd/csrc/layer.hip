@@ -5,14 +5,15 @@
 // the same split of the work, so results are equal bit for bit); what changes is when.
 //
 // One workgroup of 8 waves per compute unit, and every workgroup takes part in every phase:
-//   wave w of workgroup b holds qkv GEMV unit 8 b + w, o GEMV unit 8 (nblk - 1 - b) + w, and the
+//   wave w of workgroup b holds qkv GEMV unit w nblk + b and o GEMV unit (7 - w) nblk + b (units
+//   dealt over the workgroups first, so each compute unit streams an equal share), and the
 //   workgroup as a whole holds attention unit (KV head b / splits, split b % splits) if b is
 //   below Hkv * splits.
-// Before it waits for anything, a workgroup requests all of its HBM bytes: its qkv weights (into
-// registers, computed first), its first KV page (registers) and its o weights, which are copied
-// straight from HBM into an LDS stash and need no registers while the attention runs.  So the
-// whole launch's 24 MB (at the Qwen2.5-7B shape) stream at once instead of phase by phase, and
-// what remains are the hand-offs:
+// A wave first streams and computes its qkv unit; then, before it waits for anything, it
+// requests the rest of its HBM bytes: its first KV page (registers) and its o weights, which are
+// copied straight from HBM into an LDS stash and need no registers while the attention runs.  So
+// the qkv weights stream alone, the later phases' bytes land during the waits, and what remains
+// are the hand-offs:
 //   * attention unit (j, s) waits until the 2G + 4 qkv tiles of KV head j (its G q heads, its k
 //     and v) are stored, counted per head;
 //   * an o GEMV unit waits for the attention outputs of the KV heads whose query heads cover its
@@ -40,6 +41,8 @@ namespace {
 using namespace dev;
 
 constexpr int kAttnLayerWaves = attn::kAttnWaves;  // 8 waves: attention units need a whole workgroup
+// o units go to the waves that do not stage the attention's inputs when they fit there
+constexpr int kOWaves = kAttnLayerWaves - attn::AttnUnit<128, 4, QDEC_KV_BF16, true, true>::kRopeWaves;
 
 __device__ __forceinline__ int gemv_units(const GemvArgs &g) { return ((g.N + kTile - 1) / kTile) * g.ks; }
 
@@ -55,10 +58,14 @@ __global__ void __launch_bounds__(attn::kAttnThreads) attn_layer_k(const LayerAr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
-  const int uq = b * kAttnLayerWaves + wave;
-  const int uo = (a.nblk - 1 - b) * kAttnLayerWaves + wave;
-  const bool q_role = uq < gemv_units(a.qkv);
-  const bool o_role = uo < gemv_units(a.o);
+  // GEMV units are dealt over the workgroups first: qkv unit w nblk + b to wave w, o unit
+  // w nblk + b to wave 7 - w, o on the last o_waves waves (4 when they suffice: then the
+  // attention's staging waves keep no stash copies in flight)
+  const int nq = gemv_units(a.qkv), no = gemv_units(a.o);
+  const int uq = wave * a.nblk + b;
+  const int uo = (kAttnLayerWaves - 1 - wave) * a.nblk + b;
+  const bool q_role = uq < nq;
+  const bool o_role = wave >= kAttnLayerWaves - a.o_waves && uo < no;
   const bool at_role = b < a.at.Hkv * a.at.splits;  // the same for the whole workgroup
   const int j = b / a.at.splits, s = b - j * a.at.splits;
 
@@ -67,15 +74,19 @@ __global__ void __launch_bounds__(attn::kAttnThreads) attn_layer_k(const LayerAr
   GemvUnit<FMT, false, EPI_STORE, kSyncConsumer, true> go;
   // optional timeline: per wave 16 marks (clock at entry, loads issued, qkv computed / combined /
   // stored, attention wait done / pages done / published / merged, o wait done / computed /
-  // combined / stored)
+  // combined, exit, attention q staged / heads rotated)
   unsigned long long *rec = a.timeline ? a.timeline + ((size_t)b * kAttnLayerWaves + wave) * 16 : nullptr;
   mark(rec, 0);
-  if (q_role) gq.start(a.qkv, uq, lane);
+  if (q_role) {
+    gq.start(a.qkv, uq, lane);
+    mark(rec, 1);
+    gq.finish(a.qkv, sm.st[wave], lane, nullptr, rec ? rec + 2 : nullptr);
+  }
+  mark(rec, 5);
+  // The later phases' bytes are requested once the wave's qkv unit is done, so the qkv weights,
+  // on the critical path, do not share HBM with them; they land while the attention waits.
   if (at_role) at.start(a.at, j, s);
   if (o_role) go.start(a.o, uo, lane, stash[wave]);
-  mark(rec, 1);
-  if (q_role) gq.finish(a.qkv, sm.st[wave], lane, nullptr, rec ? rec + 2 : nullptr);
-  mark(rec, 5);
   // (the attention's first LDS write follows a workgroup barrier, so every wave is past its
   // qkv unit's use of the union by then)
   if (at_role) at.finish(a.at, j, s, sm.at, rec ? rec + 6 : nullptr);
@@ -110,6 +121,8 @@ const void *layer_kernel(int wfmt, int kv_fmt, int G) {
 bool layer_fusion_supported(int G, int D) { return D == 128 && (G == 4 || G == 6 || G == 7 || G == 8); }
 
 int attn_layer_waves() { return kAttnLayerWaves; }
+
+int attn_layer_o_waves() { return kOWaves; }  // preferred; all waves when the o plan needs them
 
 int attn_layer_stash_runs() { return kStashRuns; }
 

@@ -166,8 +166,8 @@ struct AttnSmem {
 
 // One (KV head j, split s) attention unit, run by a whole workgroup of kAttnThreads threads.
 // SYNC: the step-synchronised form of the fused layer kernels (AttnArgs: epoch, wait_cnt, done).
-// start() requests the wave's first KV page (nothing else happens before it); finish() does the
-// rest, so a kernel can issue other roles' loads, or compute, between the two.
+// start() requests the RoPE table and the wave's first KV page (nothing else happens before it);
+// finish() does the rest, so a kernel can issue other roles' loads, or compute, between the two.
 template <int D, int G, int KVF, bool ROPE, bool SYNC>
 struct AttnUnit {
   static constexpr int DPL = D / 16;
@@ -176,10 +176,15 @@ struct AttnUnit {
   // (A second page buffer spilled registers of the 7-query-head unit and was slower at every
   // context and batch measured.)
   static constexpr int PF = 1;
+  // Waves 0 .. kRopeWaves - 1 stage the q, k, v rows and norm + rotate the heads; the others may
+  // carry long-running loads of other roles (which in-order memory counters would make these
+  // steps wait for).
+  static constexpr int kRopeWaves = 4;
   int pos, T, P, nwt, gw, last_page;
   __amdgpu_buffer_rsrc_t kr, vr;
   Row<D, KVF> kp[PF][4], vp[PF][4];
   bool have[PF];
+  double cs[ROPE ? 2 * DPL : 1];  // fp64 (cos, sin) of the lane's rotation pairs
 
   __device__ __forceinline__ void start(const AttnArgs &a, int j, int s) {
     const int lane = threadIdx.x & 63;
@@ -189,11 +194,20 @@ struct AttnUnit {
     pos = *a.pos;
     T = pos + 1;
     P = max(0, min((T + 15) >> 4, a.n_pages));  // never index outside the page table
-    // pages are dealt round-robin over all NW * splits waves of the KV head: wave gw = NW s + wave
-    // takes pages gw, gw + nwt, gw + 2 nwt, ...
+    // pages are dealt round-robin over all NW * splits waves of the KV head, splits first: wave
+    // gw = s + splits * wave takes pages gw, gw + nwt, gw + 2 nwt, ...  So every split gets a
+    // page before any split gets a second one, and the waves of a workgroup that hold pages are
+    // the first ones (one per SIMD while a workgroup holds at most four pages).
     nwt = NW * a.splits;
-    gw = NW * s + wave;
+    gw = s + a.splits * wave;
     last_page = ((T + 15) >> 4) - 1;
+    if constexpr (ROPE) {
+      if (wave < kRopeWaves) {
+        const int i0 = (part * DPL) % (D / 2);
+#pragma unroll
+        for (int e = 0; e < 2 * DPL; ++e) cs[e] = a.rope_cs[2 * i0 + e];
+      }
+    }
     const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
     kr = rsrc(a.k_pool, pool_bytes);
     vr = rsrc(a.v_pool, pool_bytes);
@@ -249,43 +263,49 @@ struct AttnUnit {
   float q[G][DPL];
   Row<D, KVF> knew, vnew;
   if constexpr (ROPE) {
-    // stage this KV head's q heads and its new k, v (one pass), then norm + rotate per lane
+    // stage this KV head's q heads and its new k, v (one pass); then wave h norms and rotates
+    // head h (q heads, then k) in place, once per workgroup; then every lane reads its dims
     const __amdgpu_buffer_rsrc_t qr = rsrc(a.qkv, (uint32_t)((a.Hq + 2 * a.Hkv) * D * 4));
-    for (int i = threadIdx.x; i < (G + 2) * D / 4; i += kAttnThreads) {
-      const int h = (i * 4) / D, d = i * 4 - h * D;
-      const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
-      *reinterpret_cast<f32x4 *>(&sq[h * D + d]) = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, (uint32_t)((row * D + d) * 4), 0, SYNC ? kAuxSc1 : 0));
-    }
-    double cs[2 * DPL];
-    {
-      const int i0 = (part * DPL) % (D / 2);
-#pragma unroll
-      for (int e = 0; e < 2 * DPL; ++e) cs[e] = a.rope_cs[2 * i0 + e];
+    if (wave < kRopeWaves) {
+      for (int i = threadIdx.x; i < (G + 2) * D / 4; i += 64 * kRopeWaves) {
+        const int h = (i * 4) / D, d = i * 4 - h * D;
+        const int row = h < G ? (j * G + h) : (h == G ? a.Hq + j : a.Hq + a.Hkv + j);
+        *reinterpret_cast<f32x4 *>(&sq[h * D + d]) = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, (uint32_t)((row * D + d) * 4), 0, SYNC ? kAuxSc1 : 0));
+      }
     }
     __syncthreads();
+    mark(rec, 8);
     const int dmate = part * DPL < D / 2 ? part * DPL + D / 2 : part * DPL - D / 2;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = wave; wave < kRopeWaves && h < G + 1; h += kRopeWaves) {
       float own[DPL], mate[DPL];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         own[e] = sq[h * D + part * DPL + e];
         mate[e] = sq[h * D + dmate + e];
       }
-      norm_rope<D>(own, mate, part, a.g_q, a.eps, cs);
+      norm_rope<D>(own, mate, part, h < G ? a.g_q : a.g_k, a.eps, cs);
+      // (the wave's reads above all precede its writes; the four token slots hold copies)
+      if (slot == 0) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) q[h][e] = own[e] * a.scale_log2;
+        for (int e = 0; e < DPL; ++e) sq[h * D + part * DPL + e] = own[e];
+      }
     }
-    float own[DPL], mate[DPL], vv[DPL];
+    __syncthreads();
+    mark(rec, 9);
+    if (gw < P) {  // (waves without a page need no q)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) q[h][e] = sq[h * D + part * DPL + e] * a.scale_log2;
+    }
+    float kk[DPL], vv[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-      own[e] = sq[G * D + part * DPL + e];
-      mate[e] = sq[G * D + dmate + e];
+      kk[e] = sq[G * D + part * DPL + e];
       vv[e] = sq[(G + 1) * D + part * DPL + e];
     }
-    norm_rope<D>(own, mate, part, a.g_k, a.eps, cs);
-    knew.set(own);
+    knew.set(kk);
     vnew.set(vv);
     // split 0 appends them for later steps (every split uses the register copy for this token).
     // A token without a cache slot (pos < 0, past the page table, or an unmapped entry) is not
@@ -411,7 +431,9 @@ struct AttnUnit {
     const u32x2 v = {__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)};
     __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + h) * 2) * 4), 0, kAuxSc1);
   }
-  drain_stores();  // this thread's partial stores are acknowledged
+  // the waves that stored wait for the acknowledgements (one counter covers loads and stores, so
+  // a wave holding other roles' loads in flight would wait for those too)
+  if (wave * 64 < C || wave * 64 < G) drain_stores();
   __syncthreads();
   if (threadIdx.x == 0)
     last = __hip_atomic_fetch_add(&a.counters[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==

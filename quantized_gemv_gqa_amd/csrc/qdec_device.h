@@ -681,13 +681,5 @@ struct GemvUnit {
   }
 };
 
-template <int FMT, bool NORM, int EPI, int SYNC = kSyncNone, int PF = 2>
-__device__ __forceinline__ void gemv_unit(const GemvArgs &a, int unit, Stage<(FMT == QDEC_W_Q4_G_ZP8) ? 32 : 16> (&sm)[2],
-                                          int lane) {
-  GemvUnit<FMT, NORM, EPI, SYNC, false, PF> u;
-  u.start(a, unit, lane);
-  u.finish(a, sm, lane);
-}
-
 }  // namespace dev
 }  // namespace qdec

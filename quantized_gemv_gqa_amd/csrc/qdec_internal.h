@@ -59,6 +59,7 @@ struct GemvArgs {
   unsigned *done;
   int Hq, Hkv, hd;
   unsigned *err;  // set on a wait that times out
+  unsigned long long *timeline;  // diagnostics: 8 clock marks per unit of a plain launch, or null
 };
 // Device atomics to one cache line serialize (about 13 ns each on MI355X), so every arrival
 // counter sits on a 128-byte line of its own.
@@ -70,10 +71,16 @@ constexpr int kArgGroupLine0 = kCounterLines - kArgGroups;
 constexpr int kArgTopLine = kArgGroupLine0 - 1;
 constexpr int kMaxSplitTiles = kArgTopLine;      // tiles 0 .. kMaxSplitTiles-1 own lines 0 ..
 
+// A plain GEMV launch deals its units over the workgroups first (unit w * blocks + b to wave w
+// of workgroup b), with at most one workgroup per compute unit, so every compute unit streams an
+// equal share.
+constexpr int kComputeUnits = 256;  // MI355X
+constexpr int kMaxGemvWaves = 16;   // waves per workgroup (1024 threads)
 struct GemvPlan {
-  int tiles, nch, ks, cps, units, blocks;
+  int tiles, nch, ks, cps, units, blocks, wpb;  // wpb: waves per workgroup
 };
 GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split);
+void gemv_set_grid(GemvPlan &p);  // blocks and waves per workgroup of a plain launch
 // Copy the plan into the arguments a kernel reads (k-splits, runs per split, INT4 group as a
 // shift): every launch path calls it once, after the arguments are filled.
 void gemv_apply_plan(GemvArgs &a, const GemvPlan &p, int wfmt);
@@ -158,10 +165,12 @@ struct LayerArgs {
   GemvArgs qkv, o;
   AttnArgs at;
   int nblk;
+  int o_waves;  // waves per workgroup holding o units (the last ones)
   unsigned long long *timeline;  // diagnostics: [nblk * waves][16] clock marks, or null
 };
 bool layer_fusion_supported(int G, int D);
 int attn_layer_waves();
+int attn_layer_o_waves();  // waves per workgroup that hold o GEMV units
 int attn_layer_stash_runs();
 int attn_layer_blocks_per_cu(int wfmt, int kv_fmt, int G);  // 0: the kernel does not fit a CU
 hipError_t launch_attn_layer(const LayerArgs &a, int wfmt, hipStream_t st);

@@ -35,7 +35,9 @@ struct qdec_step {
   void *gemv_ws = nullptr;
   qdec::GemvPlan p_qkv, p_o, p_gu, p_down, p_lm;
   int nblk = 0;    // workgroups of the fused attention launch (one per compute unit)
+  int o_waves = 0;  // its waves per workgroup that hold o units
   unsigned long long *timeline = nullptr;  // diagnostics: per-wave clock marks of the fused launches
+  unsigned long long *mlp_timeline = nullptr;  // diagnostics: per-unit clock marks of gate/up and down
   int splits = 1;  // attention splits per KV head in use (the config's, capped for the fused launch)
   int ssq_n = 0;
   hipGraph_t graph[2] = {nullptr, nullptr};      // [per-op]: captured step
@@ -82,7 +84,7 @@ GemvPlan layer_plan(int wfmt, int N, int K, int waves, int max_cps) {
     p.cps = (p.nch + ks - 1) / ks;
     p.ks = (p.nch + p.cps - 1) / p.cps;
     p.units = p.tiles * p.ks;
-    p.blocks = (p.units + 3) / 4;
+    gemv_set_grid(p);
     return p;
   }
   p.units = 0;
@@ -174,6 +176,25 @@ GemvArgs gemv_args(const qdec_step *h, const void *W, const void *S, const float
   return a;
 }
 
+// The MLP timeline records of layer l: gate/up units, then down units, 8 marks each.
+unsigned long long *mlp_rec(const qdec_step *h, int l, bool down) {
+  if (!h->mlp_timeline) return nullptr;
+  const size_t per_layer = (size_t)(h->p_gu.units + h->p_down.units) * 8;
+  return h->mlp_timeline + l * per_layer + (down ? (size_t)h->p_gu.units * 8 : 0);
+}
+
+// Captured graphs hold the launch list with its arguments: a change of those drops them (the
+// next GRAPH call captures again).
+void drop_graphs(qdec_step *h) {
+  for (int v = 0; v < 2; ++v) {
+    if (h->exec[v]) (void)hipGraphExecDestroy(h->exec[v]);
+    if (h->graph[v]) (void)hipGraphDestroy(h->graph[v]);
+    h->exec[v] = nullptr;
+    h->graph[v] = nullptr;
+    h->graph_stream[v] = nullptr;
+  }
+}
+
 // Records the next timing event after a launch while qdec_step_kernel_times runs a step.
 void step_mark(qdec_step *h, hipStream_t st) {
   if (h->timing && h->tev_n < h->tev.size()) (void)hipEventRecord(h->tev[h->tev_n++], st);
@@ -258,6 +279,7 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   gemv_apply_plan(la.qkv, h->p_qkv, c.wfmt);
   gemv_apply_plan(la.o, h->p_o, c.wfmt);
   la.nblk = h->nblk;
+  la.o_waves = h->o_waves;
   la.timeline = h->timeline ? h->timeline + (size_t)l * h->nblk * attn_layer_waves() * 16 : nullptr;
   hipError_t e = launch_attn_layer(la, c.wfmt, st);
   if (e != hipSuccess) return e;
@@ -268,12 +290,14 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   g.gamma = w.g_ffn;
   g.ssq = h->ssqB;
   g.epi = EPI_SWIGLU;
+  g.timeline = mlp_rec(h, l, false);
   e = launch_gemv(c.wfmt, g, h->p_gu, st);
   if (e != hipSuccess) return e;
   step_mark(h, st);
   GemvArgs d = gemv_args(h, w.w_down, w.s_down, h->mlp, hA, H, I, h->p_down);
   d.residual = h->hB;
   d.ssq_out = h->ssq;
+  d.timeline = mlp_rec(h, l, true);
   return launch_gemv(c.wfmt, d, h->p_down, st);
 }
 
@@ -334,10 +358,12 @@ qdec_status enqueue_step(qdec_step *h, hipStream_t st, int *count, bool per_op) 
     GemvArgs g = gemv_args(h, w.w_gu, w.s_gu, s.hidden, h->mlp, 2 * I, H, h->p_gu);
     g.gamma = w.g_ffn;
     g.epi = EPI_SWIGLU;
+    g.timeline = mlp_rec(h, l, false);
     QDEC_CK(launch_gemv(wf, g, h->p_gu, st));
     GemvArgs d = gemv_args(h, w.w_down, w.s_down, h->mlp, s.hidden, H, I, h->p_down);
     d.residual = s.hidden;
     d.ssq_out = h->ssq;
+    d.timeline = mlp_rec(h, l, true);
     QDEC_CK(launch_gemv(wf, d, h->p_down, st));
     if (s.trace) QDEC_CK(launch_copy(s.hidden, s.trace + (size_t)(l + 1) * H, H, st));
   }
@@ -646,11 +672,17 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
       const int nblk = std::min(cus, kMaxLayerBlocks);
       const int waves = nblk * attn_layer_waves();
       const GemvPlan pq = layer_plan(cfg->wfmt, nqkv, cfg->hidden, waves, 1 << 30);
-      const GemvPlan po = layer_plan(cfg->wfmt, cfg->hidden, qd, waves, attn_layer_stash_runs());
+      int ow = attn_layer_o_waves();
+      GemvPlan po = layer_plan(cfg->wfmt, cfg->hidden, qd, nblk * ow, attn_layer_stash_runs());
+      if (po.units == 0) {
+        ow = attn_layer_waves();
+        po = layer_plan(cfg->wfmt, cfg->hidden, qd, nblk * ow, attn_layer_stash_runs());
+      }
       const int S = std::min(cfg->num_splits, nblk / cfg->n_kv_heads);
       if (pq.units > 0 && po.units > 0 && S >= 1) {
         h->layer_ok = true;
         h->nblk = nblk;
+        h->o_waves = ow;
         h->p_qkv = pq;
         h->p_o = po;
         h->splits = S;
@@ -771,19 +803,9 @@ qdec_status qdec_step_set_sampling(qdec_step *h, float temperature, int top_k, f
   h->top_k = top_k;
   h->top_p = top_p;
   h->seed = seed;
-  // captured graphs hold the old launch list: drop them (the next GRAPH call captures again)
-  for (int v = 0; v < 2; ++v) {
-    if (h->exec[v]) (void)hipGraphExecDestroy(h->exec[v]);
-    if (h->graph[v]) (void)hipGraphDestroy(h->graph[v]);
-    h->exec[v] = nullptr;
-    h->graph[v] = nullptr;
-    h->graph_stream[v] = nullptr;
-  }
+  drop_graphs(h);
   return QDEC_OK;
 }
-
-
-
 
 
 int qdec_step_layer_blocks(const qdec_step *h) { return h && h->layer_ok ? h->nblk : 0; }
@@ -792,6 +814,18 @@ qdec_status qdec_step_layer_timeline(qdec_step *h, uint64_t *ts) {
   QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_layer_timeline: null handle");
   QDEC_REQUIRE(!ts || h->layer_ok, QDEC_EUNSUPPORTED, "qdec_step_layer_timeline: this step has no fused attention launch");
   h->timeline = reinterpret_cast<unsigned long long *>(ts);
+  drop_graphs(h);
+  return QDEC_OK;
+}
+
+qdec_status qdec_step_mlp_timeline(qdec_step *h, uint64_t *ts, int *units) {
+  QDEC_REQUIRE(h, QDEC_EINVAL, "qdec_step_mlp_timeline: null handle");
+  if (units) {
+    units[0] = h->p_gu.units;
+    units[1] = h->p_down.units;
+  }
+  h->mlp_timeline = reinterpret_cast<unsigned long long *>(ts);
+  drop_graphs(h);
   return QDEC_OK;
 }
 

@@ -150,6 +150,7 @@ def test_layer_kernels_equal_per_op_bitwise(name):
     for mode in (q.STEP_GRAPH, q.STEP_GRAPH | q.STEP_PER_OP):
         dk = q.upload_kv(kv, wl.kv_fmt)
         st = q.DecodeStep(dm, dk, pos0=30, token0=model["token"], trace=True, num_splits=2)
+        assert st.layer_blocks > 0, "this shape must get the fused attention launch"
         res = []
         with torch.cuda.stream(torch.cuda.Stream()):
             for _ in range(3):
@@ -161,6 +162,22 @@ def test_layer_kernels_equal_per_op_bitwise(name):
         st.close()
     for a, b in zip(outs[q.STEP_GRAPH], outs[q.STEP_GRAPH | q.STEP_PER_OP]):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_fused_attention_launch_is_used_at_full_size(name):
+    """Every workload whose shape the fused attention launch supports (head dim 128, 4/6/7/8 q
+    heads per KV head) gets it at its full size and default splits: a plan that stops fitting
+    would otherwise fall back to per-op launches silently."""
+    wl = synth.WORKLOADS[name]
+    G = wl.n_heads // wl.n_kv_heads
+    model = synth.make_model(wl, n_layers=1)
+    kv = synth.make_kv(wl, 40, n_layers=1, ctx=30)
+    start = {"token0": model["token"]} if "token" in model else {"h0": model["h0"]}
+    st = q.DecodeStep(q.upload_model(model), q.upload_kv(kv, wl.kv_fmt), pos0=30, **start)
+    want = wl.head_dim == 128 and G in (4, 6, 7, 8)
+    assert (st.layer_blocks > 0) == want, (name, st.layer_blocks)
+    st.close()
 
 
 def test_step_errors_are_reported():

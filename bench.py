@@ -346,14 +346,16 @@ def per_kernel_roofline(wl, st, stream, reps: int):
     return out, total
 
 
-def stream_read_gbps(dev, stream, gib: float = 2.0, reps: int = 5):
-    """Plain streaming read of `gib` GiB (qdec_stream_read), HIP events around `reps` reads."""
+def stream_read_gbps(dev, stream, gib: float = 2.0, reps: int = 8, warm: int = 3):
+    """Plain streaming read of `gib` GiB (qdec_stream_read), HIP events around `reps` reads after
+    `warm` untimed ones (the first reads of a fresh buffer run up to 30 % slower)."""
     import quantized_gemv_gqa_amd as q
     buf = torch.empty(int(gib * (1 << 30)) // 16 * 4, dtype=torch.int32, device=dev)
     buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     with torch.cuda.stream(stream):
-        q.stream_read(buf, sink)
+        for _ in range(warm):
+            q.stream_read(buf, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):

@@ -16,15 +16,20 @@
 // are the hand-offs:
 //   * attention unit (j, s) waits until the 2G + 4 qkv tiles of KV head j (its G q heads, its k
 //     and v) are stored, counted per head;
-//   * an o GEMV unit waits for the attention outputs of the KV heads whose query heads cover its
-//     k-range (a flag per KV head, set by the split merge).
+//   * the splits publish their partials as (value, tag) pairs, one 8-byte store each, which a
+//     reader sees whole or not at all; query head j G + i is merged by split i of KV head j (all
+//     G heads in parallel), which polls the tags of every split's partial, so the splits neither
+//     wait for their stores to be acknowledged nor count themselves in;
+//   * the merged outputs go out as tagged pairs too, and an o GEMV unit polls the pairs of its
+//     k-range directly (no flag).  The tag is the step number times the layer count plus the
+//     layer, so a pair left by another layer or step never matches.
 // Producers never wait for consumers, and the grid is one workgroup per compute unit of a
 // kernel that fits once per unit, so all workgroups are resident together and every wait is
 // for a workgroup that is running.  Waits are bounded polls: a step whose producers do not
 // arrive in time sets the step's error word instead of hanging.
 //
-// Flags and counters are monotonic: the step number e (advanced by the embedding kernel at the
-// start of each step) is the target, so nothing has to be cleared between steps.  Data crossing
+// Counters and tags are monotonic: the step number e (advanced by the embedding kernel at the
+// start of each step) sets the target, so nothing has to be cleared between steps.  Data crossing
 // workgroups inside a launch uses device-coherent stores and loads (sc1), and a producer's
 // counter moves only after its stores are acknowledged.  The residual stream alternates between
 // two buffers (hA, read by the qkv GEMV and as o's residual, written by down; hB, written by o

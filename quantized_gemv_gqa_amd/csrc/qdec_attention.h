@@ -143,7 +143,6 @@ __device__ __forceinline__ void norm_rope(float (&own)[D / 16], float (&mate)[D 
 
 constexpr int kAttnWaves = 8;                  // waves per workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kMergeLoads = 20;  // partial outputs a merging thread loads per pass (G = 7, 8: 40 splits in one pass)
 
 __device__ __forceinline__ void store_sc1_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kAuxSc1);
@@ -158,8 +157,9 @@ struct AttnSmem {
   static constexpr int NW = kAttnWaves;
   static constexpr int C = G * D / 4;  // f32x4 columns of a split's partial output
   float m[NW][G], l[NW][G];
-  f32x4 o[NW * C];  // per-wave partial outputs, then the merge's per-thread sums
-  float w[kMaxMergeSplits][G], ls[kMaxMergeSplits][G];
+  // per-wave partial outputs, then a merged head's per-row sums (kAttnThreads of them)
+  f32x4 o[NW * C > kAttnThreads ? NW * C : kAttnThreads];
+  float w[kMaxMergeSplits], ls[kMaxMergeSplits];  // a merged head's split weights and sums
   float q[ROPE ? (G + 2) * D : 1];
   unsigned flag;
 };
@@ -235,12 +235,9 @@ struct AttnUnit {
   __device__ __forceinline__ void finish(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm,
                                         unsigned long long *rec = nullptr) {
   constexpr int C = G * D / 4;                                                // f32x4 columns
-  constexpr int R = (kAttnThreads / C) < NW ? (kAttnThreads / C) : NW;        // merge threads per column
   auto &sm_m = sm.m;
   auto &sm_l = sm.l;
   auto &sm_o = sm.o;
-  auto &sw = sm.w;
-  auto &sl = sm.ls;
   auto &sq = sm.q;
   unsigned &last = sm.flag;
   const int lane = threadIdx.x & 63;
@@ -403,13 +400,8 @@ struct AttnUnit {
     }
   }
   __syncthreads();
-  // merge the NW waves and publish the split's partial through device-coherent stores (the
-  // merging block may sit on another XCD): o at [s][head][D], (m, l) at [s][head][2]
-  float *wso = a.ws;
-  float *wsml = a.ws + (size_t)a.splits * a.Hq * D;
-  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
-  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
-  for (int c = threadIdx.x; c < C; c += kAttnThreads) {
+  // merge the NW waves into the split's partial: o (G heads x D) and per head (m, l)
+  auto column = [&](int c) {
     const int h = c / (D / 4);
     float mx = kNegBig;
 #pragma unroll
@@ -417,22 +409,65 @@ struct AttnUnit {
     f32x4 val = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) val += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_o[w * C + c];
-    store_sc1_b128(orr, (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 4), val);
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float mx = kNegBig;
+    return val;
+  };
+  auto head_ml = [&](int h, float &mx, float &lsum) {
+    mx = kNegBig;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
-    float lsum = 0.f;
+    lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) lsum += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_l[w][h];
+  };
+  if constexpr (SYNC) {
+    // Published as (value, tag) pairs, each pair one 8-byte store that a reader sees whole or not
+    // at all, so no counter is needed: the mergers poll the tags (tag: this step's number times
+    // the layer count plus the layer).  Pairs o at [s][head][D], then (m, tag, l, tag) at [s][head].
+    const unsigned tag = e * a.tag_mul + a.tag_add;
+    const __amdgpu_buffer_rsrc_t tor = rsrc(a.tws, (uint32_t)((size_t)a.splits * a.Hq * D * 8));
+    const __amdgpu_buffer_rsrc_t tmr = rsrc(a.tws + (size_t)a.splits * a.Hq * D * 2, (uint32_t)((size_t)a.splits * a.Hq * 16));
+    for (int c = threadIdx.x; c < C; c += kAttnThreads) {
+      const u32x4 vb = __builtin_bit_cast(u32x4, column(c));
+      const uint32_t off = (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 8);
+      u32x4 lo, hi;
+      lo.x = vb.x; lo.y = tag; lo.z = vb.y; lo.w = tag;
+      hi.x = vb.z; hi.y = tag; hi.z = vb.w; hi.w = tag;
+      __builtin_amdgcn_raw_buffer_store_b128(lo, tor, off, 0, kAuxSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, tor, off + 16, 0, kAuxSc1);
+    }
+    if (threadIdx.x < G) {
+      float mx, lsum;
+      head_ml(threadIdx.x, mx, lsum);
+      u32x4 v;
+      v.x = __builtin_bit_cast(uint32_t, mx); v.y = tag; v.z = __builtin_bit_cast(uint32_t, lsum); v.w = tag;
+      __builtin_amdgcn_raw_buffer_store_b128(v, tmr, (uint32_t)(((size_t)s * a.Hq + j * G + threadIdx.x) * 16), 0, kAuxSc1);
+    }
+    // every wave is done with this unit's LDS before any leaves (a kernel may reuse it next)
+    __syncthreads();
+    mark(rec, 2);
+    // query head j G + hh is merged by split hh % splits, as soon as its partials are all seen
+    // (its output goes out as tagged pairs too: the o GEMV polls them, no flag needed)
+    for (int hh = s; hh < G; hh += a.splits)
+      if (!merge_head<true>(a, j * G + hh, sm, tag)) return;
+    mark(rec, 3);
+    return;
+  }
+  // merge the NW waves and publish the split's partial through device-coherent stores (the
+  // merging block may sit on another XCD): o at [s][head][D], (m, l) at [s][head][2]
+  float *wso = a.ws;
+  float *wsml = a.ws + (size_t)a.splits * a.Hq * D;
+  const __amdgpu_buffer_rsrc_t orr = rsrc(wso, (uint32_t)((size_t)a.splits * a.Hq * D * 4));
+  const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
+  for (int c = threadIdx.x; c < C; c += kAttnThreads)
+    store_sc1_b128(orr, (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 4), column(c));
+  if (threadIdx.x < G) {
+    float mx, lsum;
+    head_ml(threadIdx.x, mx, lsum);
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 v = {__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)};
-    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + h) * 2) * 4), 0, kAuxSc1);
+    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + threadIdx.x) * 2) * 4), 0, kAuxSc1);
   }
-  // the waves that stored wait for the acknowledgements (one counter covers loads and stores, so
-  // a wave holding other roles' loads in flight would wait for those too)
+  // the waves that stored wait for the acknowledgements
   if (wave * 64 < C || wave * 64 < G) drain_stores();
   __syncthreads();
   if (threadIdx.x == 0)
@@ -441,88 +476,147 @@ struct AttnUnit {
   __syncthreads();
   mark(rec, 2);
   if (!last) return;
+  // the last split block of KV head j merges its G query heads, one after another
+  for (int hh = 0; hh < G; ++hh) merge_head<false>(a, j * G + hh, sm, 0u);
+  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  mark(rec, 3);
+  }
 
-  // The last split block of KV head j merges all splits of its G query heads:
-  //   out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
-  // Splits without keys carry m = -1e30, l = 0, o = 0 and get weight 0.  Every (m, l) pair and
-  // the first kMergeLoads partial outputs of each thread are requested in one burst; thread
-  // (r, c) takes column c of splits r, r + R, r + 2R, ...; one wave per query head reduces the
-  // maxima and sums in LDS.
-  const int t = threadIdx.x;
-  const int cc = t % C, rr = t / C;
-  const bool mt = rr < R;
-  const int hc = cc / (D / 4);
-  const int nml = a.splits * G;
-  constexpr int kMlLoads = (kMaxMergeSplits * 8 + kAttnThreads - 1) / kAttnThreads;
-  uint64_t mlv[kMlLoads];
+  // The merge of query head h's split partials:
+  //   out[h][d] = sum_s w_s o_s[d],  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s',  M = max_s m_s,
+  // splits without keys (m = -1e30, l = 0, o = 0) weighing nothing.  Fixed order whatever the
+  // caller: thread (r, c) adds column c (4 dims) of splits r, r + RH, r + 2 RH, ... in that order,
+  // then the RH rows are added in row order.  TAGGED (the fused launch): the partials are
+  // (value, tag) pairs, all requested at once and polled until every tag equals `tag`, and the
+  // output is stored as tagged pairs in tout; else plain values of a finished launch phase, and the
+  // output is stored in out.  Returns false if a poll gave up (the error word is then set).
+  template <bool TAGGED>
+  __device__ __forceinline__ bool merge_head(const AttnArgs &a, int h, AttnSmem<D, G, ROPE> &sm, unsigned tag) {
+    constexpr int CH = D / 4;                // f32x4 columns of one head
+    constexpr int RH = kAttnThreads / CH;    // split rows: 16 at D = 128, 32 at D = 64
+    constexpr int kBurst = 4;                // partial columns a thread has in flight
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int r = t / CH, c = t - r * CH;
+    const int S = a.splits;
+    float *const ww = sm.w;
+    float *const wl = sm.ls;
+    bool ok = true;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (TAGGED) {
+      const __amdgpu_buffer_rsrc_t tor = rsrc(a.tws, (uint32_t)((size_t)S * a.Hq * D * 8));
+      const __amdgpu_buffer_rsrc_t tmr = rsrc(a.tws + (size_t)S * a.Hq * D * 2, (uint32_t)((size_t)S * a.Hq * 16));
+      auto col_off = [&](int ss) { return ss < S ? (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 8) : 0x80000000u; };
+      // the first burst of partial columns goes out with the (m, l) requests
+      u32x4 lo[kBurst], hi[kBurst];
 #pragma unroll
-  for (int k = 0; k < kMlLoads; ++k) {
-    const int i = t + kAttnThreads * k;
-    const int ss = i / G, h = i - ss * G;
-    const uint32_t off = i < nml ? (uint32_t)((((size_t)ss * a.Hq + j * G + h) * 2) * 4) : 0x80000000u;
-    mlv[k] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, off, 0, kAuxSc1));
-  }
-  f32x4 ov[kMergeLoads];
-  auto load_pass = [&](int s0) {
+      for (int u = 0; u < kBurst; ++u) {
+        lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(r + RH * u), 0, kAuxSc1));
+        hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(r + RH * u) + 16, 0, kAuxSc1));
+      }
+      for (int i = t; i < S; i += kAttnThreads) {
+        const uint32_t off = (uint32_t)(((size_t)i * a.Hq + h) * 16);
+        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tmr, off, 0, kAuxSc1));
+        unsigned spins = 0;
+        while (v.y != tag || v.w != tag) {
+          if (!poll_step(spins, a.err)) {
+            ok = false;
+            v.x = __builtin_bit_cast(uint32_t, kNegBig); v.y = tag; v.z = 0u; v.w = tag;
+            break;
+          }
+          v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tmr, off, 0, kAuxSc1));
+        }
+        // (whole-vector bit casts: a bit cast of one element of a vector compiles to element 0)
+        const f32x4 vf = __builtin_bit_cast(f32x4, v);
+        ww[i] = vf.x;
+        wl[i] = vf.z;
+      }
+      __syncthreads();
+      merge_weights(ww, wl, S, wave, lane);
+      __syncthreads();
+      for (int s0 = r;; ) {
 #pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) {
-      const int ss = s0 + rr + R * u;
-      const uint32_t off = (mt && ss < a.splits) ? (uint32_t)((((size_t)ss * a.Hq + j * G) * D + 4 * cc) * 4) : 0x80000000u;
-      ov[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kAuxSc1));
+        for (int u = 0; u < kBurst; ++u) {
+          const int ss = s0 + RH * u;
+          if (ss >= S) break;
+          unsigned spins = 0;
+          while (ok && (lo[u].y != tag || lo[u].w != tag || hi[u].y != tag || hi[u].w != tag)) {
+            if (!poll_step(spins, a.err)) { ok = false; break; }
+            lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(ss), 0, kAuxSc1));
+            hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(ss) + 16, 0, kAuxSc1));
+          }
+          const f32x4 lf = __builtin_bit_cast(f32x4, lo[u]), hf = __builtin_bit_cast(f32x4, hi[u]);
+          const f32x4 o = {lf.x, lf.z, hf.x, hf.z};
+          acc += ww[ss] * o;
+        }
+        s0 += RH * kBurst;
+        if (s0 >= S) break;
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(s0 + RH * u), 0, kAuxSc1));
+          hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(s0 + RH * u) + 16, 0, kAuxSc1));
+        }
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t orr = rsrc(a.ws, (uint32_t)((size_t)S * a.Hq * D * 4));
+      const __amdgpu_buffer_rsrc_t mlr = rsrc(a.ws + (size_t)S * a.Hq * D, (uint32_t)((size_t)S * a.Hq * 2 * 4));
+      for (int i = t; i < S; i += kAttnThreads) {
+        const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, (uint32_t)(((size_t)i * a.Hq + h) * 8), 0, kAuxSc1));
+        ww[i] = __builtin_bit_cast(float, (uint32_t)v);
+        wl[i] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+      }
+      __syncthreads();
+      merge_weights(ww, wl, S, wave, lane);
+      __syncthreads();
+      for (int s0 = r; s0 < S; s0 += RH * kBurst) {
+        f32x4 ov[kBurst];
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int ss = s0 + RH * u;
+          const uint32_t off = ss < S ? (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 4) : 0x80000000u;
+          ov[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kAuxSc1));
+        }
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int ss = s0 + RH * u;
+          if (ss >= S) break;
+          acc += ww[ss] * ov[u];
+        }
+      }
     }
-  };
-  load_pass(0);
+    sm.o[r * CH + c] = acc;
+    __syncthreads();
+    if (t < CH) {
+      f32x4 out = sm.o[t];
 #pragma unroll
-  for (int k = 0; k < kMlLoads; ++k) {
-    const int i = t + kAttnThreads * k;
-    if (i < nml) {
-      const int ss = i / G, h = i - ss * G;
-      sw[ss][h] = __builtin_bit_cast(float, (uint32_t)mlv[k]);
-      sl[ss][h] = __builtin_bit_cast(float, (uint32_t)(mlv[k] >> 32));
+      for (int rr = 1; rr < RH; ++rr) out += sm.o[rr * CH + t];
+      if constexpr (TAGGED) {
+        const u32x4 vb = __builtin_bit_cast(u32x4, out);
+        u32x4 p0, p1;
+        p0.x = vb.x; p0.y = tag; p0.z = vb.y; p0.w = tag;
+        p1.x = vb.z; p1.y = tag; p1.z = vb.w; p1.w = tag;
+        const __amdgpu_buffer_rsrc_t tr = rsrc(a.tout, (uint32_t)(a.Hq * D * 8));
+        const uint32_t off = (uint32_t)(((size_t)h * D + 4 * t) * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(p0, tr, off, 0, kAuxSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(p1, tr, off + 16, 0, kAuxSc1);
+      } else {
+        *reinterpret_cast<f32x4 *>(a.out + (size_t)h * D + 4 * t) = out;
+      }
     }
+    __syncthreads();  // (the next head reuses the LDS above)
+    return ok;
   }
-  __syncthreads();
-  if (wave < G) {
-    const int h = wave;
+
+  // The split weights of a merge (wave 0): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
+  __device__ __forceinline__ static void merge_weights(float *ww, const float *wl, int S, int wave, int lane) {
+    if (wave != 0) return;
     float M = kNegBig;
-    for (int ss = lane; ss < a.splits; ss += 64) M = fmaxf(M, sw[ss][h]);
+    for (int i = lane; i < S; i += 64) M = fmaxf(M, ww[i]);
     M = wave_max(M);
     float L = 0.f;
-    for (int ss = lane; ss < a.splits; ss += 64) L = fmaf(__builtin_amdgcn_exp2f(sw[ss][h] - M), sl[ss][h], L);
+    for (int i = lane; i < S; i += 64) L = fmaf(__builtin_amdgcn_exp2f(ww[i] - M), wl[i], L);
     L = wave_sum(L);
     const float inv = 1.0f / L;
-    for (int ss = lane; ss < a.splits; ss += 64) sw[ss][h] = __builtin_amdgcn_exp2f(sw[ss][h] - M) * inv;
-  }
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0;;) {
-#pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) {
-      const int ss = s0 + rr + R * u;
-      if (mt && ss < a.splits) acc += sw[ss][hc] * ov[u];
-    }
-    s0 += R * kMergeLoads;
-    if (s0 >= a.splits) break;
-    load_pass(s0);
-  }
-  if (mt) sm_o[rr * C + cc] = acc;
-  __syncthreads();
-  if (t < C) {
-    f32x4 out = sm_o[t];
-#pragma unroll
-    for (int r = 1; r < R; ++r) out += sm_o[r * C + t];
-    if constexpr (SYNC)
-      store_sc1_b128(rsrc(a.out, (uint32_t)(a.Hq * D * 4)), (uint32_t)(((size_t)j * G * D + 4 * t) * 4), out);
-    else
-      *reinterpret_cast<f32x4 *>(a.out + (size_t)j * G * D + 4 * t) = out;
-  }
-  if (t == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (SYNC) {
-    drain_stores();
-    __syncthreads();
-    if (t == 0) __hip_atomic_store(a.done + j, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  mark(rec, 3);
+    for (int i = lane; i < S; i += 64) ww[i] = __builtin_amdgcn_exp2f(ww[i] - M) * inv;
   }
 };
 

@@ -168,6 +168,19 @@ __device__ __forceinline__ void poll_pause(unsigned spins) {
     __builtin_amdgcn_s_sleep(8);
 }
 
+// One step of a poll loop: pause, then give up (false) once the step's error word is set (checked
+// every 1024 polls) or after kLayerSpinLimit polls (setting it).
+__device__ inline bool poll_step(unsigned &spins, unsigned *err) {
+  poll_pause(spins);
+  ++spins;
+  if ((spins & 1023u) == 0 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return false;
+  if (spins > kLayerSpinLimit) {
+    __hip_atomic_store(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  return true;
+}
+
 // one thread: *p >= target
 __device__ inline bool poll_count(const unsigned *p, unsigned target, unsigned *err) {
   unsigned spins = 0;
@@ -621,6 +634,41 @@ struct GemvUnit {
     }
   }
 
+  // The activations of the stash's two batches from (value, tag) pairs, polled until every tag
+  // of the unit's k-range equals this launch's tag (past the range: zeros).  False if the poll
+  // gave up (the error word is then set).
+  __device__ __forceinline__ bool load_tagged_acts(const GemvArgs &a, GemvBatch<FMT, NORM> &A, GemvBatch<FMT, NORM> &B, unsigned e,
+                                                   int lane) {
+    const unsigned tag = e * a.xt_tag_mul + a.xt_tag_add;
+    const __amdgpu_buffer_rsrc_t tr = rsrc(a.xt + (size_t)c0 * CK * 2, (uint32_t)nrun * CK * 8);
+    const bool in_a = lane * 4 < kBatch * CK && lane * 4 < nrun * CK;
+    const bool in_b = lane * 4 < kBatch * CK && kBatch * CK + lane * 4 < nrun * CK;
+    const uint32_t oa = in_a ? (uint32_t)(lane * 4) * 8u : 0x80000000u;
+    const uint32_t ob = in_b ? (uint32_t)(kBatch * CK + lane * 4) * 8u : 0x80000000u;
+    u32x4 a0, a1, b0, b1;
+    unsigned spins = 0;
+    for (;;) {
+      a0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, oa, 0, kAuxSc1));
+      a1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, oa + 16, 0, kAuxSc1));
+      b0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, ob, 0, kAuxSc1));
+      b1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, ob + 16, 0, kAuxSc1));
+      const bool ok = (!in_a || (a0.y == tag && a0.w == tag && a1.y == tag && a1.w == tag)) &&
+                      (!in_b || (b0.y == tag && b0.w == tag && b1.y == tag && b1.w == tag));
+      if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+      if (!poll_step(spins, a.err)) return false;
+    }
+    // (whole-vector bit casts: a bit cast of one element of a vector compiles to element 0)
+    const f32x4 fa0 = __builtin_bit_cast(f32x4, a0), fa1 = __builtin_bit_cast(f32x4, a1);
+    const f32x4 fb0 = __builtin_bit_cast(f32x4, b0), fb1 = __builtin_bit_cast(f32x4, b1);
+    A.x = f32x4{fa0.x, fa0.z, fa1.x, fa1.z};
+    B.x = f32x4{fb0.x, fb0.z, fb1.x, fb1.z};
+    if constexpr (NORM) {
+      A.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, in_a ? (uint32_t)(lane * 4) * 4u : 0x80000000u, 0, 0));
+      B.g = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(gr, in_b ? (uint32_t)(kBatch * CK + lane * 4) * 4u : 0x80000000u, 0, 0));
+    }
+    return true;
+  }
+
   __device__ __forceinline__ void finish(const GemvArgs &a, Stage<CK> (&sm)[2], int lane, const u32x4 *stash = nullptr,
                                         unsigned long long *rec = nullptr) {
     unsigned e = 0;
@@ -628,16 +676,24 @@ struct GemvUnit {
     if constexpr (SYNC == kSyncConsumer) {
       // the producers of activations k = c0 CK .. (c0 + nrun) CK - 1 (the weights are already
       // on their way)
-      if (!poll_flags(a.wait_flags, (c0 * CK) / a.wait_div, ((c0 + nrun) * CK - 1) / a.wait_div, e, a.err, lane)) return;
-      mark(rec, 0);
+      // (tagged activations carry their own readiness: polled below, when they are loaded)
+      if (!a.xt) {
+        if (!poll_flags(a.wait_flags, (c0 * CK) / a.wait_div, ((c0 + nrun) * CK - 1) / a.wait_div, e, a.err, lane)) return;
+        mark(rec, 0);
+      }
     }
     float acc = 0.f;
     const int nb = (nrun + kBatch - 1) / kBatch;
     if constexpr (WLDS) {
       static_assert(kStashRuns == 2 * kBatch, "two batches per stash");
       GemvBatch<FMT, NORM> B;
-      load_acts<FMT, NORM, XCOH>(A, xr, gr, 0, lane);
-      load_acts<FMT, NORM, XCOH>(B, xr, gr, kBatch, lane);
+      if (XCOH && a.xt) {
+        if (!load_tagged_acts(a, A, B, e, lane)) return;
+        mark(rec, 0);
+      } else {
+        load_acts<FMT, NORM, XCOH>(A, xr, gr, 0, lane);
+        load_acts<FMT, NORM, XCOH>(B, xr, gr, kBatch, lane);
+      }
       __builtin_amdgcn_s_waitcnt(0);  // the stash copies (not tracked by the compiler) have landed
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll

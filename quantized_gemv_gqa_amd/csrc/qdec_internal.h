@@ -60,6 +60,10 @@ struct GemvArgs {
   int Hq, Hkv, hd;
   unsigned *err;  // set on a wait that times out
   unsigned long long *timeline;  // diagnostics: 8 clock marks per unit of a plain launch, or null
+  // Consumer form with tagged activations: x is read as (value, tag) pairs from xt, polled until
+  // every tag equals *epoch * xt_tag_mul + xt_tag_add (no separate wait).
+  const uint32_t *xt;
+  unsigned xt_tag_mul, xt_tag_add;
 };
 // Device atomics to one cache line serialize (about 13 ns each on MI355X), so every arrival
 // counter sits on a 128-byte line of its own.
@@ -129,13 +133,17 @@ struct AttnArgs {
   float *out;              // [Hq][D]
   // Step-synchronised form (fused layer kernel; null otherwise): wait until
   // wait_cnt[j * kLine] >= *epoch * wait_per_step (the qkv tiles of KV head j are stored), read qkv
-  // with device-coherent loads, store out device-coherently and set done[j] = *epoch when the
-  // merge of KV head j is complete.
+  // with device-coherent loads, publish the split's partial as (value, tag) pairs in tws
+  // ([splits][Hq][D] pairs, then [splits][Hq] (m, tag, l, tag); tag = *epoch * tag_mul + tag_add),
+  // merge query head h on split h % G % splits of its KV head and store its output as tagged
+  // pairs in tout.
   const unsigned *epoch;
   const unsigned *wait_cnt;
   unsigned wait_per_step;
-  unsigned *done;
   unsigned *err;
+  uint32_t *tws;
+  uint32_t *tout;  // merged output as tagged pairs [Hq][D] (fused launch)
+  unsigned tag_mul, tag_add;
 };
 constexpr int kMaxMergeSplits = 256;
 // The attention kernels address a layer's K or V pool through one buffer resource with 32-bit
@@ -149,6 +157,7 @@ inline bool kv_pool_fits(long long n_pages, int Hkv, int D, int kv_fmt) {
 constexpr unsigned kErrWait = 1u, kErrKvSlot = 2u;
 constexpr size_t kAttnCounterBytes = 64 * 128;  // one line per KV head, up to 64 KV heads
 size_t attn_workspace_bytes(int Hq, int D, int splits);
+inline size_t attn_tagged_bytes(int Hq, int D, int splits) { return (size_t)splits * Hq * (2 * D + 4) * 4; }
 hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
 
 // Append one token's k, v ([Hkv][D] fp32) into the pools at *pos.

@@ -25,6 +25,8 @@ struct qdec_step {
   qdec_state state;
   // workspace carve-up
   float *qkv = nullptr, *attn = nullptr, *mlp = nullptr, *ssq = nullptr, *attn_ws = nullptr;
+  uint32_t *attn_tws = nullptr;   // the fused launch's tagged split partials
+  uint32_t *attn_tout = nullptr;  // and its tagged merged attention output
   double *rope_cs = nullptr;  // this step's RoPE (cos, sin) table, written by the embed kernel
   // fused attention kernel (three launches per layer)
   bool layer_ok = false;
@@ -63,7 +65,7 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qkv, attn, mlp, ssq, attn_ws, rope_cs, gemv_ws, gemv_ws2, lsync, err, sample_ws, hB, ssqB, total;
+  size_t qkv, attn, mlp, ssq, attn_ws, attn_tws, attn_tout, rope_cs, gemv_ws, gemv_ws2, lsync, err, sample_ws, hB, ssqB, total;
 };
 
 // The fused attention launch has one workgroup per compute unit, at most this many (the GEMV
@@ -91,9 +93,8 @@ GemvPlan layer_plan(int wfmt, int N, int K, int waves, int max_cps) {
   return p;
 }
 
-// Per layer: the qkv tile counts (one 128-byte line per KV head) and the attention-done flags
-// (one line).
-size_t lsync_layer_words(int Hkv) { return (size_t)Hkv * kLine + kLine; }
+// Per layer: the qkv tile counts (one 128-byte line per KV head).
+size_t lsync_layer_words(int Hkv) { return (size_t)Hkv * kLine; }
 
 Layout layout_of(const qdec_config &c) {
   Layout L{};
@@ -105,6 +106,8 @@ Layout layout_of(const qdec_config &c) {
   L.mlp = off; off += align256((size_t)c.inter * 4);
   L.ssq = off; off += align256((size_t)((c.hidden + 63) / 64) * 4);
   L.attn_ws = off; off += align256(attn_workspace_bytes(c.n_heads, c.head_dim, c.num_splits));
+  L.attn_tws = off; off += align256(attn_tagged_bytes(c.n_heads, c.head_dim, c.num_splits));
+  L.attn_tout = off; off += align256((size_t)c.n_heads * c.head_dim * 8);
   L.rope_cs = off; off += align256((size_t)c.head_dim * sizeof(double));
   size_t g = gemv_workspace_bytes(c.wfmt, nqkv, c.hidden);
   g = std::max(g, gemv_workspace_bytes(c.wfmt, c.hidden, qd));
@@ -250,7 +253,6 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   unsigned *const epoch = h->lsync;
   unsigned *const ls = h->lsync + 32 + (size_t)l * h->lsync_layer_words;
   unsigned *const qkv_cnt = ls;                            // [Hkv lines]
-  unsigned *const attn_done = ls + (size_t)Hkv * kLine;    // [Hkv] in one line
   float *const hA = s.hidden;
   LayerArgs la{};
   la.qkv = gemv_args(h, w.w_qkv, w.s_qkv, hA, h->qkv, nqkv, H, h->p_qkv);
@@ -266,15 +268,19 @@ hipError_t enqueue_layer(qdec_step *h, int l, hipStream_t st) {
   la.at.epoch = epoch;
   la.at.wait_cnt = qkv_cnt;
   la.at.wait_per_step = (unsigned)((G + 2) * (D / kTile));
-  la.at.done = attn_done;
   la.at.err = h->err;
+  la.at.tws = h->attn_tws;
+  la.at.tout = h->attn_tout;
+  la.at.tag_mul = (unsigned)c.n_layers;
+  la.at.tag_add = (unsigned)l;
   la.o = gemv_args(h, w.w_o, w.s_o, h->attn, h->hB, H, qd, h->p_o);
   gemv_bind_workspace(la.o, h->p_o, h->gemv_ws2);
   la.o.residual = hA;
   la.o.ssq_out = h->ssqB;
   la.o.epoch = epoch;
-  la.o.wait_flags = attn_done;
-  la.o.wait_div = G * D;  // attention outputs per KV head
+  la.o.xt = h->attn_tout;  // the merged attention output, tagged like the split partials
+  la.o.xt_tag_mul = (unsigned)c.n_layers;
+  la.o.xt_tag_add = (unsigned)l;
   la.o.err = h->err;
   gemv_apply_plan(la.qkv, h->p_qkv, c.wfmt);
   gemv_apply_plan(la.o, h->p_o, c.wfmt);
@@ -641,6 +647,8 @@ qdec_status qdec_step_create(const qdec_config *cfg, const qdec_model *m, const 
   h->mlp = reinterpret_cast<float *>(ws + L.mlp);
   h->ssq = reinterpret_cast<float *>(ws + L.ssq);
   h->attn_ws = reinterpret_cast<float *>(ws + L.attn_ws);
+  h->attn_tws = reinterpret_cast<uint32_t *>(ws + L.attn_tws);
+  h->attn_tout = reinterpret_cast<uint32_t *>(ws + L.attn_tout);
   h->rope_cs = reinterpret_cast<double *>(ws + L.rope_cs);
   h->gemv_ws = ws + L.gemv_ws;
   h->sample_ws = ws + L.sample_ws;

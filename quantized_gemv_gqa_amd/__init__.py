@@ -459,15 +459,15 @@ def upload_kv(kv: dict, kv_fmt: str, device="cuda") -> dict:
             "v": [_to_dev(a, device, dt) for a in kv["v"]]}
 
 
-def default_splits(n_kv_heads: int, ctx: int, pages_per_wave: int = 1) -> int:
-    """Attention split count: at most `pages_per_wave` KV pages for each of a split's 8 waves
-    (pages are dealt round-robin over all waves of a KV head, and the wave with the most pages
-    sets the split's time), rounded up to a multiple of 8 so a context that grows by a few pages
-    does not give some waves a second page, at most 64 (past that a longer context gives each
-    wave more pages).  Measured at 4096 tokens, Qwen2.5-7B shape: 40 splits 1.958 ms per step, 32
-    splits 1.980 ms, 48 splits 1.962 ms."""
+def default_splits(n_kv_heads: int, ctx: int, pages_per_split: int = 4) -> int:
+    """Attention split count: at most `pages_per_split` KV pages per split (pages are dealt to the
+    splits first, so a split's pages sit on its first waves, one per SIMD of the compute unit),
+    rounded up to a multiple of 8 so a context that grows by a few pages keeps the same count, at
+    most 64 (past that a longer context gives each wave more pages).  Measured at 4096 tokens,
+    Qwen2.5-7B shape: 64 splits 1.704 ms per step, 56 splits 1.711, 48 splits 1.721, 40 splits
+    1.714."""
     pages = max(1, -(-(ctx + 1) // PAGE))
-    s = -(-pages // (8 * pages_per_wave))
+    s = -(-pages // pages_per_split)
     s = -(-s // 8) * 8
     return int(max(1, min(s, 64)))
 

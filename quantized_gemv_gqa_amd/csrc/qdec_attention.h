@@ -62,17 +62,23 @@ struct Row {
   }
 };
 
-// Online-softmax update of one wave with one 16-token page: token slot sub*4 + slot of the page
-// sits in this lane's kp[sub] / vp[sub]; tokens at or past T are masked.
+// Online-softmax update of one wave with up to four 4-token quarters of the context: token
+// t0[sub] + slot sits in this lane's kp[sub] / vp[sub] for sub < nsub (uniform); tokens at or past
+// T are masked (an unmapped quarter has t0 = T).  Subs from nsub on are skipped.
 template <int D, int G, int KVF>
-__device__ __forceinline__ void attend_page(Row<D, KVF> (&kp)[4], Row<D, KVF> (&vp)[4], int p, int T, int slot,
-                                            const float (&q)[G][D / 16], float (&m)[G], float (&l)[G],
-                                            float (&o)[G][D / 16]) {
+__device__ __forceinline__ void attend_quarters(Row<D, KVF> (&kp)[4], Row<D, KVF> (&vp)[4], const int (&t0)[4],
+                                                int nsub, int T, int slot, const float (&q)[G][D / 16],
+                                                float (&m)[G], float (&l)[G], float (&o)[G][D / 16]) {
   constexpr int DPL = D / 16;
   float sc[4][G];
 #pragma unroll
   for (int sub = 0; sub < 4; ++sub) {
-    const bool valid = p * 16 + sub * 4 + slot < T;
+    if (sub >= nsub) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[sub][h] = -INFINITY;
+      continue;
+    }
+    const bool valid = t0[sub] + slot < T;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float d = 0.f;
@@ -101,13 +107,15 @@ __device__ __forceinline__ void attend_page(Row<D, KVF> (&kp)[4], Row<D, KVF> (&
     for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
   }
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub)
+  for (int sub = 0; sub < 4; ++sub) {
+    if (sub >= nsub) break;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
       const float vv = vp[sub].get(e);
 #pragma unroll
       for (int h = 0; h < G; ++h) o[h][e] = fmaf(sc[sub][h], vv, o[h][e]);
     }
+  }
 }
 
 // Optional RMSNorm over the head (DPL dims per lane, 16 lanes) and RoPE rotation of one head
@@ -165,9 +173,11 @@ struct AttnSmem {
 };
 
 // One (KV head j, split s) attention unit, run by a whole workgroup of kAttnThreads threads.
-// SYNC: the step-synchronised form of the fused layer kernels (AttnArgs: epoch, wait_cnt, done).
-// start() requests the RoPE table and the wave's first KV page (nothing else happens before it);
-// finish() does the rest, so a kernel can issue other roles' loads, or compute, between the two.
+// SYNC: the step-synchronised form of the fused layer kernels (AttnArgs: epoch, wait_cnt, tws,
+// tout).  start() requests the RoPE table and the wave's first KV page (nothing else happens
+// before it); pages() waits for the inputs and attends to the wave's pages; publish() merges the
+// workgroup's waves and publishes (and merges) the split.  A kernel can issue other roles' loads,
+// or compute, between the three; finish() is pages() then publish().
 template <int D, int G, int KVF, bool ROPE, bool SYNC>
 struct AttnUnit {
   static constexpr int DPL = D / 16;
@@ -180,10 +190,12 @@ struct AttnUnit {
   // carry long-running loads of other roles (which in-order memory counters would make these
   // steps wait for).
   static constexpr int kRopeWaves = 4;
-  int pos, T, P, nwt, gw, last_page;
+  int pos, T, Q, npw, pw, nq, last_page;
+  int nwp;       // waves of this split that hold quarters (the first ones)
+  unsigned ep;   // the step number (SYNC)
   __amdgpu_buffer_rsrc_t kr, vr;
   Row<D, KVF> kp[PF][4], vp[PF][4];
-  bool have[PF];
+  int t0[PF][4];
   double cs[ROPE ? 2 * DPL : 1];  // fp64 (cos, sin) of the lane's rotation pairs
 
   __device__ __forceinline__ void start(const AttnArgs &a, int j, int s) {
@@ -193,13 +205,18 @@ struct AttnUnit {
     const int part = lane & 15;
     pos = *a.pos;
     T = pos + 1;
-    P = max(0, min((T + 15) >> 4, a.n_pages));  // never index outside the page table
-    // pages are dealt round-robin over all NW * splits waves of the KV head, splits first: wave
-    // gw = s + splits * wave takes pages gw, gw + nwt, gw + 2 nwt, ...  So every split gets a
-    // page before any split gets a second one, and the waves of a workgroup that hold pages are
-    // the first ones (one per SIMD while a workgroup holds at most four pages).
-    nwt = NW * a.splits;
-    gw = s + a.splits * wave;
+    // The context is dealt in quarters of a page (4 tokens; quarter g is sub-block g % 4 of page
+    // g / 4) so that the work spreads evenly over the SIMDs: per KV head npw = W splits waves hold
+    // quarters, W = Q / (4 splits) clamped to 1 .. NW (a wave is added only once every wave has
+    // four quarters, a page's worth), splits first: wave pw = s + splits * wave takes quarters
+    // pw, pw + npw, pw + 2 npw, ..., four at a time.  Quarters beyond an even share land one per
+    // wave: a quarter's work more, not a page's on a SIMD that is busy with another page.
+    Q = max(0, min((T + 3) >> 2, 4 * a.n_pages));  // never index outside the page table
+    const int W = min(NW, max(1, Q / (4 * a.splits)));
+    npw = W * a.splits;
+    pw = s + a.splits * wave;
+    nq = (wave < W && pw < Q) ? (Q - pw + npw - 1) / npw : 0;
+    nwp = Q > s ? min(W, (Q - s + a.splits - 1) / a.splits) : 0;  // wave < nwp  <=>  nq > 0
     last_page = ((T + 15) >> 4) - 1;
     if constexpr (ROPE) {
       if (wave < kRopeWaves) {
@@ -211,28 +228,41 @@ struct AttnUnit {
     const uint32_t pool_bytes = (uint32_t)((size_t)a.n_pages * a.Hkv * 16 * D * EB);
     kr = rsrc(a.k_pool, pool_bytes);
     vr = rsrc(a.v_pool, pool_bytes);
-    const size_t head_stride = (size_t)16 * D;  // elements of one head's slice of a page
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int p = gw + nwt * i;
-      have[i] = false;
-      if (p < P) {
-        const int phys = a.page_table[p];
+    for (int i = 0; i < PF; ++i) load_group(a, j, i, i, slot, part);
+  }
+
+  // Requests quarters 4 k .. 4 k + 3 of this wave into buffer b (t0 = T for a quarter past the
+  // wave's share or on an unmapped page: its tokens are masked, nothing is read).
+  __device__ __forceinline__ void load_group(const AttnArgs &a, int j, int k, int b, int slot, int part) {
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const int i = 4 * k + sub;
+      t0[b][sub] = T;
+      if (i < nq) {
+        const int g = pw + npw * i;
+        const int phys = a.page_table[g >> 2];
         if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
-          have[i] = true;
-          const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub) {
-            const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
-            kp[i][sub].load(kr, off);
-            vp[i][sub].load(vr, off);
-          }
+          t0[b][sub] = 4 * g;
+          const size_t row = (((size_t)phys * a.Hkv + j) * 16 + (g & 3) * 4 + slot) * D + part * DPL;
+          kp[b][sub].load(kr, (uint32_t)(row * EB));
+          vp[b][sub].load(vr, (uint32_t)(row * EB));
         }
       }
     }
   }
 
+  __device__ __forceinline__ bool holds_page() const { return nq > 0; }
+
   __device__ __forceinline__ void finish(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm,
+                                        unsigned long long *rec = nullptr) {
+    if (pages(a, j, s, sm, rec)) publish(a, j, s, sm, rec);
+  }
+
+  // Waits for the inputs (SYNC), stages q, k, v (ROPE), attends to the wave's pages and leaves
+  // each page-holding wave's (m, l, o) in LDS.  Returns false (for the whole workgroup) if the
+  // wait gave up.
+  __device__ __forceinline__ bool pages(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm,
                                         unsigned long long *rec = nullptr) {
   constexpr int C = G * D / 4;                                                // f32x4 columns
   auto &sm_m = sm.m;
@@ -244,7 +274,6 @@ struct AttnUnit {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane >> 4;
   const int part = lane & 15;
-  const size_t head_stride = (size_t)16 * D;
 
   unsigned e = 0;
   if constexpr (SYNC) {
@@ -253,9 +282,10 @@ struct AttnUnit {
     e = __builtin_amdgcn_readfirstlane(*a.epoch);
     if (threadIdx.x == 0) last = poll_count(a.wait_cnt + j * kLine, e * a.wait_per_step, a.err) ? 1u : 0u;
     __syncthreads();
-    if (!last) return;  // (every thread of the workgroup leaves together)
-    __syncthreads();    // everyone has read the flag before it is reused
+    if (!last) return false;  // (every thread of the workgroup leaves together)
+    __syncthreads();          // everyone has read the flag before it is reused
   }
+  ep = e;
   mark(rec, 0);
   float q[G][DPL];
   Row<D, KVF> knew, vnew;
@@ -290,7 +320,7 @@ struct AttnUnit {
     }
     __syncthreads();
     mark(rec, 9);
-    if (gw < P) {  // (waves without a page need no q)
+    if (nq > 0) {  // (waves without quarters need no q)
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -326,7 +356,7 @@ struct AttnUnit {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) q[h][e] = a.q[(size_t)(j * G + h) * D + part * DPL + e] * a.scale_log2;
   }
-  const int new_sub = (pos & 15) >> 2, new_slot = pos & 3;
+  const int new_slot = pos & 3;
 
   float m[G], l[G], o[G][DPL];
 #pragma unroll
@@ -336,31 +366,24 @@ struct AttnUnit {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
-  auto page = [&](Row<D, KVF> (&kq)[4], Row<D, KVF> (&vq)[4], int p) {
-    if (ROPE && p == last_page) {  // the newest token's row comes from registers
+  const int qnew = pos >> 2;  // the newest token's quarter
+  auto group = [&](Row<D, KVF> (&kq)[4], Row<D, KVF> (&vq)[4], const int (&tq)[4], int nsub) {
+    if (ROPE) {  // the newest token's row comes from registers
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub)
-        if (sub == new_sub && slot == new_slot) {
+        if (tq[sub] == 4 * qnew && slot == new_slot) {
           kq[sub] = knew;
           vq[sub] = vnew;
         }
     }
-    attend_page<D, G, KVF>(kq, vq, p, T, slot, q, m, l, o);
+    attend_quarters<D, G, KVF>(kq, vq, tq, nsub, T, slot, q, m, l, o);
   };
 #pragma unroll
   for (int i = 0; i < PF; ++i)
-    if (have[i]) page(kp[i], vp[i], gw + nwt * i);
-  for (int p = gw + PF * nwt; p < P; p += nwt) {
-    const int phys = a.page_table[p];
-    if (phys < 0 || phys >= a.n_pages) continue;
-    const size_t base = ((size_t)phys * a.Hkv + j) * head_stride;
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-      const uint32_t off = (uint32_t)((base + (size_t)(sub * 4 + slot) * D + part * DPL) * EB);
-      kp[0][sub].load(kr, off);
-      vp[0][sub].load(vr, off);
-    }
-    page(kp[0], vp[0], p);
+    if (4 * i < nq) group(kp[i], vp[i], t0[i], min(4, nq - 4 * i));
+  for (int k = PF; 4 * k < nq; ++k) {
+    load_group(a, j, k, 0, slot, part);
+    group(kp[0], vp[0], t0[0], min(4, nq - 4 * k));
   }
 
   // merge the four token slots of this wave (lanes part, part+16, part+32, part+48): lane
@@ -384,40 +407,55 @@ struct AttnUnit {
     }
   };
   mark(rec, 1);
-  merge_pairs(pair16);
-  merge_pairs(pair32);
-  if (slot == 0) {
+  // (waves without pages hold nothing to merge and leave the SIMDs to the ones with pages)
+  if (wave < nwp) {
+    merge_pairs(pair16);
+    merge_pairs(pair32);
+    if (slot == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e4 = 0; e4 < DPL / 4; ++e4)
-        sm_o[wave * C + (h * D + part * DPL) / 4 + e4] =
-            f32x4{o[h][4 * e4], o[h][4 * e4 + 1], o[h][4 * e4 + 2], o[h][4 * e4 + 3]};
-      if (part == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
+        for (int e4 = 0; e4 < DPL / 4; ++e4)
+          sm_o[wave * C + (h * D + part * DPL) / 4 + e4] =
+              f32x4{o[h][4 * e4], o[h][4 * e4 + 1], o[h][4 * e4 + 2], o[h][4 * e4 + 3]};
+        if (part == 0) {
+          sm_m[wave][h] = m[h];
+          sm_l[wave][h] = l[h];
+        }
       }
     }
   }
+  return true;
+  }
+
+  // Merges the page-holding waves' states into the split's partial and publishes it; SYNC: then
+  // merges the query heads this split is responsible for.
+  __device__ __forceinline__ void publish(const AttnArgs &a, int j, int s, AttnSmem<D, G, ROPE> &sm,
+                                          unsigned long long *rec = nullptr) {
+  constexpr int C = G * D / 4;  // f32x4 columns
+  auto &sm_m = sm.m;
+  auto &sm_l = sm.l;
+  auto &sm_o = sm.o;
+  unsigned &last = sm.flag;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const unsigned e = ep;
   __syncthreads();
-  // merge the NW waves into the split's partial: o (G heads x D) and per head (m, l)
+  // merge the page-holding waves into the split's partial: o (G heads x D) and per head (m, l);
+  // a split without pages publishes m = -1e30, l = 0, o = 0
+  const int nw = nwp;
   auto column = [&](int c) {
     const int h = c / (D / 4);
     float mx = kNegBig;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, sm_m[w][h]);
     f32x4 val = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) val += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_o[w * C + c];
+    for (int w = 0; w < nw; ++w) val += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_o[w * C + c];
     return val;
   };
   auto head_ml = [&](int h, float &mx, float &lsum) {
     mx = kNegBig;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w][h]);
+    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, sm_m[w][h]);
     lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) lsum += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_l[w][h];
+    for (int w = 0; w < nw; ++w) lsum += __builtin_amdgcn_exp2f(sm_m[w][h] - mx) * sm_l[w][h];
   };
   if constexpr (SYNC) {
     // Published as (value, tag) pairs, each pair one 8-byte store that a reader sees whole or not

@@ -622,11 +622,8 @@ struct GemvUnit {
     if constexpr (FMT == QDEC_W_Q8_ROW) pre_scale = reinterpret_cast<const float *>(a.S)[n];  // padded to tiles
     if constexpr (WLDS) {
 #pragma unroll
-      for (int r = 0; r < kStashRuns; ++r) {
+      for (int r = 0; r < kStashRuns; ++r)
         if (r < nrun) lds_dma_b128(wr, (uint32_t)r * (kTile * 16) + lane * 16, stash + r * kTile);
-        if constexpr (Q4)
-          s_all[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, (uint32_t)(((c0 + r) >> gshift) - g0) * (kTile * 2) + lane * 2, 0, 0);
-      }
     } else {
       static_assert(SYNC != kSyncConsumer, "a consumer's activations are loaded after its wait");
 #pragma unroll
@@ -687,6 +684,13 @@ struct GemvUnit {
     if constexpr (WLDS) {
       static_assert(kStashRuns == 2 * kBatch, "two batches per stash");
       GemvBatch<FMT, NORM> B;
+      // The stash's scales are requested here, not in start(): held from there, the compiler
+      // converts them at once, so start() would wait for the whole stash copy.
+      if constexpr (Q4) {
+#pragma unroll
+        for (int r = 0; r < kStashRuns; ++r)
+          s_all[r] = __builtin_amdgcn_raw_buffer_load_b16(sr, (uint32_t)(((c0 + r) >> gshift) - g0) * (kTile * 2) + lane * 2, 0, 0);
+      }
       if (XCOH && a.xt) {
         if (!load_tagged_acts(a, A, B, e, lane)) return;
         mark(rec, 0);

@@ -57,7 +57,7 @@ def test_gemm_parity(wfmt, N, K, nb, split):
 class Batch:
     """One batched workload on both sides: device pools/tables and the oracle's copy."""
 
-    def __init__(self, name, ctxs, n_layers=2, max_blocks=None, spare=8):
+    def __init__(self, name, ctxs, n_layers=2, max_blocks=None, spare=8, num_splits=8):
         wl = synth.WORKLOADS[name] if isinstance(name, str) else name
         self.wl = wl
         self.model = synth.make_model(wl, n_layers=n_layers)
@@ -75,7 +75,7 @@ class Batch:
         self.d_tables = dev(self.tables)
         self.d_pos = torch.zeros(B, dtype=torch.int32, device="cuda")
         self.d_tok = torch.zeros(B, dtype=torch.int32, device="cuda")
-        self.gpu = q.BatchDecode(self.dm, self.kp, self.vp, self.d_tables, self.d_pos, self.d_tok)
+        self.gpu = q.BatchDecode(self.dm, self.kp, self.vp, self.d_tables, self.d_pos, self.d_tok, num_splits=num_splits)
         self.h_orc = np.zeros((B, wl.hidden), np.float32)
 
     def map_blocks(self, pos):
@@ -131,6 +131,31 @@ def test_batch_step_matches_oracle():
                     toks[b] = tg[b]
                     pos[b] += 1
     assert bt.gpu.kernel_count == 1 + 5 * 2 + 3
+
+
+def test_batch_long_contexts_at_the_split_cap():
+    """Eight sequences near 4096 tokens with the split count batch_splits picks there: 8 sequences
+    x 4 KV heads x 8 splits = 256 attention workgroups, the cap.  Two layers of the Qwen2.5-7B
+    shape, an eager step then a graph replay, against the oracle."""
+    ctxs = [4096 - 37 * b for b in range(8)]
+    S = q.batch_splits(8, 4, max(ctxs))
+    assert S * 8 * 4 == 256, S
+    bt = Batch("qwen2.5-7b-q4", ctxs, num_splits=S)
+    rng = np.random.default_rng(4096)
+    toks = rng.integers(0, bt.wl.vocab, 8).astype(np.int32)
+    pos = np.array(ctxs, np.int32)
+    with torch.cuda.stream(torch.cuda.Stream()):
+        for s in range(2):
+            bt.map_blocks(pos)
+            bt.d_pos.copy_(torch.from_numpy(pos))
+            bt.d_tok.copy_(torch.from_numpy(toks))
+            bt.gpu.step(q.STEP_EAGER if s == 0 else q.STEP_GRAPH)
+            sync()
+            nxt, lg = bt.orc.step_batch(bt.tables, pos, toks, bt.h_orc)
+            tg = _check_slots(bt, pos, toks, nxt, lg, "step %d" % s)
+            assert np.array_equal(host(bt.d_pos), pos + 1)
+            toks = tg.copy()
+            pos = pos + 1
 
 
 @pytest.mark.parametrize("wfmt", ["q4", "q8"])

@@ -96,10 +96,14 @@ def _kv_rows(pool, wl, pt, t0, t1):
     return a.astype(np.float32) if wl.kv_fmt == "f32" else (a.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("name,ctx,T", [("qwen2.5-7b-q4", 40, 100), ("qwen2.5-7b-q4", 0, 256), ("qwen3-8b-q8", 5, 64),
-                                        ("qwen2.5-1.5b-q8", 16, 33)])
-def test_prefill_matches_oracle(name, ctx, T):
-    p = Prompt(name, ctx, T)
+@pytest.mark.parametrize("name,ctx,T,n_layers", [("qwen2.5-7b-q4", 40, 100, 2), ("qwen2.5-7b-q4", 0, 256, 2),
+                                                 ("qwen2.5-7b-q4", 0, 512, 2), ("qwen2.5-7b-q4", 24, 80, 4),
+                                                 ("qwen3-8b-q8", 5, 64, 2), ("qwen2.5-1.5b-q8", 16, 33, 2),
+                                                 ("qwen2.5-1.5b-q8", 3, 130, 6)])
+def test_prefill_matches_oracle(name, ctx, T, n_layers):
+    """Whole prefills (up to 512 tokens, 2 to 6 layers) against the oracle's: last hidden state,
+    logits and token, and every prompt token's K/V in every layer."""
+    p = Prompt(name, ctx, T, n_layers)
     with torch.cuda.stream(torch.cuda.Stream()):
         p.gpu.prefill(dev(p.tokens))
         sync()
@@ -115,7 +119,7 @@ def test_prefill_matches_oracle(name, ctx, T):
         assert srt[-1] - srt[-2] <= LOGIT_TOL, (tok, ref["token"])
     assert int(host(p.gpu.token_log)[0]) == tok
     pt = p.kv["page_table"]
-    for l in range(2):
+    for l in range(n_layers):
         for mine, theirs in ((p.dk["k"][l], p.orc.k[l]), (p.dk["v"][l], p.orc.v[l])):
             g = _kv_rows(host(mine).view(np.uint16) if p.wl.kv_fmt == "bf16" else host(mine), p.wl, pt, ctx, ctx + T)
             o = _kv_rows(theirs, p.wl, pt, ctx, ctx + T)

@@ -34,8 +34,10 @@ namespace {
 using namespace dev;
 
 // Waves a launch aims for: few k-splits keep the split-K tail short on small matrices (up to 128
-// tiles), more waves stream the large ones (measured on MI355X).
-constexpr int kTargetUnitsSmall = 1024;
+// tiles), more waves stream the large ones (measured on MI355X: for the down projections, about
+// six waves per compute unit beat four and eight: one wave per SIMD hides too little latency, and
+// 35 k-splits need a second burst of partial loads in the combine).
+constexpr int kTargetUnitsSmall = 1512;
 constexpr int kTargetUnitsLarge = 2048;
 constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
 

@@ -386,43 +386,81 @@ struct AttnUnit {
     group(kp[0], vp[0], t0[0], min(4, nq - 4 * k));
   }
 
-  // merge the four token slots of this wave (lanes part, part+16, part+32, part+48): lane
-  // swaps give both lanes of a pair the same (first, second) states, so they agree exactly
-  auto merge_pairs = [&](auto pair) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float ma, mb, la, lb;
-      pair(m[h], ma, mb);
-      pair(l[h], la, lb);
-      const float mx = fmaxf(ma, mb);
-      const float a1 = __builtin_amdgcn_exp2f(ma - mx), a2 = __builtin_amdgcn_exp2f(mb - mx);
-      l[h] = la * a1 + lb * a2;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        float oa, ob;
-        pair(o[h][e], oa, ob);
-        o[h][e] = oa * a1 + ob * a2;
-      }
-      m[h] = mx;
-    }
-  };
+  // Merge the four token slots of this wave (lanes part, part + 16, part + 32, part + 48):
+  // rescale every slot to the heads' common maximum, then sum the slots' (o, l) values with a
+  // butterfly of row swaps that reduces four values at once (3 swaps and 3 adds per four
+  // values; each row of lanes ends up holding the sums of a different one of the four).
   mark(rec, 1);
   // (waves without pages hold nothing to merge and leave the SIMDs to the ones with pages)
   if (wave < nwp) {
-    merge_pairs(pair16);
-    merge_pairs(pair32);
-    if (slot == 0) {
+    constexpr int CPH = DPL / 4;                    // float4 chunks of a head per lane
+    constexpr int NCH = G * CPH;                    // chunk slots, then the l slots
+    constexpr int NS = NCH + (G + 3) / 4;
+    constexpr int K = (NS + 3) / 4;                 // blocks of 16 values (4 slots x 4)
+    float M[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h) {
+      float x, y;
+      pair16(m[h], x, y);
+      pair32(fmaxf(x, y), x, y);
+      M[h] = fmaxf(x, y);
+    }
+    // value 16 k + 4 j + r: element j of slot 4 k + r (chunk (h, c) = slot 2 h + c or, past the
+    // chunks, l of heads 4 (slot - NCH) + j)
+    float v[16 * K];
 #pragma unroll
-        for (int e4 = 0; e4 < DPL / 4; ++e4)
-          sm_o[wave * C + (h * D + part * DPL) / 4 + e4] =
-              f32x4{o[h][4 * e4], o[h][4 * e4 + 1], o[h][4 * e4 + 2], o[h][4 * e4 + 3]};
-        if (part == 0) {
-          sm_m[wave][h] = m[h];
-          sm_l[wave][h] = l[h];
+    for (int i = 0; i < 16 * K; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = __builtin_amdgcn_exp2f(m[h] - M[h]);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int sl = h * CPH + e / 4;
+        v[16 * (sl / 4) + 4 * (e % 4) + sl % 4] = o[h][e] * al;
+      }
+      const int sl = NCH + h / 4;
+      v[16 * (sl / 4) + 4 * (h % 4) + sl % 4] = l[h] * al;
+    }
+    auto rowsum16 = [](float x, float y) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                      false, false);
+      const unsigned r0 = r[0], r1 = r[1];  // (copied out before the casts: see pair16)
+      return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    };
+    auto rowsum32 = [](float x, float y) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                      false, false);
+      const unsigned r0 = r[0], r1 = r[1];
+      return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    };
+    auto butterfly = [&](float a0, float a1, float a2, float a3) {
+      return rowsum32(rowsum16(a0, a1), rowsum16(a2, a3));
+    };
+    // which of the four values this lane's row ends up with (the same for every group): found
+    // by running the butterfly on markers
+    const float mk = butterfly(1.f, 2.f, 4.f, 8.f);  // 4, 8, 16 or 32
+    const int q = mk < 6.f ? 0 : (mk < 12.f ? 1 : (mk < 24.f ? 2 : 3));
+    float t[4 * K];
+#pragma unroll
+    for (int g = 0; g < 4 * K; ++g) t[g] = butterfly(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+    // lane (q, part) holds element j of slot 4 k + q in t[4 k + j]
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int sl = 4 * k + q;
+      if (sl < NCH) {
+        const int h = sl / CPH, c = sl % CPH;
+        sm_o[wave * C + (h * D + part * DPL) / 4 + c] = f32x4{t[4 * k], t[4 * k + 1], t[4 * k + 2], t[4 * k + 3]};
+      } else if (sl < NS && part == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int h = 4 * (sl - NCH) + jj;
+          if (h < G) sm_l[wave][h] = t[4 * k + jj];
         }
       }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) sm_m[wave][h] = M[h];
     }
   }
   return true;

@@ -9,9 +9,9 @@
 //   dealt over the workgroups first, so each compute unit streams an equal share), and the
 //   workgroup as a whole holds attention unit (KV head b / splits, split b % splits) if b is
 //   below Hkv * splits.
-// A wave first streams and computes its qkv unit; then, before it waits for anything, it
-// requests the rest of its HBM bytes: its first KV page (registers) and its o weights, which are
-// copied straight from HBM into an LDS stash and need no registers while the attention runs.  So
+// A wave first streams and computes its qkv unit; then it requests its first KV quarters
+// (registers), and once the attention has its pages, its o weights, which are copied straight
+// from HBM into an LDS stash and need no registers while the attention publishes and merges.  So
 // the qkv weights stream alone, the later phases' bytes land during the waits, and what remains
 // are the hand-offs:
 //   * attention unit (j, s) waits until the 2G + 4 qkv tiles of KV head j (its G q heads, its k
@@ -89,12 +89,16 @@ __global__ void __launch_bounds__(attn::kAttnThreads) attn_layer_k(const LayerAr
   }
   mark(rec, 5);
   // The later phases' bytes are requested once the wave's qkv unit is done, so the qkv weights,
-  // on the critical path, do not share HBM with them; they land while the attention waits.
+  // on the critical path, do not share HBM with them: the first KV quarters then, the o weights
+  // once the attention has its pages (they land while it publishes and merges; requested
+  // earlier, they compete with the qkv split-K hand-off).
   if (at_role) at.start(a.at, j, s);
-  if (o_role) go.start(a.o, uo, lane, stash[wave]);
   // (the attention's first LDS write follows a workgroup barrier, so every wave is past its
   // qkv unit's use of the union by then)
-  if (at_role) at.finish(a.at, j, s, sm.at, rec ? rec + 6 : nullptr);
+  bool at_ok = true;
+  if (at_role) at_ok = at.pages(a.at, j, s, sm.at, rec ? rec + 6 : nullptr);
+  if (o_role) go.start(a.o, uo, lane, stash[wave]);
+  if (at_role && at_ok) at.publish(a.at, j, s, sm.at, rec ? rec + 6 : nullptr);
   if (o_role) go.finish(a.o, sm.st[wave], lane, stash[wave], rec ? rec + 10 : nullptr);
   mark(rec, 13);
 }

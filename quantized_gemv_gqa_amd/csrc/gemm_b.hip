@@ -560,7 +560,9 @@ int gemm_b_columns(int batch) { return batch <= 2 ? 2 : (batch <= 4 ? 4 : 8); }
 // sums; the waves are limited by staging the columns' activations, not by their number).
 GemvPlan gemm_b_plan(int wfmt, int N, int K, int nb_max, bool allow_split) {
   (void)nb_max;
-  return gemv_plan(wfmt, N, K, allow_split);
+  // (the skinny GEMMs keep about four waves per compute unit on the small matrices: more k-splits
+  // made the batched step slower at every batch size)
+  return gemv_plan(wfmt, N, K, allow_split, 1024);
 }
 
 size_t gemm_b_workspace_bytes(int wfmt, int N, int K, int nb_max) {

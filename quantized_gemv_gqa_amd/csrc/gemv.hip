@@ -127,16 +127,17 @@ void gemv_apply_plan(GemvArgs &a, const GemvPlan &p, int wfmt) {
   a.group = gshift;
 }
 
-GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split) {
+GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split, int target_small) {
   GemvPlan p;
   const int ck = (wfmt == QDEC_W_Q4_G_ZP8) ? 32 : 16;
   p.tiles = (N + kTile - 1) / kTile;
   p.nch = K / ck;
   int ks = 1;
   if (allow_split && p.tiles <= kMaxSplitTiles) {
-    const int target = p.tiles <= 128 ? kTargetUnitsSmall : kTargetUnitsLarge;
+    const int target = p.tiles <= 128 ? (target_small > 0 ? target_small : kTargetUnitsSmall) : kTargetUnitsLarge;
     ks = (target + p.tiles / 2) / p.tiles;
-    ks = max(1, min(ks, p.nch / kMinChunks));
+    // (at most one burst of partial loads in the combine: a second costs a round trip)
+    ks = max(1, min(min(ks, kCombineBurst), p.nch / kMinChunks));
   }
   p.cps = (p.nch + ks - 1) / ks;
   p.ks = (p.nch + p.cps - 1) / p.cps;

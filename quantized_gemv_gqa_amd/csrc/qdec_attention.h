@@ -207,12 +207,15 @@ struct AttnUnit {
     T = pos + 1;
     // The context is dealt in quarters of a page (4 tokens; quarter g is sub-block g % 4 of page
     // g / 4) so that the work spreads evenly over the SIMDs: per KV head npw = W splits waves hold
-    // quarters, W = Q / (4 splits) clamped to 1 .. NW (a wave is added only once every wave has
-    // four quarters, a page's worth), splits first: wave pw = s + splits * wave takes quarters
-    // pw, pw + npw, pw + 2 npw, ..., four at a time.  Quarters beyond an even share land one per
-    // wave: a quarter's work more, not a page's on a SIMD that is busy with another page.
+    // quarters, splits first: wave pw = s + splits * wave takes quarters pw, pw + npw,
+    // pw + 2 npw, ..., four at a time.  With x = Q / (4 splits) quarter groups per split, W is
+    // ceil(x) while that is at most 4 (one wave per SIMD, each with at most one group), 4 up to
+    // x = 8 (a fifth wave would share a SIMD with a busy one: the quarters beyond an even share
+    // go one per wave instead), 8 beyond (two waves per SIMD, evenly loaded).
     Q = max(0, min((T + 3) >> 2, 4 * a.n_pages));  // never index outside the page table
-    const int W = min(NW, max(1, Q / (4 * a.splits)));
+    const int q4 = 4 * a.splits;
+    const int W = Q <= 4 * q4 ? max(1, (Q + q4 - 1) / q4) : (Q < 8 * q4 ? 4 : NW);
+    static_assert(NW == 8, "the wave counts above assume 8 waves on 4 SIMDs");
     npw = W * a.splits;
     pw = s + a.splits * wave;
     nq = (wave < W && pw < Q) ? (Q - pw + npw - 1) / npw : 0;
@@ -234,6 +237,32 @@ struct AttnUnit {
 
   // Requests quarters 4 k .. 4 k + 3 of this wave into buffer b (t0 = T for a quarter past the
   // wave's share or on an unmapped page: its tokens are masked, nothing is read).
+  // The page-table entries of quarters 4 k .. 4 k + 3 of this wave, one per lane 0 .. 3 (-1
+  // past the wave's share): one load for the group.
+  __device__ __forceinline__ int group_entries(const AttnArgs &a, int k, int lane) const {
+    return (lane < 4 && 4 * k + lane < nq) ? a.page_table[(pw + npw * (4 * k + lane)) >> 2] : -1;
+  }
+
+  // Requests the rows of quarters 4 k .. 4 k + 3 into buffer b, their page-table entries from
+  // group_entries (lane sub holds the entry of quarter 4 k + sub).
+  __device__ __forceinline__ void rows_of(int ent, int j, int k, int b, int slot, int part, const AttnArgs &a) {
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const int i = 4 * k + sub;
+      t0[b][sub] = T;
+      if (i < nq) {
+        const int g = pw + npw * i;
+        const int phys = __builtin_amdgcn_readlane(ent, sub);
+        if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
+          t0[b][sub] = 4 * g;
+          const size_t row = (((size_t)phys * a.Hkv + j) * 16 + (g & 3) * 4 + slot) * D + part * DPL;
+          kp[b][sub].load(kr, (uint32_t)(row * EB));
+          vp[b][sub].load(vr, (uint32_t)(row * EB));
+        }
+      }
+    }
+  }
+
   __device__ __forceinline__ void load_group(const AttnArgs &a, int j, int k, int b, int slot, int part) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
@@ -378,11 +407,15 @@ struct AttnUnit {
     }
     attend_quarters<D, G, KVF>(kq, vq, tq, nsub, T, slot, q, m, l, o);
   };
+  // later groups (long contexts): each group's four page-table entries come in one load, made
+  // one group ahead, so a group costs one round trip for its rows only
+  int ent = 4 * PF < nq ? group_entries(a, PF, lane) : -1;
 #pragma unroll
   for (int i = 0; i < PF; ++i)
     if (4 * i < nq) group(kp[i], vp[i], t0[i], min(4, nq - 4 * i));
   for (int k = PF; 4 * k < nq; ++k) {
-    load_group(a, j, k, 0, slot, part);
+    rows_of(ent, j, k, 0, slot, part, a);
+    if (4 * (k + 1) < nq) ent = group_entries(a, k + 1, lane);
     group(kp[0], vp[0], t0[0], min(4, nq - 4 * k));
   }
 

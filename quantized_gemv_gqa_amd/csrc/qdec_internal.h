@@ -83,7 +83,9 @@ constexpr int kMaxGemvWaves = 16;   // waves per workgroup (1024 threads)
 struct GemvPlan {
   int tiles, nch, ks, cps, units, blocks, wpb;  // wpb: waves per workgroup
 };
-GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split);
+// target_small > 0: the waves a launch aims for on matrices of up to 128 tiles, in place of the
+// decode GEMV's default
+GemvPlan gemv_plan(int wfmt, int N, int K, bool allow_split, int target_small = 0);
 void gemv_set_grid(GemvPlan &p);  // blocks and waves per workgroup of a plain launch
 // Copy the plan into the arguments a kernel reads (k-splits, runs per split, INT4 group as a
 // shift): every launch path calls it once, after the arguments are filled.

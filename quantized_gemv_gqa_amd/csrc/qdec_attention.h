@@ -165,7 +165,8 @@ struct AttnSmem {
   static constexpr int NW = kAttnWaves;
   static constexpr int C = G * D / 4;  // f32x4 columns of a split's partial output
   float m[NW][G], l[NW][G];
-  // per-wave partial outputs, then a merged head's per-row sums (kAttnThreads of them)
+  // per-wave partial outputs, then a merged head's per-row sums (kAttnThreads of them), or the
+  // split weights of all G heads (standalone merge)
   f32x4 o[NW * C > kAttnThreads ? NW * C : kAttnThreads];
   float w[kMaxMergeSplits], ls[kMaxMergeSplits];  // a merged head's split weights and sums
   float q[ROPE ? (G + 2) * D : 1];
@@ -585,8 +586,8 @@ struct AttnUnit {
   __syncthreads();
   mark(rec, 2);
   if (!last) return;
-  // the last split block of KV head j merges its G query heads, one after another
-  for (int hh = 0; hh < G; ++hh) merge_head<false>(a, j * G + hh, sm, 0u);
+  // the last split block of KV head j merges its G query heads, all at once
+  merge_heads_all(a, j, sm);
   if (threadIdx.x == 0) __hip_atomic_store(&a.counters[j * kLine], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   mark(rec, 3);
   }
@@ -713,6 +714,51 @@ struct AttnUnit {
     }
     __syncthreads();  // (the next head reuses the LDS above)
     return ok;
+  }
+
+  // The merge of all G query heads of KV head j in the standalone kernels (the last split to
+  // arrive): wave h merges head j G + h, lane c < D / 4 column c, with merge_head's summation
+  // order (row r adds splits r, r + RH, r + 2 RH, ... in that order; the rows are then added in
+  // row order), so the fused and standalone kernels agree bit for bit.
+  __device__ __forceinline__ void merge_heads_all(const AttnArgs &a, int j, AttnSmem<D, G, ROPE> &sm) {
+    constexpr int CH = D / 4;                // f32x4 columns of one head
+    constexpr int RH = kAttnThreads / CH;    // split rows: 16 at D = 128, 32 at D = 64
+    static_assert(G <= kAttnWaves, "one wave per head");
+    static_assert(sizeof(sm.o) >= 2 * G * kMaxMergeSplits * sizeof(float), "the heads' weights fit");
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int S = a.splits;
+    float *const mw = reinterpret_cast<float *>(sm.o);      // [G][kMaxMergeSplits]
+    float *const ml = mw + G * kMaxMergeSplits;             // [G][kMaxMergeSplits]
+    const __amdgpu_buffer_rsrc_t orr = rsrc(a.ws, (uint32_t)((size_t)S * a.Hq * D * 4));
+    const __amdgpu_buffer_rsrc_t mlr = rsrc(a.ws + (size_t)S * a.Hq * D, (uint32_t)((size_t)S * a.Hq * 2 * 4));
+    __syncthreads();  // (every wave is done with the partials in sm.o)
+    for (int i = t; i < G * S; i += kAttnThreads) {
+      const int h = i / S, ss = i - h * S;
+      const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, (uint32_t)(((size_t)ss * a.Hq + j * G + h) * 8), 0, kAuxSc1));
+      mw[h * kMaxMergeSplits + ss] = __builtin_bit_cast(float, (uint32_t)v);
+      ml[h * kMaxMergeSplits + ss] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+    }
+    __syncthreads();
+    if (wave < G) merge_weights(mw + wave * kMaxMergeSplits, ml + wave * kMaxMergeSplits, S, 0, lane);
+    __syncthreads();
+    if (wave < G && lane < CH) {
+      const float *const ww = mw + wave * kMaxMergeSplits;
+      f32x4 out = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < RH; ++r) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ss = r; ss < S; ss += RH) {
+          const f32x4 o = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, (uint32_t)((((size_t)ss * a.Hq + j * G + wave) * D + 4 * lane) * 4), 0, kAuxSc1));
+          acc += ww[ss] * o;
+        }
+        if (r == 0)
+          out = acc;
+        else
+          out += acc;
+      }
+      *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + wave) * D + 4 * lane) = out;
+    }
+    __syncthreads();
   }
 
   // The split weights of a merge (wave 0): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.

@@ -4,14 +4,20 @@ Each mutant is a copy of the oracle source with one plausible mistake planted in
 term, a wrong sign, a wrong index, a swapped operand), compiled to a temporary library.  The
 pins of tests/oracle_pins.py must reject every mutant; a mutant that passes them all means a
 class of mistakes the pins cannot see.
+
+Every mutant runs in a child process of its own: a planted index mistake can write outside an
+array (a sequence reading another sequence's block table reaches an unallocated -1 entry), and
+the heap it corrupts must not be the test runner's.  A child that dies of a signal has been
+caught too: the mistake is loud.
 """
+import concurrent.futures
 import os
 import subprocess
+import sys
 
 import pytest
 
 import oracle as O
-import oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(O.__file__), "qdec_oracle.c")
 
@@ -81,32 +87,57 @@ MUTANTS = [
 ]
 
 
-@pytest.fixture(scope="module")
-def source():
-    with open(SRC) as f:
-        return f.read()
+_CHILD = r"""
+import sys
+sys.path[:0] = sys.argv[2:]
+import oracle as O
+import oracle_pins as P
+O.use_library(sys.argv[1])
+for chk in P.ALL_CHECKS:
+    try:
+        chk()
+    except AssertionError:
+        print("caught by", chk.__name__)
+        break
+else:
+    print("passed every pin")
+"""
 
 
-@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_reject_mutant(name, edits, source, tmp_path):
+def _run_mutant(name, edits, source, work):
     src = source
     for old, new in edits:
-        assert src.count(old) == 1, f"mutation site for {name} not unique: {old!r}"
+        if src.count(old) != 1:
+            return None, f"mutation site for {name} not unique: {old!r}", ""
         src = src.replace(old, new)
-    c = tmp_path / "mutant.c"
-    c.write_text(src)
-    so = tmp_path / "libmutant.so"
+    c = os.path.join(work, name + ".c")
+    with open(c, "w") as f:
+        f.write(src)
+    so = os.path.join(work, "lib" + name + ".so")
     subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-                           "-I", os.path.dirname(SRC), str(c), "-o", str(so), "-lm"])
-    caught = []
-    try:
-        O.use_library(str(so))
-        for chk in P.ALL_CHECKS:
-            try:
-                chk()
-            except AssertionError:
-                caught.append(chk.__name__)
-                break
-    finally:
-        O.use_library(None)
-    assert caught, f"mutant {name} passed every pin"
+                           "-I", os.path.dirname(SRC), c, "-o", so, "-lm"])
+    tests = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-c", _CHILD, so, tests, os.path.dirname(tests)],
+                       capture_output=True, text=True, env=env, timeout=600)
+    return r.returncode, r.stdout, r.stderr
+
+
+@pytest.fixture(scope="module")
+def verdicts(tmp_path_factory):
+    with open(SRC) as f:
+        source = f.read()
+    work = str(tmp_path_factory.mktemp("mutants"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        futs = {name: ex.submit(_run_mutant, name, edits, source, work) for name, edits in MUTANTS}
+        return {name: f.result() for name, f in futs.items()}
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_pins_reject_mutant(name, verdicts):
+    rc, out, err = verdicts[name]
+    assert rc is not None, out
+    if rc < 0:
+        return  # the planted mistake crashed the oracle (e.g. an out-of-bounds write)
+    assert rc == 0, f"mutant {name}: child failed\n{err[-2000:]}"
+    assert "caught by" in out, f"mutant {name} passed every pin"

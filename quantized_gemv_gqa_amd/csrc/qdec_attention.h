@@ -191,7 +191,7 @@ struct AttnUnit {
   // carry long-running loads of other roles (which in-order memory counters would make these
   // steps wait for).
   static constexpr int kRopeWaves = 4;
-  int pos, T, Q, npw, pw, nq, last_page;
+  int pos, T, Q, npw, pw, gb, nq, last_page;
   int nwp;       // waves of this split that hold quarters (the first ones)
   unsigned ep;   // the step number (SYNC)
   __amdgpu_buffer_rsrc_t kr, vr;
@@ -207,20 +207,36 @@ struct AttnUnit {
     pos = *a.pos;
     T = pos + 1;
     // The context is dealt in quarters of a page (4 tokens; quarter g is sub-block g % 4 of page
-    // g / 4) so that the work spreads evenly over the SIMDs: per KV head npw = W splits waves hold
-    // quarters, splits first: wave pw = s + splits * wave takes quarters pw, pw + npw,
-    // pw + 2 npw, ..., four at a time.  With x = Q / (4 splits) quarter groups per split, W is
-    // ceil(x) while that is at most 4 (one wave per SIMD, each with at most one group), 4 up to
-    // x = 8 (a fifth wave would share a SIMD with a busy one: the quarters beyond an even share
-    // go one per wave instead), 8 beyond (two waves per SIMD, evenly loaded).
+    // g / 4) so that the work spreads evenly over the SIMDs and no wave waits for a second round
+    // trip it could have shared out: per KV head npw = W splits waves hold quarters, splits
+    // first: wave pw = s + splits * wave takes quarters gb + pw, gb + pw + npw, ..., four at a
+    // time.  With x = Q / (4 splits) quarter groups per split:
+    //   x <= 4: W = ceil(x) waves (one per SIMD), each with at most one group;
+    //   4 < x <= 8: waves 0 .. 3 take the first 16 splits quarters, exactly one group each, and
+    //     waves 4 .. 7 (gb = 16 splits) the rest, at most one group each: a group beyond the
+    //     first on one wave would cost its split a serial round trip (the step just past a
+    //     context of 16 splits pages leaves one such quarter);
+    //   x > 8: all 8 waves (two per SIMD, evenly loaded).
     Q = max(0, min((T + 3) >> 2, 4 * a.n_pages));  // never index outside the page table
     const int q4 = 4 * a.splits;
-    const int W = Q <= 4 * q4 ? max(1, (Q + q4 - 1) / q4) : (Q < 8 * q4 ? 4 : NW);
     static_assert(NW == 8, "the wave counts above assume 8 waves on 4 SIMDs");
-    npw = W * a.splits;
-    pw = s + a.splits * wave;
-    nq = (wave < W && pw < Q) ? (Q - pw + npw - 1) / npw : 0;
-    nwp = Q > s ? min(W, (Q - s + a.splits - 1) / a.splits) : 0;  // wave < nwp  <=>  nq > 0
+    gb = 0;
+    if (Q > 4 * q4 && Q <= 8 * q4) {
+      const int hi = wave >= 4;
+      const int Qh = hi ? Q - 4 * q4 : 4 * q4;  // the quarters of this half of the waves
+      gb = hi ? 4 * q4 : 0;
+      npw = q4;
+      pw = s + a.splits * (wave - 4 * hi);
+      nq = pw < Qh ? (Qh - pw + npw - 1) / npw : 0;
+      const int R = Q - 4 * q4;
+      nwp = 4 + (R > s ? min(4, (R - s + a.splits - 1) / a.splits) : 0);  // wave < nwp  <=>  nq > 0
+    } else {
+      const int W = Q <= 4 * q4 ? max(1, (Q + q4 - 1) / q4) : NW;
+      npw = W * a.splits;
+      pw = s + a.splits * wave;
+      nq = (wave < W && pw < Q) ? (Q - pw + npw - 1) / npw : 0;
+      nwp = Q > s ? min(W, (Q - s + a.splits - 1) / a.splits) : 0;  // wave < nwp  <=>  nq > 0
+    }
     last_page = ((T + 15) >> 4) - 1;
     if constexpr (ROPE) {
       if (wave < kRopeWaves) {
@@ -241,7 +257,7 @@ struct AttnUnit {
   // The page-table entries of quarters 4 k .. 4 k + 3 of this wave, one per lane 0 .. 3 (-1
   // past the wave's share): one load for the group.
   __device__ __forceinline__ int group_entries(const AttnArgs &a, int k, int lane) const {
-    return (lane < 4 && 4 * k + lane < nq) ? a.page_table[(pw + npw * (4 * k + lane)) >> 2] : -1;
+    return (lane < 4 && 4 * k + lane < nq) ? a.page_table[(gb + pw + npw * (4 * k + lane)) >> 2] : -1;
   }
 
   // Requests the rows of quarters 4 k .. 4 k + 3 into buffer b, their page-table entries from
@@ -252,7 +268,7 @@ struct AttnUnit {
       const int i = 4 * k + sub;
       t0[b][sub] = T;
       if (i < nq) {
-        const int g = pw + npw * i;
+        const int g = gb + pw + npw * i;
         const int phys = __builtin_amdgcn_readlane(ent, sub);
         if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
           t0[b][sub] = 4 * g;
@@ -270,7 +286,7 @@ struct AttnUnit {
       const int i = 4 * k + sub;
       t0[b][sub] = T;
       if (i < nq) {
-        const int g = pw + npw * i;
+        const int g = gb + pw + npw * i;
         const int phys = a.page_table[g >> 2];
         if (phys >= 0 && phys < a.n_pages) {  // documented precondition; never read outside
           t0[b][sub] = 4 * g;

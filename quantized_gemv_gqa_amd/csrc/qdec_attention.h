@@ -608,113 +608,128 @@ struct AttnUnit {
   mark(rec, 3);
   }
 
-  // The merge of query head h's split partials:
-  //   out[h][d] = sum_s w_s o_s[d],  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s',  M = max_s m_s,
-  // splits without keys (m = -1e30, l = 0, o = 0) weighing nothing.  Fixed order whatever the
-  // caller: thread (r, c) adds column c (4 dims) of splits r, r + RH, r + 2 RH, ... in that order,
-  // then the RH rows are added in row order.  TAGGED (the fused launch): the partials are
-  // (value, tag) pairs, all requested at once and polled until every tag equals `tag`, and the
-  // output is stored as tagged pairs in tout; else plain values of a finished launch phase, and the
-  // output is stored in out.  Returns false if a poll gave up (the error word is then set).
+  // The merge of query head h's split partials (m_s, l_s, o_s; a split without keys has
+  // m = -1e30, l = 0, o = 0 and weighs nothing):
+  //   out[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+  // in a fixed order whatever the caller: row r of RH takes splits r, r + RH, r + 2 RH, ... in
+  // bursts of kBurst (MergeState::add, a running maximum with its rescaled sums), then the rows
+  // are folded in row order (MergeState::fold).  The fused and standalone kernels agree bit for
+  // bit.
+  static constexpr int CH = D / 4;                // f32x4 columns of one head
+  static constexpr int RH = kAttnThreads / CH;    // split rows: 16 at D = 128, 32 at D = 64
+  static constexpr int kBurst = 4;                // splits of a row in flight at once
+
+  struct MergeState {
+    float M, l;
+    f32x4 acc;
+    __device__ __forceinline__ MergeState() : M(kNegBig), l(0.f), acc{0.f, 0.f, 0.f, 0.f} {}
+    __device__ __forceinline__ void rescale(float Mn) {
+      const float sc = __builtin_amdgcn_exp2f(M - Mn);
+      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+      l *= sc;
+      M = Mn;
+    }
+    __device__ __forceinline__ void add_one(float p, float lv, f32x4 o) {
+      acc.x = fmaf(p, o.x, acc.x); acc.y = fmaf(p, o.y, acc.y);
+      acc.z = fmaf(p, o.z, acc.z); acc.w = fmaf(p, o.w, acc.w);
+      l = fmaf(p, lv, l);
+    }
+    // splits u < n of a burst
+    __device__ __forceinline__ void add(const float (&m)[kBurst], const float (&lv)[kBurst], const f32x4 (&o)[kBurst], int n) {
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < kBurst; ++u)
+        if (u < n) Mn = fmaxf(Mn, m[u]);
+      rescale(Mn);
+#pragma unroll
+      for (int u = 0; u < kBurst; ++u)
+        if (u < n) add_one(__builtin_amdgcn_exp2f(m[u] - Mn), lv[u], o[u]);
+    }
+    // the next row's state
+    __device__ __forceinline__ void fold(float Mr, float lr, f32x4 ar) {
+      rescale(fmaxf(M, Mr));
+      add_one(__builtin_amdgcn_exp2f(Mr - M), lr, ar);
+    }
+    __device__ __forceinline__ f32x4 out() const {
+      const float inv = 1.0f / l;
+      return f32x4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    }
+  };
+
+  // TAGGED (the fused launch): the partials are (value, tag) pairs; a thread requests the (m, l)
+  // pair and the column of each split of its burst at once and requests again, all together,
+  // whichever came back with another tag, until every tag equals `tag` (so the last split to
+  // publish costs one round trip once its stores are visible, and the polls after the first
+  // reread only the splits still missing); the output is stored as tagged pairs in tout.  Else
+  // plain values of a finished launch phase, and the output is stored in out.  Returns false if
+  // a poll gave up (the error word is then set).
   template <bool TAGGED>
   __device__ __forceinline__ bool merge_head(const AttnArgs &a, int h, AttnSmem<D, G, ROPE> &sm, unsigned tag) {
-    constexpr int CH = D / 4;                // f32x4 columns of one head
-    constexpr int RH = kAttnThreads / CH;    // split rows: 16 at D = 128, 32 at D = 64
-    constexpr int kBurst = 4;                // partial columns a thread has in flight
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     const int r = t / CH, c = t - r * CH;
     const int S = a.splits;
-    float *const ww = sm.w;
-    float *const wl = sm.ls;
     bool ok = true;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    MergeState row;
     if constexpr (TAGGED) {
       const __amdgpu_buffer_rsrc_t tor = rsrc(a.tws, (uint32_t)((size_t)S * a.Hq * D * 8));
       const __amdgpu_buffer_rsrc_t tmr = rsrc(a.tws + (size_t)S * a.Hq * D * 2, (uint32_t)((size_t)S * a.Hq * 16));
-      auto col_off = [&](int ss) { return ss < S ? (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 8) : 0x80000000u; };
-      // the first burst of partial columns goes out with the (m, l) requests
-      u32x4 lo[kBurst], hi[kBurst];
+      for (int s0 = r; s0 < S; s0 += RH * kBurst) {
+        const int n = min(kBurst, (S - s0 + RH - 1) / RH);
+        u32x4 ml[kBurst], lo[kBurst], hi[kBurst];
+        bool have[kBurst];
 #pragma unroll
-      for (int u = 0; u < kBurst; ++u) {
-        lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(r + RH * u), 0, kAuxSc1));
-        hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(r + RH * u) + 16, 0, kAuxSc1));
-      }
-      for (int i = t; i < S; i += kAttnThreads) {
-        const uint32_t off = (uint32_t)(((size_t)i * a.Hq + h) * 16);
-        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tmr, off, 0, kAuxSc1));
-        unsigned spins = 0;
-        while (v.y != tag || v.w != tag) {
+        for (int u = 0; u < kBurst; ++u) have[u] = u >= n;
+        for (unsigned spins = 0;;) {
+#pragma unroll
+          for (int u = 0; u < kBurst; ++u) {
+            if (have[u]) continue;
+            const int ss = s0 + RH * u;
+            const uint32_t oo = (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 8);
+            ml[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tmr, (uint32_t)(((size_t)ss * a.Hq + h) * 16), 0, kAuxSc1));
+            lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, oo, 0, kAuxSc1));
+            hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, oo + 16, 0, kAuxSc1));
+          }
+          bool all = true;
+#pragma unroll
+          for (int u = 0; u < kBurst; ++u) {
+            if (!have[u])
+              have[u] = ml[u].y == tag && ml[u].w == tag && lo[u].y == tag && lo[u].w == tag && hi[u].y == tag && hi[u].w == tag;
+            all = all && have[u];
+          }
+          if (all) break;
           if (!poll_step(spins, a.err)) {
             ok = false;
-            v.x = __builtin_bit_cast(uint32_t, kNegBig); v.y = tag; v.z = 0u; v.w = tag;
             break;
           }
-          v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tmr, off, 0, kAuxSc1));
         }
-        // (whole-vector bit casts: a bit cast of one element of a vector compiles to element 0)
-        const f32x4 vf = __builtin_bit_cast(f32x4, v);
-        ww[i] = vf.x;
-        wl[i] = vf.z;
-      }
-      __syncthreads();
-      merge_weights(ww, wl, S, wave, lane);
-      __syncthreads();
-      for (int s0 = r;; ) {
+        if (!ok) break;
+        float m[kBurst], lv[kBurst];
+        f32x4 o[kBurst];
 #pragma unroll
         for (int u = 0; u < kBurst; ++u) {
-          const int ss = s0 + RH * u;
-          if (ss >= S) break;
-          unsigned spins = 0;
-          while (ok && (lo[u].y != tag || lo[u].w != tag || hi[u].y != tag || hi[u].w != tag)) {
-            if (!poll_step(spins, a.err)) { ok = false; break; }
-            lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(ss), 0, kAuxSc1));
-            hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(ss) + 16, 0, kAuxSc1));
-          }
+          // (whole-vector bit casts: a bit cast of one element of a vector compiles to element 0)
+          const f32x4 mf = __builtin_bit_cast(f32x4, ml[u]);
           const f32x4 lf = __builtin_bit_cast(f32x4, lo[u]), hf = __builtin_bit_cast(f32x4, hi[u]);
-          const f32x4 o = {lf.x, lf.z, hf.x, hf.z};
-          acc += ww[ss] * o;
+          m[u] = mf.x;
+          lv[u] = mf.z;
+          o[u] = f32x4{lf.x, lf.z, hf.x, hf.z};
         }
-        s0 += RH * kBurst;
-        if (s0 >= S) break;
-#pragma unroll
-        for (int u = 0; u < kBurst; ++u) {
-          lo[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(s0 + RH * u), 0, kAuxSc1));
-          hi[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tor, col_off(s0 + RH * u) + 16, 0, kAuxSc1));
-        }
+        row.add(m, lv, o, n);
       }
     } else {
-      const __amdgpu_buffer_rsrc_t orr = rsrc(a.ws, (uint32_t)((size_t)S * a.Hq * D * 4));
-      const __amdgpu_buffer_rsrc_t mlr = rsrc(a.ws + (size_t)S * a.Hq * D, (uint32_t)((size_t)S * a.Hq * 2 * 4));
-      for (int i = t; i < S; i += kAttnThreads) {
-        const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, (uint32_t)(((size_t)i * a.Hq + h) * 8), 0, kAuxSc1));
-        ww[i] = __builtin_bit_cast(float, (uint32_t)v);
-        wl[i] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
-      }
-      __syncthreads();
-      merge_weights(ww, wl, S, wave, lane);
-      __syncthreads();
-      for (int s0 = r; s0 < S; s0 += RH * kBurst) {
-        f32x4 ov[kBurst];
-#pragma unroll
-        for (int u = 0; u < kBurst; ++u) {
-          const int ss = s0 + RH * u;
-          const uint32_t off = ss < S ? (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 4) : 0x80000000u;
-          ov[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, off, 0, kAuxSc1));
-        }
-#pragma unroll
-        for (int u = 0; u < kBurst; ++u) {
-          const int ss = s0 + RH * u;
-          if (ss >= S) break;
-          acc += ww[ss] * ov[u];
-        }
-      }
+      load_row(a, h, r, c, row);
     }
-    sm.o[r * CH + c] = acc;
+    sm.o[r * CH + c] = row.acc;
+    if (c == 0) {
+      sm.w[r] = row.M;
+      sm.ls[r] = row.l;
+    }
     __syncthreads();
     if (t < CH) {
-      f32x4 out = sm.o[t];
+      MergeState tot;
 #pragma unroll
-      for (int rr = 1; rr < RH; ++rr) out += sm.o[rr * CH + t];
+      for (int rr = 0; rr < RH; ++rr) tot.fold(sm.w[rr], sm.ls[rr], sm.o[rr * CH + t]);
+      const f32x4 out = tot.out();
       if constexpr (TAGGED) {
         const u32x4 vb = __builtin_bit_cast(u32x4, out);
         u32x4 p0, p1;
@@ -732,62 +747,47 @@ struct AttnUnit {
     return ok;
   }
 
-  // The merge of all G query heads of KV head j in the standalone kernels (the last split to
-  // arrive): wave h merges head j G + h, lane c < D / 4 column c, with merge_head's summation
-  // order (row r adds splits r, r + RH, r + 2 RH, ... in that order; the rows are then added in
-  // row order), so the fused and standalone kernels agree bit for bit.
-  __device__ __forceinline__ void merge_heads_all(const AttnArgs &a, int j, AttnSmem<D, G, ROPE> &sm) {
-    constexpr int CH = D / 4;                // f32x4 columns of one head
-    constexpr int RH = kAttnThreads / CH;    // split rows: 16 at D = 128, 32 at D = 64
-    static_assert(G <= kAttnWaves, "one wave per head");
-    static_assert(sizeof(sm.o) >= 2 * G * kMaxMergeSplits * sizeof(float), "the heads' weights fit");
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // Row r of head h's merge from the plain partials of a finished phase: o at [s][head][D],
+  // (m, l) at [s][head][2].
+  __device__ __forceinline__ static void load_row(const AttnArgs &a, int h, int r, int c, MergeState &row) {
     const int S = a.splits;
-    float *const mw = reinterpret_cast<float *>(sm.o);      // [G][kMaxMergeSplits]
-    float *const ml = mw + G * kMaxMergeSplits;             // [G][kMaxMergeSplits]
     const __amdgpu_buffer_rsrc_t orr = rsrc(a.ws, (uint32_t)((size_t)S * a.Hq * D * 4));
     const __amdgpu_buffer_rsrc_t mlr = rsrc(a.ws + (size_t)S * a.Hq * D, (uint32_t)((size_t)S * a.Hq * 2 * 4));
-    __syncthreads();  // (every wave is done with the partials in sm.o)
-    for (int i = t; i < G * S; i += kAttnThreads) {
-      const int h = i / S, ss = i - h * S;
-      const uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, (uint32_t)(((size_t)ss * a.Hq + j * G + h) * 8), 0, kAuxSc1));
-      mw[h * kMaxMergeSplits + ss] = __builtin_bit_cast(float, (uint32_t)v);
-      ml[h * kMaxMergeSplits + ss] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
-    }
-    __syncthreads();
-    if (wave < G) merge_weights(mw + wave * kMaxMergeSplits, ml + wave * kMaxMergeSplits, S, 0, lane);
-    __syncthreads();
-    if (wave < G && lane < CH) {
-      const float *const ww = mw + wave * kMaxMergeSplits;
-      f32x4 out = {0.f, 0.f, 0.f, 0.f};
-      for (int r = 0; r < RH; ++r) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int ss = r; ss < S; ss += RH) {
-          const f32x4 o = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, (uint32_t)((((size_t)ss * a.Hq + j * G + wave) * D + 4 * lane) * 4), 0, kAuxSc1));
-          acc += ww[ss] * o;
-        }
-        if (r == 0)
-          out = acc;
-        else
-          out += acc;
+    for (int s0 = r; s0 < S; s0 += RH * kBurst) {
+      const int n = min(kBurst, (S - s0 + RH - 1) / RH);
+      float m[kBurst], lv[kBurst];
+      f32x4 o[kBurst];
+#pragma unroll
+      for (int u = 0; u < kBurst; ++u) {
+        const int ss = s0 + RH * u;
+        const bool in = u < n;
+        const uint64_t v = __builtin_bit_cast(
+            uint64_t, __builtin_amdgcn_raw_buffer_load_b64(mlr, in ? (uint32_t)(((size_t)ss * a.Hq + h) * 8) : 0x80000000u, 0, kAuxSc1));
+        m[u] = __builtin_bit_cast(float, (uint32_t)v);
+        lv[u] = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+        o[u] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, in ? (uint32_t)((((size_t)ss * a.Hq + h) * D + 4 * c) * 4) : 0x80000000u, 0, kAuxSc1));
       }
-      *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + wave) * D + 4 * lane) = out;
+      row.add(m, lv, o, n);
     }
-    __syncthreads();
   }
 
-  // The split weights of a merge (wave 0): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
-  __device__ __forceinline__ static void merge_weights(float *ww, const float *wl, int S, int wave, int lane) {
-    if (wave != 0) return;
-    float M = kNegBig;
-    for (int i = lane; i < S; i += 64) M = fmaxf(M, ww[i]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int i = lane; i < S; i += 64) L = fmaf(__builtin_amdgcn_exp2f(ww[i] - M), wl[i], L);
-    L = wave_sum(L);
-    const float inv = 1.0f / L;
-    for (int i = lane; i < S; i += 64) ww[i] = __builtin_amdgcn_exp2f(ww[i] - M) * inv;
+  // The merge of all G query heads of KV head j in the standalone kernels (the last split to
+  // arrive): wave h merges head j G + h, lane c < D / 4 column c, row by row in merge_head's
+  // order, folding each row as it is done.
+  __device__ __forceinline__ void merge_heads_all(const AttnArgs &a, int j, AttnSmem<D, G, ROPE> &sm) {
+    static_assert(G <= kAttnWaves, "one wave per head");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave < G && lane < CH) {
+      MergeState tot;
+      for (int r = 0; r < RH; ++r) {
+        MergeState row;
+        load_row(a, j * G + wave, r, lane, row);
+        tot.fold(row.M, row.l, row.acc);
+      }
+      *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + wave) * D + 4 * lane) = tot.out();
+    }
+    __syncthreads();
   }
 };
 

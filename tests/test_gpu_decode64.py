@@ -25,6 +25,8 @@ a free run re-checks one token id; a second run feeds 64 distinct seeded token i
 The greedy argmax fused into the lm head's epilogue is checked for its tie rule (smallest index
 among the maxima, across tiles of different reduction groups) with constructed lm-head rows.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -169,8 +171,15 @@ class Run:
 
 
 @pytest.mark.parametrize("name", ["qwen2.5-7b-q4", "qwen2.5-1.5b-q8", "qwen3-8b-q8", "qwen2.5-7b-q4-32k"])
+def _progress(name, s, t0):
+    """One line per step (seen under pytest -s): a step of a large model with its oracle takes
+    seconds of CPU time."""
+    print("%s step %d done, %.1f s" % (name, s, time.time() - t0), flush=True)
+
+
 def test_greedy_64_steps_match_oracle(name):
     """64 free-running greedy steps on both sides, graph replay, every layer checked every step."""
+    t0 = time.time()
     r = Run(name)
     pos0 = r.wl.ctx
     tok = r.model["token"]
@@ -189,6 +198,7 @@ def test_greedy_64_steps_match_oracle(name):
                 ties.append((s, gtok, ref["token"], m))
                 r.gpu.token.fill_(ref["token"])  # continue both sides from the oracle's token
             tok = ref["token"]
+            _progress(name, s, t0)
         sync()
     assert r.gpu.read_error() == 0
     assert int(host(r.gpu.pos)[0]) == pos0 + STEPS
@@ -201,6 +211,7 @@ def test_teacher_forced_64_distinct_tokens():
     """The Qwen2.5-7B-shape INT4 model fed 64 distinct seeded token ids on both sides (the
     token, position, KV append and attention differ at every step): per-layer hidden states and
     logits at every step, and each step's greedy token against the oracle's."""
+    t0 = time.time()
     r = Run("qwen2.5-7b-q4")
     pos0 = r.wl.ctx
     toks = np.random.default_rng(20261202).choice(r.wl.vocab, STEPS, replace=False).astype(np.int32)
@@ -216,6 +227,7 @@ def test_teacher_forced_64_distinct_tokens():
                 argmax_equal += 1
             else:
                 assert _margin(ref["logits"]) <= LOGIT_TOL, (s, gtok, ref["token"])
+            _progress("teacher-forced", s, t0)
         sync()
     assert r.gpu.read_error() == 0
     print("teacher-forced: %d/%d greedy tokens identical, %d distinct outputs, cache codes synced at %d steps, "

@@ -170,13 +170,13 @@ class Run:
         return ref
 
 
-@pytest.mark.parametrize("name", ["qwen2.5-7b-q4", "qwen2.5-1.5b-q8", "qwen3-8b-q8", "qwen2.5-7b-q4-32k"])
 def _progress(name, s, t0):
     """One line per step (seen under pytest -s): a step of a large model with its oracle takes
     seconds of CPU time."""
     print("%s step %d done, %.1f s" % (name, s, time.time() - t0), flush=True)
 
 
+@pytest.mark.parametrize("name", ["qwen2.5-7b-q4", "qwen2.5-1.5b-q8", "qwen3-8b-q8", "qwen2.5-7b-q4-32k"])
 def test_greedy_64_steps_match_oracle(name):
     """64 free-running greedy steps on both sides, graph replay, every layer checked every step."""
     t0 = time.time()

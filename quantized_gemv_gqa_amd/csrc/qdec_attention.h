@@ -773,21 +773,64 @@ struct AttnUnit {
   }
 
   // The merge of all G query heads of KV head j in the standalone kernels (the last split to
-  // arrive): wave h merges head j G + h, lane c < D / 4 column c, row by row in merge_head's
-  // order, folding each row as it is done.
+  // arrive), by the whole workgroup: the row states (head, row r, column c) of a share of the rows
+  // at a time (as many as the LDS holds), every thread taking several with all their loads in
+  // flight, go to LDS; thread (head, c) then folds them in row order, so the result is
+  // merge_head's bit for bit.
+  static constexpr int kMergeSlots = (int)(sizeof(AttnSmem<D, G, ROPE>::o) / sizeof(f32x4));
+  static constexpr int merge_passes() {
+    int p = 1;
+    while (p < RH && (RH % p != 0 || G * (RH / p) * CH > kMergeSlots)) p *= 2;
+    return p;
+  }
   __device__ __forceinline__ void merge_heads_all(const AttnArgs &a, int j, AttnSmem<D, G, ROPE> &sm) {
-    static_assert(G <= kAttnWaves, "one wave per head");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (wave < G && lane < CH) {
-      MergeState tot;
-      for (int r = 0; r < RH; ++r) {
-        MergeState row;
-        load_row(a, j * G + wave, r, lane, row);
-        tot.fold(row.M, row.l, row.acc);
+    constexpr int NPASS = merge_passes();
+    constexpr int HALF = RH / NPASS;                      // rows per pass
+    constexpr int ITEMS = G * HALF * CH;                  // row states per pass
+    constexpr int PER = (ITEMS + kAttnThreads - 1) / kAttnThreads;
+    static_assert(ITEMS <= kMergeSlots, "a pass's row states fit");
+    static_assert(G * RH <= kMaxMergeSplits, "the rows' (M, l) fit");
+    static_assert(G * CH <= kAttnThreads, "one folding thread per head and column");
+    const int t = threadIdx.x;
+    const int fh = t / CH, fc = t - fh * CH;              // the folding thread's head and column
+    MergeState tot;
+    __syncthreads();  // (every wave is done with the partials in sm.o)
+#pragma unroll
+    for (int half = 0; half < NPASS; ++half) {
+      MergeState row[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = t + kAttnThreads * u;
+        if (i < ITEMS) {
+          const int h = i / (HALF * CH), rem = i - h * (HALF * CH);
+          const int r = half * HALF + rem / CH, c = rem - (rem / CH) * CH;
+          load_row(a, j * G + h, r, c, row[u]);
+        }
       }
-      *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + wave) * D + 4 * lane) = tot.out();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int i = t + kAttnThreads * u;
+        if (i < ITEMS) {
+          const int h = i / (HALF * CH), rem = i - h * (HALF * CH);
+          const int r = half * HALF + rem / CH, c = rem - (rem / CH) * CH;
+          sm.o[i] = row[u].acc;
+          if (c == 0) {
+            sm.w[h * RH + r] = row[u].M;
+            sm.ls[h * RH + r] = row[u].l;
+          }
+        }
+      }
+      __syncthreads();
+      if (t < G * CH) {
+#pragma unroll
+        for (int rr = 0; rr < HALF; ++rr) {
+          const int r = half * HALF + rr;
+          tot.fold(sm.w[fh * RH + r], sm.ls[fh * RH + r], sm.o[(fh * HALF + rr) * CH + fc]);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    if (t < G * CH) *reinterpret_cast<f32x4 *>(a.out + (size_t)(j * G + fh) * D + 4 * fc) = tot.out();
   }
 };
 

@@ -545,6 +545,7 @@ hipError_t launch_nb(const GemmBArgs &a, int blocks, hipStream_t st) {
 template <int FMT>
 hipError_t launch_fmt(const GemmBArgs &a, int blocks, hipStream_t st) {
   switch (a.nb_max) {
+    case 1: return launch_nb<FMT, 1>(a, blocks, st);
     case 2: return launch_nb<FMT, 2>(a, blocks, st);
     case 4: return launch_nb<FMT, 4>(a, blocks, st);
     case 8: return launch_nb<FMT, 8>(a, blocks, st);
@@ -554,7 +555,8 @@ hipError_t launch_fmt(const GemmBArgs &a, int blocks, hipStream_t st) {
 
 }  // namespace
 
-int gemm_b_columns(int batch) { return batch <= 2 ? 2 : (batch <= 4 ? 4 : 8); }
+// (one column alone: staging and multiplying a second, empty one cost a third of the time)
+int gemm_b_columns(int batch) { return batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8)); }
 
 // The k-split plan is the GEMV's (measured: splitting further for the batch only adds partial
 // sums; the waves are limited by staging the columns' activations, not by their number).

@@ -4,7 +4,7 @@
 
 namespace qdec {
 
-// Skinny GEMM (gemm_b.hip): Y[b] = W X[b] for b < nb columns, nb <= nb_max in {2, 4, 8}.
+// Skinny GEMM (gemm_b.hip): Y[b] = W X[b] for b < nb columns, nb <= nb_max in {1, 2, 4, 8}.
 struct GemmBArgs {
   const uint8_t *W;        // packed tile64 weights
   const void *S;           // packed scales
@@ -32,7 +32,7 @@ struct GemmBArgs {
   // stored outputs in rows 64 t .. 64 t + 63 (stored columns only)
   float *ssq_out;
 };
-int gemm_b_columns(int batch);  // nb_max for a batch size (2, 4 or 8)
+int gemm_b_columns(int batch);  // nb_max for a batch size (1, 2, 4 or 8)
 size_t gemm_b_workspace_bytes(int wfmt, int N, int K, int nb_max);
 hipError_t launch_gemm_b(int wfmt, GemmBArgs a, void *ws, hipStream_t st);
 

@@ -159,11 +159,11 @@ def test_batch_long_contexts_at_the_split_cap():
 
 
 @pytest.mark.parametrize("wfmt", ["q4", "q8"])
-@pytest.mark.parametrize("ctxs", [[20, 33], [20, 33, 7], [5, 9, 17, 30, 41, 47, 64, 70]])
+@pytest.mark.parametrize("ctxs", [[33], [20, 33], [20, 33, 7], [5, 9, 17, 30, 41, 47, 64, 70]])
 def test_batch_wide_hidden_matches_oracle(wfmt, ctxs):
     """Hidden 4160 (65 tiles of 64 rows): each folded RMSNorm adds more than 64 per-tile sums of
-    squares per column, and the last tile is ragged for the norm's producers; 2, 3 and 8 slots take
-    the two-column, four-column and eight-column GEMMs."""
+    squares per column, and the last tile is ragged for the norm's producers; 1, 2, 3 and 8 slots
+    take the one-, two-, four- and eight-column GEMMs."""
     from dataclasses import replace
     wl = replace(synth.WORKLOADS["qwen2.5-7b-q4"], name="wide-h4160-" + wfmt, hidden=4160, inter=512, vocab=1000,
                  wfmt=wfmt, ctx=64, shuffled_pages=True, seed=1010)

@@ -527,6 +527,10 @@ struct AttnUnit {
   unsigned &last = sm.flag;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned e = ep;
+  // the heads' (m, l) go out from the last wave, which merges no columns (C <= 256 columns sit on
+  // the first four waves), beside the columns rather than after them
+  static_assert(C <= 64 * (kAttnWaves - 1), "the last wave holds no column");
+  const int hml = (int)threadIdx.x - 64 * (kAttnWaves - 1);
   __syncthreads();
   // merge the page-holding waves into the split's partial: o (G heads x D) and per head (m, l);
   // a split without pages publishes m = -1e30, l = 0, o = 0
@@ -561,12 +565,12 @@ struct AttnUnit {
       __builtin_amdgcn_raw_buffer_store_b128(lo, tor, off, 0, kAuxSc1);
       __builtin_amdgcn_raw_buffer_store_b128(hi, tor, off + 16, 0, kAuxSc1);
     }
-    if (threadIdx.x < G) {
+    if (hml >= 0 && hml < G) {
       float mx, lsum;
-      head_ml(threadIdx.x, mx, lsum);
+      head_ml(hml, mx, lsum);
       u32x4 v;
       v.x = __builtin_bit_cast(uint32_t, mx); v.y = tag; v.z = __builtin_bit_cast(uint32_t, lsum); v.w = tag;
-      __builtin_amdgcn_raw_buffer_store_b128(v, tmr, (uint32_t)(((size_t)s * a.Hq + j * G + threadIdx.x) * 16), 0, kAuxSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(v, tmr, (uint32_t)(((size_t)s * a.Hq + j * G + hml) * 16), 0, kAuxSc1);
     }
     // every wave is done with this unit's LDS before any leaves (a kernel may reuse it next)
     __syncthreads();
@@ -586,15 +590,15 @@ struct AttnUnit {
   const __amdgpu_buffer_rsrc_t mlr = rsrc(wsml, (uint32_t)((size_t)a.splits * a.Hq * 2 * 4));
   for (int c = threadIdx.x; c < C; c += kAttnThreads)
     store_sc1_b128(orr, (uint32_t)((((size_t)s * a.Hq + j * G) * D + 4 * c) * 4), column(c));
-  if (threadIdx.x < G) {
+  if (hml >= 0 && hml < G) {
     float mx, lsum;
-    head_ml(threadIdx.x, mx, lsum);
+    head_ml(hml, mx, lsum);
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 v = {__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)};
-    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + threadIdx.x) * 2) * 4), 0, kAuxSc1);
+    __builtin_amdgcn_raw_buffer_store_b64(v, mlr, (uint32_t)((((size_t)s * a.Hq + j * G + hml) * 2) * 4), 0, kAuxSc1);
   }
   // the waves that stored wait for the acknowledgements
-  if (wave * 64 < C || wave * 64 < G) drain_stores();
+  if (wave * 64 < C || wave == kAttnWaves - 1) drain_stores();
   __syncthreads();
   if (threadIdx.x == 0)
     last = __hip_atomic_fetch_add(&a.counters[j * kLine], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==

@@ -34,10 +34,11 @@ namespace {
 using namespace dev;
 
 // Waves a launch aims for: few k-splits keep the split-K tail short on small matrices (up to 128
-// tiles), more waves stream the large ones (measured on MI355X: for the down projections, about
-// six waves per compute unit beat four and eight: one wave per SIMD hides too little latency, and
-// 35 k-splits need a second burst of partial loads in the combine).
-constexpr int kTargetUnitsSmall = 1512;
+// tiles), more waves stream the large ones (measured on MI355X: for the down projections about
+// seven waves per compute unit, the most whose k-splits still fit one burst of partial loads in
+// the combine, beat four and six; one wave per SIMD hides too little latency, and 35 k-splits
+// need a second burst).
+constexpr int kTargetUnitsSmall = 1792;
 constexpr int kTargetUnitsLarge = 2048;
 constexpr int kMinChunks = 4;       // at least 4 KiB of weights per wave
 

@@ -531,7 +531,9 @@ struct AttnUnit {
   // the first four waves), beside the columns rather than after them
   static_assert(C <= 64 * (kAttnWaves - 1), "the last wave holds no column");
   const int hml = (int)threadIdx.x - 64 * (kAttnWaves - 1);
-  __syncthreads();
+  // (an LDS-only barrier: a wave of another role may have its LDS DMA copies still in flight,
+  // into a stash no other wave reads, and must not hold the split's publish for them)
+  lds_barrier();
   // merge the page-holding waves into the split's partial: o (G heads x D) and per head (m, l);
   // a split without pages publishes m = -1e30, l = 0, o = 0
   const int nw = nwp;
@@ -572,8 +574,9 @@ struct AttnUnit {
       v.x = __builtin_bit_cast(uint32_t, mx); v.y = tag; v.z = __builtin_bit_cast(uint32_t, lsum); v.w = tag;
       __builtin_amdgcn_raw_buffer_store_b128(v, tmr, (uint32_t)(((size_t)s * a.Hq + j * G + hml) * 16), 0, kAuxSc1);
     }
-    // every wave is done with this unit's LDS before any leaves (a kernel may reuse it next)
-    __syncthreads();
+    // every wave is done with this unit's LDS before any leaves (a kernel may reuse it next; an
+    // LDS-only barrier, so that the split's stores just issued are not waited for here)
+    lds_barrier();
     mark(rec, 2);
     // query head j G + hh is merged by split hh % splits, as soon as its partials are all seen
     // (its output goes out as tagged pairs too: the o GEMV polls them, no flag needed)

@@ -35,6 +35,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Workgroup barrier for data that waves exchange through LDS with ordinary LDS instructions: the
+// wave's own LDS accesses are complete (lgkmcnt 0) before it arrives, and the compiler moves no
+// memory access across it.  Unlike __syncthreads() it does not wait for the wave's LDS DMA copies
+// (a workgroup fence counts them as LDS writes): a wave whose DMA copies into a buffer that only it
+// reads does not hold the others for them (its own later LDS reads still wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // DPP lane permutation of a float (gfx9 dpp_ctrl encodings)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -460,15 +460,16 @@ def upload_kv(kv: dict, kv_fmt: str, device="cuda") -> dict:
 
 
 def default_splits(n_kv_heads: int, ctx: int, pages_per_split: int = 4) -> int:
-    """Attention split count: at most `pages_per_split` KV pages per split (pages are dealt to the
-    splits first, so a split's pages sit on its first waves, one per SIMD of the compute unit),
-    rounded up to a multiple of 8 so a context that grows by a few pages keeps the same count, at
-    most 64 (past that a longer context gives each wave more pages).  Measured at 4096 tokens,
-    Qwen2.5-7B shape: 64 splits 1.704 ms per step, 56 splits 1.711, 48 splits 1.721, 40 splits
-    1.714."""
+    """Attention split count: at most `pages_per_split` KV pages per split (the context is dealt
+    to the splits first, so a split's keys sit on its first waves, one per SIMD of the compute
+    unit), rounded up to a multiple of 4 so a context that grows by a few pages keeps the same
+    count, at most 64 (past that a longer context gives each wave more keys).  Measured on
+    MI355X, ms per step: Qwen2.5-7B shape at 4096 tokens, 64 splits 1.546-1.550, 60 1.551, 56
+    1.549-1.553, 48 1.561-1.564; Qwen2.5-1.5B shape at 1024 tokens, 16 splits 1.065-1.067, 20
+    1.054-1.058, 24 1.064, 32 1.070-1.072, 64 1.089-1.093."""
     pages = max(1, -(-(ctx + 1) // PAGE))
     s = -(-pages // pages_per_split)
-    s = -(-s // 8) * 8
+    s = -(-s // 4) * 4
     return int(max(1, min(s, 64)))
 
 

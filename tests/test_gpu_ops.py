@@ -195,6 +195,9 @@ ATTN_CASES = [
     ("bf16", 28, 4, 128, 49, 16), ("bf16", 28, 4, 128, 17, 2), ("bf16", 28, 4, 128, 16, 4),
     ("bf16", 28, 4, 128, 15, 1), ("bf16", 12, 2, 128, 1025, 128), ("bf16", 32, 8, 128, 4097, 32),
     ("bf16", 8, 8, 128, 300, 7), ("bf16", 8, 1, 64, 33, 3), ("f32", 6, 3, 128, 100, 256),
+    # shares ending in a lone quarter past whole groups (requested with the first group): five
+    # and nine quarters on a wave, the lone one holding older tokens or the newest
+    ("bf16", 28, 4, 128, 259, 1), ("bf16", 28, 4, 128, 261, 2), ("bf16", 8, 2, 64, 1029, 4),
 ]
 
 
